@@ -1,0 +1,215 @@
+"""CPU oracle for the MACaQ online W4A4 linear layer.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` are the only callers. The product package
+never imports this module, and this module never imports the product package.
+
+This file only marshals numpy arrays into the plain C implementation in
+``macaq_oracle.c`` (built with gcc, ``-ffp-contract=off``); every step of the
+arithmetic lives there, with its sources:
+
+* "MACaQ: Fast, Model Agnostic Calibrated Quantization for Low-Precision
+  Weights and Activations" (paper card, Abstract) -- per-channel scale and
+  block-Hadamard online on the activations, inverse absorbed into the same
+  layer's weights, MXFP4 W4A4, round-to-nearest weights.
+* OCP Microscaling Formats v1.0 -- E2M1 elements, one E8M0 scale per 32.
+
+Parity status per function (what pins it, see ``tests/test_oracle_pins.py``):
+calibrate, multipliers, transform_rows, quant_rows, dequant_rows, gemm_codes,
+linear and linear_grouped are all pinned by closed forms, hand-worked values
+and brute force; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "macaq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmacaq_oracle.so")
+_lib = None
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+def build() -> str:
+    """Compile the oracle with gcc (IEEE fp32, no contraction into FMA)."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread",
+           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.oracle_calibrate.argtypes = [vp, _int, _i64, _i64, _i64, _f32p]
+    lib.oracle_multipliers.argtypes = [_f32p, _i64, _int, _f32p, _f32p]
+    lib.oracle_transform_rows.argtypes = [vp, _int, _i64, _i64, _i64, _f32p, _int, _f32p]
+    lib.oracle_quant_rows.argtypes = [vp, _int, _i64, _i64, _i64, _f32p, _int, _u8p, _u8p]
+    lib.oracle_dequant_rows.argtypes = [_u8p, _u8p, _i64, _i64, _f64p]
+    lib.oracle_gemm_codes.argtypes = [_u8p, _u8p, _i64, _u8p, _u8p, _i64, _i64, _f64p, _int]
+    lib.oracle_linear.argtypes = [vp, _i64, _i64, _i64, _f32p, _int, _u8p, _u8p, _i64, _f64p, _int]
+    lib.oracle_linear_grouped.argtypes = [vp, _i32p, _int, _i64, _i64, _f32p, _int, _u8p, _u8p, _i64,
+                                          _f64p, _int]
+    for f in (lib.oracle_calibrate, lib.oracle_multipliers, lib.oracle_transform_rows, lib.oracle_quant_rows,
+              lib.oracle_dequant_rows, lib.oracle_gemm_codes, lib.oracle_linear, lib.oracle_linear_grouped):
+        f.restype = _int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray, t):
+    return a.ctypes.data_as(t)
+
+
+def _opt_f32(a):
+    if a is None:
+        return None, _f32p()
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a, _ptr(a, _f32p)
+
+
+def _elems(x: np.ndarray):
+    """(contiguous array, dtype id): uint16 holds bf16 bits (0), float32 is 1."""
+    if x.dtype == np.uint16:
+        return np.ascontiguousarray(x), 0
+    if x.dtype == np.float32:
+        return np.ascontiguousarray(x), 1
+    raise TypeError("oracle inputs are bf16 bits (uint16) or float32, got %s" % x.dtype)
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        raise ValueError("%s rejected its arguments (code %d)" % (name, rc))
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def calibrate(xcal: np.ndarray) -> np.ndarray:
+    """s[k] = sqrt(max_r |xcal[r, k]|) as fp32 (1 for an all-zero channel)."""
+    lib = _load()
+    x, dt = _elems(xcal)
+    R, K = x.shape
+    s = np.empty(K, np.float32)
+    _check(lib.oracle_calibrate(x.ctypes.data, dt, R, K, K, _ptr(s, _f32p)), "calibrate")
+    return s
+
+
+def multipliers(s: np.ndarray, b: int):
+    """(a, r): activation multiplier c_b / s and weight multiplier c_b * s."""
+    lib = _load()
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    K = s.shape[0]
+    a = np.empty(K, np.float32)
+    r = np.empty(K, np.float32)
+    _check(lib.oracle_multipliers(_ptr(s, _f32p), K, b, _ptr(a, _f32p), _ptr(r, _f32p)), "multipliers")
+    return a, r
+
+
+def transform_rows(x: np.ndarray, m, b: int) -> np.ndarray:
+    """fp32 rows of S_b (m * x) (no multiply when m is None, no Hadamard when b == 0)."""
+    lib = _load()
+    x, dt = _elems(x)
+    M, K = x.shape
+    m_keep, mp = _opt_f32(m)
+    t = np.empty((M, K), np.float32)
+    _check(lib.oracle_transform_rows(x.ctypes.data, dt, M, K, K, mp, b, _ptr(t, _f32p)), "transform_rows")
+    return t
+
+
+def quant_rows(x: np.ndarray, m, b: int):
+    """(codes uint8 [M, K/2], scales uint8 [M, K/32]) of MXFP4(S_b (m * x))."""
+    lib = _load()
+    x, dt = _elems(x)
+    M, K = x.shape
+    m_keep, mp = _opt_f32(m)
+    codes = np.empty((M, K // 2), np.uint8)
+    scales = np.empty((M, K // 32), np.uint8)
+    _check(lib.oracle_quant_rows(x.ctypes.data, dt, M, K, K, mp, b, _ptr(codes, _u8p), _ptr(scales, _u8p)),
+           "quant_rows")
+    return codes, scales
+
+
+def prepare_weights(w: np.ndarray, r, b: int):
+    """W' = MXFP4(W D^-1 H^T) row by row: the same row quantizer with r."""
+    return quant_rows(w, r, b)
+
+
+def dequant_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    lib = _load()
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    M, K2 = codes.shape
+    out = np.empty((M, 2 * K2), np.float64)
+    _check(lib.oracle_dequant_rows(_ptr(codes, _u8p), _ptr(scales, _u8p), M, 2 * K2, _ptr(out, _f64p)),
+           "dequant_rows")
+    return out
+
+
+def gemm_codes(a_codes, a_scales, w_codes, w_scales, threads: int | None = None) -> np.ndarray:
+    """fp64 y[m, n] = sum_k dq(A[m, k]) dq(W'[n, k])."""
+    lib = _load()
+    ac = np.ascontiguousarray(a_codes, np.uint8)
+    as_ = np.ascontiguousarray(a_scales, np.uint8)
+    wc = np.ascontiguousarray(w_codes, np.uint8)
+    ws = np.ascontiguousarray(w_scales, np.uint8)
+    M, N, K = ac.shape[0], wc.shape[0], 2 * ac.shape[1]
+    y = np.empty((M, N), np.float64)
+    _check(lib.oracle_gemm_codes(_ptr(ac, _u8p), _ptr(as_, _u8p), M, _ptr(wc, _u8p), _ptr(ws, _u8p), N, K,
+                                 _ptr(y, _f64p), threads or default_threads()), "gemm_codes")
+    return y
+
+
+def linear(x: np.ndarray, a, b: int, w_codes, w_scales, threads: int | None = None) -> np.ndarray:
+    """fp64 y = W' Q(H D x) for bf16 rows x (uint16 bits)."""
+    lib = _load()
+    x = np.ascontiguousarray(x, np.uint16)
+    M, K = x.shape
+    a_keep, ap = _opt_f32(a)
+    wc = np.ascontiguousarray(w_codes, np.uint8)
+    ws = np.ascontiguousarray(w_scales, np.uint8)
+    N = wc.shape[0]
+    y = np.empty((M, N), np.float64)
+    _check(lib.oracle_linear(x.ctypes.data, M, K, K, ap, b, _ptr(wc, _u8p), _ptr(ws, _u8p), N, _ptr(y, _f64p),
+                             threads or default_threads()), "linear")
+    return y
+
+
+def linear_grouped(x: np.ndarray, offsets: np.ndarray, a, b: int, w_codes, w_scales,
+                   threads: int | None = None) -> np.ndarray:
+    """Per expert e, rows [off[e], off[e+1]) of x through a[e] and W'_e."""
+    lib = _load()
+    x = np.ascontiguousarray(x, np.uint16)
+    T, K = x.shape
+    off = np.ascontiguousarray(offsets, np.int32)
+    E = off.shape[0] - 1
+    a_keep, ap = _opt_f32(a)
+    wc = np.ascontiguousarray(w_codes, np.uint8)
+    ws = np.ascontiguousarray(w_scales, np.uint8)
+    N = wc.shape[1]
+    y = np.zeros((T, N), np.float64)
+    _check(lib.oracle_linear_grouped(x.ctypes.data, _ptr(off, _i32p), E, T, K, ap, b, _ptr(wc, _u8p),
+                                     _ptr(ws, _u8p), N, _ptr(y, _f64p), threads or default_threads()),
+           "linear_grouped")
+    return y

@@ -1,0 +1,340 @@
+/*
+ * CPU oracle for the MACaQ online W4A4 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do. It shares no source with the HIP library.
+ *
+ * What it computes (sources):
+ *   - "MACaQ: Fast, Model Agnostic Calibrated Quantization for Low-Precision
+ *     Weights and Activations" (paper card, Abstract): every linear layer is
+ *     treated on its own; a per-channel scale and a block-Hadamard transform
+ *     are applied online to the layer's activations, the inverse transforms
+ *     are absorbed into that layer's weights, and both sides are MXFP4 (W4A4),
+ *     with round-to-nearest as the weight rounding that Flip-Refinement later
+ *     improves on.
+ *   - "MACaQ - Huawei open-sources a 4-bit quantizer ..." (How it works): the
+ *     same per-channel scale plus block-Hadamard rotation, the inverse folded
+ *     into the weights, nothing crossing a layer boundary.
+ *   - MX format (OCP Microscaling Formats v1.0): 32 E2M1 elements share one
+ *     E8M0 power-of-two scale; E2M1 magnitudes are 0, .5, 1, 1.5, 2, 3, 4, 6.
+ *
+ * Readings where the pages are silent (each one is a choice, not page text):
+ *   - D divides the activations by s_k = sqrt(max_r |x_rk|) over calibration
+ *     rows, and multiplies the weight columns by s_k.
+ *   - H is the orthonormal Sylvester block-Hadamard S_b / sqrt(b) on
+ *     contiguous, aligned b-blocks along K. The 1/sqrt(b) is folded into the
+ *     per-channel multipliers on both sides: a_k = c_b / s_k, r_k = c_b * s_k
+ *     with c_b = RN32(1/sqrt(b)).
+ *   - The transform runs in fp32: one multiply, then butterfly stages of
+ *     span h = 1, 2, 4, ..., b/2 in that order, each (u, v) -> (u + v, u - v).
+ *     The quantized codes are decided in this precision on both sides.
+ *   - MX scale: floor(log2(amax)) - 2 (2 is the largest E2M1 exponent),
+ *     clamped to E8M0's lowest value 2^-127; an all-zero block gets 2^-127.
+ *   - E2M1 rounding: to nearest, ties to the even code, saturating at 6; the
+ *     sign of the input is kept, so a negative value that rounds to 0 gives
+ *     code 8.
+ *   - Packing: element 2i in the low nibble of byte i, 2i+1 in the high
+ *     nibble; scales are one byte per 32 elements, row-major.
+ *   - The GEMM over codes accumulates in fp64 (a sum of dyadic products,
+ *     exact at the sizes used).
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fPIC -shared -pthread
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL 1
+
+/* ------------------------------------------------------------------ */
+/* Element access                                                      */
+/* ------------------------------------------------------------------ */
+
+/* A bf16 value is the upper half of an fp32; widening is exact. */
+static float bf16_to_float(uint16_t h) {
+  uint32_t bits = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return f;
+}
+
+/* dtype 0: bf16 (uint16 bits); dtype 1: fp32 */
+static float load_elem(const void* base, int dtype, int64_t idx) {
+  if (dtype == 0) return bf16_to_float(((const uint16_t*)base)[idx]);
+  return ((const float*)base)[idx];
+}
+
+static int valid_block(int b) { return b == 0 || b == 32 || b == 64 || b == 128; }
+
+/* ------------------------------------------------------------------ */
+/* Per-channel scale (calibration) and the folded multipliers          */
+/* ------------------------------------------------------------------ */
+
+/* s_k = sqrt(max over calibration rows of |x_rk|), rounded once to fp32;
+   a channel that is zero on every calibration row gets s_k = 1. */
+int oracle_calibrate(const void* xcal, int dtype, int64_t R, int64_t K, int64_t ld, float* s) {
+  if (!xcal || !s || R < 1 || K < 1 || ld < K) return ORACLE_EINVAL;
+  for (int64_t k = 0; k < K; ++k) {
+    float mx = 0.0f;
+    for (int64_t r = 0; r < R; ++r) {
+      float v = fabsf(load_elem(xcal, dtype, r * ld + k));
+      if (v > mx) mx = v;
+    }
+    s[k] = (mx == 0.0f) ? 1.0f : sqrtf(mx);
+  }
+  return ORACLE_OK;
+}
+
+/* c_b = RN32(1/sqrt(b)) (1 when b == 0); a_k = RN32(c_b / s_k),
+   r_k = RN32(c_b * s_k). Either output may be NULL. */
+int oracle_multipliers(const float* s, int64_t K, int b, float* a, float* r) {
+  if (!s || K < 1 || !valid_block(b)) return ORACLE_EINVAL;
+  float cb = 1.0f;
+  if (b > 0) cb = sqrtf(1.0f / (float)b); /* 1/b is exact; sqrtf rounds once */
+  for (int64_t k = 0; k < K; ++k) {
+    if (a) a[k] = cb / s[k];
+    if (r) r[k] = cb * s[k];
+  }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Transform of one row: per-channel multiply, then block-Hadamard      */
+/* ------------------------------------------------------------------ */
+
+/* t = S_b (m .* v) on each aligned b-block, in fp32, stages of span
+   h = 1, 2, ..., b/2. m == NULL means no multiply; b == 0 means no
+   Hadamard. */
+static void transform_row(const void* x, int dtype, int64_t row_off, const float* m, int64_t K, int b,
+                          float* t) {
+  for (int64_t k = 0; k < K; ++k) {
+    float v = load_elem(x, dtype, row_off + k);
+    t[k] = m ? v * m[k] : v;
+  }
+  if (b == 0) return;
+  for (int64_t base = 0; base < K; base += b) {
+    float* blk = t + base;
+    for (int h = 1; h < b; h *= 2) {
+      for (int i = 0; i < b; ++i) {
+        if (i & h) continue;
+        float u = blk[i];
+        float w = blk[i + h];
+        blk[i] = u + w;
+        blk[i + h] = u - w;
+      }
+    }
+  }
+}
+
+int oracle_transform_rows(const void* x, int dtype, int64_t M, int64_t K, int64_t ld, const float* m, int b,
+                          float* t) {
+  if (!x || !t || M < 1 || K < 1 || ld < K || !valid_block(b)) return ORACLE_EINVAL;
+  if (b > 0 && K % b != 0) return ORACLE_EINVAL;
+  for (int64_t r = 0; r < M; ++r) transform_row(x, dtype, r * ld, m, K, b, t + r * K);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP4 encoding                                                       */
+/* ------------------------------------------------------------------ */
+
+/* E2M1 magnitude of each 3-bit code */
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* Round a non-negative magnitude (already divided by the block scale) to the
+   nearest E2M1 magnitude. Between two neighbours the decision is a compare
+   with their midpoint, which is exact; a value on the midpoint goes to the
+   neighbour with the even code (even mantissa bit). Above 6 saturates. */
+static unsigned e2m1_round_magnitude(double u) {
+  if (u >= kE2M1[7]) return 7;
+  unsigned c = 0;
+  while (!(u < kE2M1[c + 1])) ++c; /* kE2M1[c] <= u < kE2M1[c+1] */
+  double mid = 0.5 * (kE2M1[c] + kE2M1[c + 1]);
+  if (u < mid) return c;
+  if (u > mid) return c + 1;
+  return (c % 2 == 0) ? c : c + 1;
+}
+
+/* Quantize one 32-element group to (32 codes, 1 E8M0 scale code). */
+static void mx_quantize_group(const float* t, uint8_t* code, uint8_t* scale_code) {
+  float amax = 0.0f;
+  for (int i = 0; i < 32; ++i) {
+    float v = fabsf(t[i]);
+    if (v > amax) amax = v;
+  }
+  int shared_exp = -127; /* 2^-127 for an all-zero group */
+  if (amax > 0.0f) {
+    int e;
+    frexpf(amax, &e);        /* amax = f * 2^e, f in [0.5, 1) */
+    int floor_log2 = e - 1;  /* so 2^floor_log2 <= amax < 2^(floor_log2+1) */
+    shared_exp = floor_log2 - 2;
+    if (shared_exp < -127) shared_exp = -127;
+  }
+  *scale_code = (uint8_t)(shared_exp + 127);
+  for (int i = 0; i < 32; ++i) {
+    /* |t| / 2^shared_exp is exact in double */
+    double u = ldexp((double)fabsf(t[i]), -shared_exp);
+    unsigned mag = e2m1_round_magnitude(u);
+    unsigned sign = signbit(t[i]) ? 1u : 0u;
+    code[i] = (uint8_t)((sign << 3) | mag);
+  }
+}
+
+/* Quantize M rows of x (after the transform with multiplier m and block b) into
+   packed codes [M, K/2] and scales [M, K/32]. */
+int oracle_quant_rows(const void* x, int dtype, int64_t M, int64_t K, int64_t ld, const float* m, int b,
+                      uint8_t* codes, uint8_t* scales) {
+  if (!x || !codes || !scales || M < 1 || K < 32 || K % 32 != 0 || ld < K || !valid_block(b))
+    return ORACLE_EINVAL;
+  if (b > 0 && K % b != 0) return ORACLE_EINVAL;
+  float* t = (float*)malloc((size_t)K * sizeof(float));
+  uint8_t* c = (uint8_t*)malloc((size_t)K);
+  if (!t || !c) {
+    free(t);
+    free(c);
+    return ORACLE_EINVAL;
+  }
+  for (int64_t r = 0; r < M; ++r) {
+    transform_row(x, dtype, r * ld, m, K, b, t);
+    for (int64_t g = 0; g < K / 32; ++g) mx_quantize_group(t + 32 * g, c + 32 * g, scales + r * (K / 32) + g);
+    for (int64_t i = 0; i < K / 2; ++i)
+      codes[r * (K / 2) + i] = (uint8_t)(c[2 * i] | (c[2 * i + 1] << 4));
+  }
+  free(t);
+  free(c);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Dequantization and the GEMM over codes (fp64)                        */
+/* ------------------------------------------------------------------ */
+
+static double dequant_elem(const uint8_t* codes, const uint8_t* scales, int64_t K, int64_t row, int64_t k) {
+  uint8_t byte = codes[row * (K / 2) + k / 2];
+  unsigned c = (k % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+  double mag = kE2M1[c & 7];
+  double v = (c & 8) ? -mag : mag;
+  int sc = scales[row * (K / 32) + k / 32];
+  return ldexp(v, sc - 127);
+}
+
+int oracle_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t M, int64_t K, double* out) {
+  if (!codes || !scales || !out || M < 1 || K < 32 || K % 32 != 0) return ORACLE_EINVAL;
+  for (int64_t r = 0; r < M; ++r)
+    for (int64_t k = 0; k < K; ++k) out[r * K + k] = dequant_elem(codes, scales, K, r, k);
+  return ORACLE_OK;
+}
+
+typedef struct {
+  const double* a; /* dequantized A [M, K] */
+  const double* w; /* dequantized W' [N, K] */
+  double* y;       /* [M, N] */
+  int64_t m0, m1, N, K;
+} gemm_job;
+
+static void* gemm_worker(void* p) {
+  gemm_job* j = (gemm_job*)p;
+  for (int64_t m = j->m0; m < j->m1; ++m) {
+    const double* ar = j->a + m * j->K;
+    for (int64_t n = 0; n < j->N; ++n) {
+      const double* wr = j->w + n * j->K;
+      double acc = 0.0;
+      for (int64_t k = 0; k < j->K; ++k) acc += ar[k] * wr[k];
+      j->y[m * j->N + n] = acc;
+    }
+  }
+  return NULL;
+}
+
+/* y[m, n] = sum_k dq(A[m, k]) * dq(W'[n, k]) in fp64, rows split over
+   `threads` workers (each output is computed the same way by one worker). */
+int oracle_gemm_codes(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M, const uint8_t* w_codes,
+                      const uint8_t* w_scales, int64_t N, int64_t K, double* y, int threads) {
+  if (!a_codes || !a_scales || !w_codes || !w_scales || !y || M < 1 || N < 1 || K < 32 || K % 32 != 0)
+    return ORACLE_EINVAL;
+  if (threads < 1) threads = 1;
+  if (threads > M) threads = (int)M;
+  double* a = (double*)malloc((size_t)M * K * sizeof(double));
+  double* w = (double*)malloc((size_t)N * K * sizeof(double));
+  gemm_job* jobs = (gemm_job*)malloc((size_t)threads * sizeof(gemm_job));
+  pthread_t* tid = (pthread_t*)malloc((size_t)threads * sizeof(pthread_t));
+  if (!a || !w || !jobs || !tid) {
+    free(a);
+    free(w);
+    free(jobs);
+    free(tid);
+    return ORACLE_EINVAL;
+  }
+  oracle_dequant_rows(a_codes, a_scales, M, K, a);
+  oracle_dequant_rows(w_codes, w_scales, N, K, w);
+  for (int i = 0; i < threads; ++i) {
+    jobs[i].a = a;
+    jobs[i].w = w;
+    jobs[i].y = y;
+    jobs[i].N = N;
+    jobs[i].K = K;
+    jobs[i].m0 = M * i / threads;
+    jobs[i].m1 = M * (i + 1) / threads;
+  }
+  int started = 0;
+  for (int i = 1; i < threads; ++i)
+    if (pthread_create(&tid[i], NULL, gemm_worker, &jobs[i]) == 0) started = i;
+    else break;
+  gemm_worker(&jobs[0]);
+  for (int i = 1; i <= started; ++i) pthread_join(tid[i], NULL);
+  for (int i = started + 1; i < threads; ++i) gemm_worker(&jobs[i]); /* any that failed to start */
+  free(a);
+  free(w);
+  free(jobs);
+  free(tid);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* The layer: activations through the transform and MXFP4, then the GEMM */
+/* ------------------------------------------------------------------ */
+
+/* y = W' . Q(H D x) for M bf16 rows of x; weights already prepared. */
+int oracle_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* a, int b,
+                  const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, double* y, int threads) {
+  if (!x || !w_codes || !w_scales || !y || M < 1 || N < 1) return ORACLE_EINVAL;
+  uint8_t* ac = (uint8_t*)malloc((size_t)M * K / 2);
+  uint8_t* as = (uint8_t*)malloc((size_t)M * K / 32);
+  if (!ac || !as) {
+    free(ac);
+    free(as);
+    return ORACLE_EINVAL;
+  }
+  int rc = oracle_quant_rows(x, 0, M, K, ldx, a, b, ac, as);
+  if (rc == ORACLE_OK) rc = oracle_gemm_codes(ac, as, M, w_codes, w_scales, N, K, y, threads);
+  free(ac);
+  free(as);
+  return rc;
+}
+
+/* Per expert e: rows [off[e], off[e+1]) of x (expert-major order) go
+   through expert e's multiplier a[e, :] and weights W'_e [N, K]. Experts
+   with no rows are skipped. */
+int oracle_linear_grouped(const uint16_t* x, const int32_t* off, int E, int64_t T, int64_t K, const float* a,
+                          int b, const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, double* y,
+                          int threads) {
+  if (!x || !off || !w_codes || !w_scales || !y || E < 1 || T < 0 || N < 1 || K < 32 || K % 32 != 0)
+    return ORACLE_EINVAL;
+  if (off[0] != 0 || off[E] != T) return ORACLE_EINVAL;
+  for (int e = 0; e < E; ++e) {
+    if (off[e + 1] < off[e]) return ORACLE_EINVAL;
+  }
+  for (int e = 0; e < E; ++e) {
+    int64_t rows = off[e + 1] - off[e];
+    if (rows == 0) continue;
+    int rc = oracle_linear(x + (int64_t)off[e] * K, rows, K, K, a ? a + (int64_t)e * K : NULL, b,
+                           w_codes + (int64_t)e * N * (K / 2), w_scales + (int64_t)e * N * (K / 32), N,
+                           y + (int64_t)off[e] * N, threads);
+    if (rc != ORACLE_OK) return rc;
+  }
+  return ORACLE_OK;
+}
