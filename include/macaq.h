@@ -1,0 +1,172 @@
+/*
+ * macaq.h -- C ABI of the MACaQ online W4A4 linear layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method ("MACaQ: Fast, Model Agnostic Calibrated Quantization for
+ * Low-Precision Weights and Activations", paper card, Abstract; restated in
+ * "MACaQ - Huawei open-sources a 4-bit quantizer for GGUF, vLLM and
+ * Diffusers", How it works): every linear layer is handled on its own. At
+ * inference a per-channel scale D and a block-Hadamard transform H are applied
+ * to the layer's activations, which are then quantized to MXFP4; the inverse
+ * transforms are absorbed offline into the same layer's MXFP4 weights:
+ *
+ *     W' = MXFP4_RTN(W D^-1 H^T),   y = W' . MXFP4(H D x)  (~= W x).
+ *
+ * Conventions used by every call (readings where the pages are silent):
+ *   - D = diag(1/s) with s_k = sqrt(max |x_k|) over calibration rows;
+ *     H = S_b / sqrt(b), S_b the Sylvester (natural-order) Hadamard matrix,
+ *     on contiguous aligned b-blocks of K, b in {32, 64, 128}; b = 0 means no
+ *     Hadamard. The 1/sqrt(b) is folded into the per-channel multipliers:
+ *     activations use a_k = RN32(c_b / s_k), weights r_k = RN32(c_b * s_k),
+ *     c_b = RN32(1/sqrt(b)) (1 when b = 0).
+ *   - The transform runs in fp32: t_k = RN32(v_k * m_k), then butterflies of
+ *     span 1, 2, 4, ..., b/2 in that order, (u, v) -> (u + v, u - v).
+ *   - MXFP4 (OCP MX v1.0): 32 consecutive elements along K share one E8M0
+ *     scale 2^(floor(log2 amax) - 2), clamped to >= 2^-127; elements are E2M1
+ *     codes (sign bit 3; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6) rounded to
+ *     nearest, ties to the even code, saturating at 6.
+ *   - Packed codes: uint8 [rows, K/2], row-major, element 2i in the low nibble
+ *     of byte i. Scales: uint8 [rows, K/32], row-major, E8M0 (bias 127).
+ *   - Activations X are bf16 [M, ldx] row-major. Outputs Y are [M, ldy]
+ *     row-major, fp32 or bf16 (round-to-nearest-even).
+ *
+ * Ownership and execution: every pointer marked "device" is device memory
+ * owned by the caller; host pointers are marked "host". The library allocates
+ * nothing, keeps no per-call state, never synchronizes, and enqueues its work
+ * on `stream` (NULL = the default stream). Calls are reentrant. Scratch that
+ * a call needs is the caller's `workspace`, whose size the matching
+ * *_workspace_size call gives.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued; on a
+ * check failure nothing is written and the status says why. MACAQ_EHIP means
+ * the HIP runtime refused a launch; macaq_last_error() has the text. Inputs
+ * must be finite: NaN or Inf in X or W give unspecified codes.
+ */
+#ifndef MACAQ_H
+#define MACAQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t. */
+typedef struct ihipStream_t* macaq_stream_t;
+
+typedef enum {
+  MACAQ_OK = 0,
+  MACAQ_EINVAL = 1,       /* null pointer, bad size, block or leading dimension */
+  MACAQ_EALIGN = 2,       /* pointer or leading dimension not aligned as documented */
+  MACAQ_EWORKSPACE = 3,   /* workspace smaller than the *_workspace_size result */
+  MACAQ_EUNSUPPORTED = 4, /* current device is not gfx950 */
+  MACAQ_EHIP = 5          /* a HIP runtime call failed; see macaq_last_error() */
+} macaq_status;
+
+typedef enum { MACAQ_BF16 = 0, MACAQ_F32 = 1 } macaq_dtype;
+
+/* Text for a status code (static storage). */
+const char* macaq_status_string(macaq_status s);
+
+/* Detail of the last failure on the calling thread (static, thread-local). */
+const char* macaq_last_error(void);
+
+/*
+ * Per-channel scale from calibration activations (the "calibrated
+ * per-channel scale" of the paper card's title and Abstract):
+ *   s[k] = RN32(sqrt(max_r |xcal[r, k]|)), or 1 when that maximum is 0.
+ * xcal: device bf16 [R, ldx]; s: device fp32 [K] (written).
+ * Requires R >= 1, K >= 1, ldx >= K.
+ */
+macaq_status macaq_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx, float* s,
+                             macaq_stream_t stream);
+
+/*
+ * Folded multipliers for one layer: a[k] = RN32(c_b / s[k]) for the
+ * activations and r[k] = RN32(c_b * s[k]) for the weights, c_b =
+ * RN32(1/sqrt(b)) (1 when b = 0). s, a, r: device fp32 [K]; a or r may be
+ * NULL to skip it. b in {0, 32, 64, 128}.
+ */
+macaq_status macaq_make_multipliers(const float* s, int64_t K, int32_t b, float* a, float* r,
+                                    macaq_stream_t stream);
+
+/*
+ * Offline half (paper card, Abstract: inverse transforms absorbed into the
+ * weights; round-to-nearest MXFP4): W' = MXFP4(rows of S_b (r .* W[n, :])).
+ * W: device [N, ldw] of w_dtype (bf16 or fp32), row n = output channel n.
+ * r: device fp32 [K] from macaq_make_multipliers, or NULL with b = 0 for
+ * plain MXFP4 weights. w_codes: device [N, K/2]; w_scales: device [N, K/32].
+ * Requires K % 32 == 0, K % b == 0, ldw >= K; W, w_codes and w_scales 16-byte
+ * aligned and ldw a multiple of 8 elements.
+ */
+macaq_status macaq_prepare_weights(const void* W, macaq_dtype w_dtype, int64_t N, int64_t K, int64_t ldw,
+                                   const float* r, int32_t b, uint8_t* w_codes, uint8_t* w_scales,
+                                   macaq_stream_t stream);
+
+/*
+ * Online activation transform on its own (paper card, Abstract: per-channel
+ * scale and block-Hadamard applied online to the activations, then MXFP4):
+ * a_codes/a_scales = MXFP4(rows of S_b (a .* X[m, :])).
+ * X: device bf16 [M, ldx]; a: device fp32 [K] or NULL (no scale); b in
+ * {0, 32, 64, 128}. a_codes: device [M, K/2]; a_scales: device [M, K/32].
+ * Alignment as macaq_prepare_weights. M = 0 is allowed and does nothing.
+ */
+macaq_status macaq_quant_act(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
+                             uint8_t* a_codes, uint8_t* a_scales, macaq_stream_t stream);
+
+/* Bytes of workspace that macaq_linear needs for these sizes. */
+size_t macaq_linear_workspace_size(int64_t M, int64_t K, int64_t N);
+
+/*
+ * The layer (paper card, Abstract: W4A4 with the activation transforms run at
+ * inference): Y[m, n] = sum_k dq(Q(S_b (a .* X[m, :]))_k) dq(W'[n, k]),
+ * accumulated in fp32 on the scaled-FP4 matrix cores.
+ * X: device bf16 [M, ldx]; a, b as macaq_quant_act (a = NULL, b = 0 is plain
+ * MXFP4); w_codes/w_scales: device, from macaq_prepare_weights with the
+ * matching r and b; Y: device [M, ldy] of y_dtype; workspace: device, at least
+ * macaq_linear_workspace_size(M, K, N) bytes, 256-byte aligned.
+ * Requires ldy >= N, ldy a multiple of 4 elements, Y 16-byte aligned.
+ */
+macaq_status macaq_linear(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
+                          const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, void* Y,
+                          macaq_dtype y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+                          macaq_stream_t stream);
+
+/*
+ * The GEMM alone on operands already in MXFP4 (the contraction step of
+ * macaq_linear; also the baseline for the cost of the activation transform):
+ * Y[m, n] = sum_k dq(A[m, k]) dq(W'[n, k]).
+ * a_codes/a_scales: device [M, K/2] / [M, K/32]; other arguments as
+ * macaq_linear.
+ */
+size_t macaq_gemm_workspace_size(int64_t M, int64_t K, int64_t N);
+macaq_status macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M, int64_t K,
+                        const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, void* Y,
+                        macaq_dtype y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+                        macaq_stream_t stream);
+
+/* Bytes of workspace that macaq_linear_grouped needs. */
+size_t macaq_linear_grouped_workspace_size(int64_t T, int32_t E, int64_t K, int64_t N);
+
+/*
+ * The layer for E experts of a mixture-of-experts block (the pages apply
+ * MACaQ unchanged to MoE models; each expert's linear layer has its own D and
+ * absorbed weights): rows [offsets[e], offsets[e+1]) of X belong to expert e
+ * and go through a[e, :] and W'_e.
+ * X: device bf16 [T, K] (contiguous, expert-major); offsets: device int32
+ * [E+1], non-decreasing, offsets[0] = 0, offsets[E] = T (not checked on the
+ * host: it lives on the device); a: device fp32 [E, K] or NULL with b = 0;
+ * w_codes: device [E, N, K/2]; w_scales: device [E, N, K/32]; Y: device
+ * [T, N] of y_dtype (row t is written for every t < T).
+ */
+macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t E, int64_t T, int64_t K,
+                                  const float* a, int32_t b, const uint8_t* w_codes, const uint8_t* w_scales,
+                                  int64_t N, void* Y, macaq_dtype y_dtype, void* workspace,
+                                  size_t workspace_bytes, macaq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MACAQ_H */

@@ -1,0 +1,248 @@
+"""ctypes binding of ``libmacaq.so`` (C ABI in ``include/macaq.h``).
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing or the device is not gfx950
+the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmacaq.so")
+_lib = None
+_lock = threading.Lock()
+
+MACAQ_BF16 = 0
+MACAQ_F32 = 1
+_STATUS_NAMES = {0: "MACAQ_OK", 1: "MACAQ_EINVAL", 2: "MACAQ_EALIGN", 3: "MACAQ_EWORKSPACE",
+                 4: "MACAQ_EUNSUPPORTED", 5: "MACAQ_EHIP"}
+
+# name -> (restype, argtypes), in the order of include/macaq.h
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_SIGNATURES = {
+    "macaq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "macaq_last_error": (ctypes.c_char_p, []),
+    "macaq_calibrate": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    "macaq_make_multipliers": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
+    "macaq_prepare_weights": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp]),
+    "macaq_quant_act": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp]),
+    "macaq_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "macaq_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64, _vp, ctypes.c_int, _i64,
+                                    _vp, _sz, _vp]),
+    "macaq_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "macaq_gemm": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, ctypes.c_int, _i64, _vp, _sz, _vp]),
+    "macaq_linear_grouped_workspace_size": (_sz, [_i64, _i32, _i64, _i64]),
+    "macaq_linear_grouped": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _i64, _vp,
+                                            ctypes.c_int, _vp, _sz, _vp]),
+}
+
+
+class MacaqError(RuntimeError):
+    def __init__(self, func: str, status: int, detail: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s): %s" % (func, _STATUS_NAMES.get(status, status),
+                                                    _status_string(status), detail))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmacaq.so; build it first only when no built library exists."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _build
+            _build.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _status_string(status: int) -> str:
+    lib = load_library()
+    return lib.macaq_status_string(status).decode()
+
+
+def _check(status: int, func: str):
+    if status != 0:
+        lib = load_library()
+        raise MacaqError(func, status, lib.macaq_last_error().decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("macaq: tensors must be on the GPU")
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return MACAQ_BF16
+    if dt == torch.float32:
+        return MACAQ_F32
+    raise ValueError("macaq: dtype %s is not bf16 or fp32" % dt)
+
+
+def calibrate(xcal: torch.Tensor) -> torch.Tensor:
+    """Per-channel scale s[k] = sqrt(max_r |xcal[r, k]|) of bf16 calibration rows."""
+    _need_cuda(xcal)
+    assert xcal.dtype == torch.bfloat16 and xcal.dim() == 2 and xcal.stride(1) == 1
+    R, K = xcal.shape
+    s = torch.empty(K, dtype=torch.float32, device=xcal.device)
+    _check(load_library().macaq_calibrate(_ptr(xcal), R, K, xcal.stride(0), _ptr(s), _stream(xcal)),
+           "macaq_calibrate")
+    return s
+
+
+def make_multipliers(s: torch.Tensor, b: int):
+    """(a, r): activation multiplier c_b / s and weight multiplier c_b * s."""
+    _need_cuda(s)
+    s = s.contiguous()
+    a = torch.empty_like(s)
+    r = torch.empty_like(s)
+    _check(load_library().macaq_make_multipliers(_ptr(s), s.numel(), b, _ptr(a), _ptr(r), _stream(s)),
+           "macaq_make_multipliers")
+    return a, r
+
+
+def prepare_weights(w: torch.Tensor, r: torch.Tensor | None, b: int):
+    """W' = MXFP4(W D^-1 H^T): (codes uint8 [N, K/2], scales uint8 [N, K/32])."""
+    _need_cuda(w, r)
+    assert w.dim() == 2 and w.stride(1) == 1
+    N, K = w.shape
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(N, K // 32, dtype=torch.uint8, device=w.device)
+    _check(load_library().macaq_prepare_weights(_ptr(w), _dtype_code(w.dtype), N, K, w.stride(0), _ptr(r), b,
+                                                _ptr(codes), _ptr(scales), _stream(w)), "macaq_prepare_weights")
+    return codes, scales
+
+
+def quant_act(x: torch.Tensor, a: torch.Tensor | None, b: int, codes: torch.Tensor | None = None,
+              scales: torch.Tensor | None = None):
+    """MXFP4(H D x) of bf16 rows: (codes uint8 [M, K/2], scales uint8 [M, K/32])."""
+    _need_cuda(x, a, codes, scales)
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty(M, K // 2, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(M, K // 32, dtype=torch.uint8, device=x.device)
+    assert codes.is_contiguous() and codes.shape == (M, K // 2) and scales.is_contiguous() and scales.shape == (M, K // 32)
+    _check(load_library().macaq_quant_act(_ptr(x), M, K, x.stride(0), _ptr(a), b, _ptr(codes), _ptr(scales),
+                                          _stream(x)), "macaq_quant_act")
+    return codes, scales
+
+
+def linear_workspace_size(M: int, K: int, N: int) -> int:
+    return int(load_library().macaq_linear_workspace_size(M, K, N))
+
+
+def gemm_workspace_size(M: int, K: int, N: int) -> int:
+    return int(load_library().macaq_gemm_workspace_size(M, K, N))
+
+
+def linear_grouped_workspace_size(T: int, E: int, K: int, N: int) -> int:
+    return int(load_library().macaq_linear_grouped_workspace_size(T, E, K, N))
+
+
+def _workspace(nbytes: int, device, given: torch.Tensor | None):
+    if given is not None:
+        return given
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def linear(x: torch.Tensor, a: torch.Tensor | None, b: int, w_codes: torch.Tensor, w_scales: torch.Tensor,
+           out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W' MXFP4(H D x) for bf16 rows x [M, K]; returns [M, N] of out_dtype."""
+    _need_cuda(x, a, w_codes, w_scales)
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    N = w_codes.shape[0]
+    y = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=x.device)
+    ws_bytes = linear_workspace_size(M, K, N)
+    ws = _workspace(ws_bytes, x.device, workspace)
+    _check(load_library().macaq_linear(_ptr(x), M, K, x.stride(0), _ptr(a), b, _ptr(w_codes), _ptr(w_scales), N,
+                                       _ptr(y), _dtype_code(y.dtype), y.stride(0), _ptr(ws), ws.numel(), _stream(x)),
+           "macaq_linear")
+    return y
+
+
+def linear_plain_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
+                      out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The GEMM alone on MXFP4 operands: y = dq(A) dq(W')^T."""
+    _need_cuda(a_codes, a_scales, w_codes, w_scales)
+    M, K = a_codes.shape[0], 2 * a_codes.shape[1]
+    N = w_codes.shape[0]
+    y = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
+    ws = _workspace(gemm_workspace_size(M, K, N), a_codes.device, workspace)
+    _check(load_library().macaq_gemm(_ptr(a_codes), _ptr(a_scales), M, K, _ptr(w_codes), _ptr(w_scales), N, _ptr(y),
+                                     _dtype_code(y.dtype), y.stride(0), _ptr(ws), ws.numel(),
+                                     _stream(a_codes)), "macaq_gemm")
+    return y
+
+
+def linear_grouped(x: torch.Tensor, offsets: torch.Tensor, a: torch.Tensor | None, b: int, w_codes: torch.Tensor,
+                   w_scales: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Per expert e: rows [off[e], off[e+1]) of x through a[e] and W'_e [N, K]."""
+    _need_cuda(x, offsets, a, w_codes, w_scales)
+    assert x.dtype == torch.bfloat16 and x.is_contiguous() and offsets.dtype == torch.int32
+    T, K = x.shape
+    E = offsets.numel() - 1
+    N = w_codes.shape[1]
+    y = out if out is not None else torch.empty(T, N, dtype=out_dtype, device=x.device)
+    ws = _workspace(linear_grouped_workspace_size(T, E, K, N), x.device, workspace)
+    _check(load_library().macaq_linear_grouped(_ptr(x), _ptr(offsets), E, T, K, _ptr(a), b, _ptr(w_codes),
+                                               _ptr(w_scales), N, _ptr(y), _dtype_code(y.dtype), _ptr(ws),
+                                               ws.numel(), _stream(x)), "macaq_linear_grouped")
+    return y
+
+
+class Layer:
+    """A prepared layer: the activation multiplier a and W' codes/scales from
+    the same calibration scale s and Hadamard block b."""
+
+    def __init__(self, a, r, b, w_codes, w_scales, s=None):
+        self.a, self.r, self.b = a, r, b
+        self.w_codes, self.w_scales, self.s = w_codes, w_scales, s
+
+    def __call__(self, x, out_dtype=torch.bfloat16, out=None, workspace=None):
+        return linear(x, self.a, self.b, self.w_codes, self.w_scales, out_dtype, out, workspace)
+
+
+def prepare_layer(w: torch.Tensor, xcal: torch.Tensor | None, b: int) -> Layer:
+    """Calibrate s on xcal, fold c_b into a and r, and prepare W'. With
+    xcal None and b == 0 the layer is plain MXFP4 (no transform)."""
+    if xcal is None:
+        if b != 0:
+            raise ValueError("a Hadamard block without a calibration scale is not a MACaQ layer")
+        codes, scales = prepare_weights(w, None, 0)
+        return Layer(None, None, 0, codes, scales)
+    s = calibrate(xcal)
+    a, r = make_multipliers(s, b)
+    codes, scales = prepare_weights(w, r, b)
+    return Layer(a, r, b, codes, scales, s)

@@ -1,0 +1,341 @@
+// C ABI of the MACaQ online W4A4 linear layer (declared in include/macaq.h).
+//
+// Host side only: argument checks (pure host code, done before any HIP call),
+// the device check, workspace carving and kernel dispatch. No call allocates,
+// synchronizes or keeps state beyond a per-device architecture cache.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "common.hpp"
+#include "macaq.h"
+
+using namespace macaq;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+macaq_status fail(macaq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+macaq_status fail(macaq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+macaq_status hip_fail(hipError_t e, const char* what) {
+  return fail(MACAQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool valid_block(int32_t b) { return b == 0 || b == 32 || b == 64 || b == 128; }
+
+// gfx950 check of the current device, cached per device id.
+constexpr int kMaxDevices = 64;
+int g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+std::mutex g_arch_mu;
+
+macaq_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MACAQ_EUNSUPPORTED, "no usable HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MACAQ_EUNSUPPORTED, "device id %d out of range", dev);
+  {
+    std::lock_guard<std::mutex> lk(g_arch_mu);
+    if (g_arch_ok[dev] == 1) return MACAQ_OK;
+    if (g_arch_ok[dev] == -1) return fail(MACAQ_EUNSUPPORTED, "device %d is not gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  {
+    std::lock_guard<std::mutex> lk(g_arch_mu);
+    g_arch_ok[dev] = ok ? 1 : -1;
+  }
+  if (!ok) return fail(MACAQ_EUNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  return MACAQ_OK;
+}
+
+constexpr size_t kWsAlign = 256;
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct LinearWs {
+  size_t codes_off, scales_off, extra_off, total;
+};
+
+LinearWs linear_ws(int64_t M, int64_t K, size_t extra_bytes) {
+  LinearWs w;
+  w.codes_off = 0;
+  w.scales_off = round_up((size_t)M * (size_t)(K / 2), kWsAlign);
+  w.extra_off = w.scales_off + round_up((size_t)M * (size_t)(K / 32), kWsAlign);
+  w.total = w.extra_off + round_up(extra_bytes, kWsAlign);
+  return w;
+}
+
+macaq_status check_quant_shape(int64_t M, int64_t K, int64_t ld, int32_t b, const char* who) {
+  if (M < 0) return fail(MACAQ_EINVAL, "%s: M = %lld < 0", who, (long long)M);
+  if (K < 32 || K % 32 != 0) return fail(MACAQ_EINVAL, "%s: K = %lld is not a positive multiple of 32", who, (long long)K);
+  if (!valid_block(b)) return fail(MACAQ_EINVAL, "%s: Hadamard block %d not in {0, 32, 64, 128}", who, b);
+  if (b > 0 && K % b != 0) return fail(MACAQ_EINVAL, "%s: K = %lld is not a multiple of b = %d", who, (long long)K, b);
+  if (ld < K) return fail(MACAQ_EINVAL, "%s: leading dimension %lld < K = %lld", who, (long long)ld, (long long)K);
+  return MACAQ_OK;
+}
+
+macaq_status check_out(const void* Y, macaq_dtype dt, int64_t N, int64_t ldy, const char* who) {
+  if (!Y) return fail(MACAQ_EINVAL, "%s: Y is NULL", who);
+  if (dt != MACAQ_BF16 && dt != MACAQ_F32) return fail(MACAQ_EINVAL, "%s: bad output dtype %d", who, (int)dt);
+  if (ldy < N) return fail(MACAQ_EINVAL, "%s: ldy = %lld < N = %lld", who, (long long)ldy, (long long)N);
+  if (!aligned(Y, 16) || ldy % 4 != 0) return fail(MACAQ_EALIGN, "%s: Y must be 16-byte aligned, ldy a multiple of 4", who);
+  return MACAQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* macaq_status_string(macaq_status s) {
+  switch (s) {
+    case MACAQ_OK: return "ok";
+    case MACAQ_EINVAL: return "invalid argument";
+    case MACAQ_EALIGN: return "misaligned pointer or leading dimension";
+    case MACAQ_EWORKSPACE: return "workspace too small or misaligned";
+    case MACAQ_EUNSUPPORTED: return "unsupported device (gfx950 required)";
+    case MACAQ_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* macaq_last_error(void) { return g_last_error; }
+
+macaq_status macaq_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx, float* s, macaq_stream_t stream) {
+  if (!xcal || !s) return fail(MACAQ_EINVAL, "macaq_calibrate: NULL pointer");
+  if (R < 1 || K < 1 || ldx < K) return fail(MACAQ_EINVAL, "macaq_calibrate: need R >= 1, K >= 1, ldx >= K");
+  if (!aligned(xcal, 2) || !aligned(s, 4)) return fail(MACAQ_EALIGN, "macaq_calibrate: misaligned pointer");
+  macaq_status st = check_device();
+  if (st != MACAQ_OK) return st;
+  hipError_t e = launch_calibrate(xcal, R, K, ldx, s, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_calibrate launch");
+}
+
+macaq_status macaq_make_multipliers(const float* s, int64_t K, int32_t b, float* a, float* r, macaq_stream_t stream) {
+  if (!s || (!a && !r)) return fail(MACAQ_EINVAL, "macaq_make_multipliers: NULL pointer");
+  if (K < 1) return fail(MACAQ_EINVAL, "macaq_make_multipliers: K < 1");
+  if (!valid_block(b)) return fail(MACAQ_EINVAL, "macaq_make_multipliers: block %d not in {0, 32, 64, 128}", b);
+  if (!aligned(s, 4) || (a && !aligned(a, 4)) || (r && !aligned(r, 4)))
+    return fail(MACAQ_EALIGN, "macaq_make_multipliers: misaligned pointer");
+  macaq_status st = check_device();
+  if (st != MACAQ_OK) return st;
+  // c_b = RN32(1/sqrt(b)): 1/b is exact in fp32 and sqrtf rounds once.
+  const float cb = b > 0 ? std::sqrt(1.0f / (float)b) : 1.0f;
+  hipError_t e = launch_multipliers(s, K, cb, a, r, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_make_multipliers launch");
+}
+
+macaq_status macaq_prepare_weights(const void* W, macaq_dtype w_dtype, int64_t N, int64_t K, int64_t ldw,
+                                   const float* r, int32_t b, uint8_t* w_codes, uint8_t* w_scales,
+                                   macaq_stream_t stream) {
+  const char* who = "macaq_prepare_weights";
+  if (!W || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (w_dtype != MACAQ_BF16 && w_dtype != MACAQ_F32) return fail(MACAQ_EINVAL, "%s: bad weight dtype", who);
+  macaq_status st = check_quant_shape(N, K, ldw, b, who);
+  if (st != MACAQ_OK) return st;
+  const size_t esz = w_dtype == MACAQ_F32 ? 4 : 2;
+  if (!aligned(W, 16) || (ldw * (int64_t)esz) % 16 != 0 || !aligned(w_codes, 16) || !aligned(w_scales, 16) ||
+      (r && !aligned(r, 16)))
+    return fail(MACAQ_EALIGN, "%s: W, r, w_codes, w_scales must be 16-byte aligned and rows of W 16-byte multiples", who);
+  if (N == 0) return MACAQ_OK;
+  st = check_device();
+  if (st != MACAQ_OK) return st;
+  QuantArgs q{};
+  q.x = W;
+  q.M = N;
+  q.K = K;
+  q.ldx = ldw;
+  q.mult = r;
+  q.codes = w_codes;
+  q.scales = w_scales;
+  hipError_t e = launch_quant_rows(q, b, w_dtype == MACAQ_F32, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_prepare_weights launch");
+}
+
+macaq_status macaq_quant_act(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
+                             uint8_t* a_codes, uint8_t* a_scales, macaq_stream_t stream) {
+  const char* who = "macaq_quant_act";
+  if (!X || !a_codes || !a_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  macaq_status st = check_quant_shape(M, K, ldx, b, who);
+  if (st != MACAQ_OK) return st;
+  if (!aligned(X, 16) || ldx % 8 != 0 || !aligned(a_codes, 16) || !aligned(a_scales, 16) || (a && !aligned(a, 16)))
+    return fail(MACAQ_EALIGN, "%s: X, a, a_codes, a_scales must be 16-byte aligned and ldx a multiple of 8", who);
+  if (M == 0) return MACAQ_OK;
+  st = check_device();
+  if (st != MACAQ_OK) return st;
+  QuantArgs q{};
+  q.x = X;
+  q.M = M;
+  q.K = K;
+  q.ldx = ldx;
+  q.mult = a;
+  q.codes = a_codes;
+  q.scales = a_scales;
+  hipError_t e = launch_quant_rows(q, b, false, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_quant_act launch");
+}
+
+size_t macaq_gemm_workspace_size(int64_t M, int64_t K, int64_t N) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return round_up(plan_gemm(M, N, K).partial_bytes, kWsAlign);
+}
+
+size_t macaq_linear_workspace_size(int64_t M, int64_t K, int64_t N) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return linear_ws(M, K, plan_gemm(M, N, K).partial_bytes).total;
+}
+
+static macaq_status gemm_common(const uint8_t* ac, const uint8_t* as, int64_t M, int64_t K, const uint8_t* wc,
+                                const uint8_t* ws, int64_t N, void* Y, macaq_dtype y_dtype, int64_t ldy,
+                                float* partial, hipStream_t stream, const char* who) {
+  GemmPlan p = plan_gemm(M, N, K);
+  GemmArgs g{};
+  g.a_codes = ac;
+  g.a_scales = as;
+  g.b_codes = wc;
+  g.b_scales = ws;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.y = Y;
+  g.ldy = ldy;
+  g.y_bf16 = y_dtype == MACAQ_BF16;
+  g.partial = partial;
+  g.splits = p.splits;
+  hipError_t e = launch_gemm(g, p, stream);
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, who);
+}
+
+macaq_status macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M, int64_t K, const uint8_t* w_codes,
+                        const uint8_t* w_scales, int64_t N, void* Y, macaq_dtype y_dtype, int64_t ldy,
+                        void* workspace, size_t workspace_bytes, macaq_stream_t stream) {
+  const char* who = "macaq_gemm";
+  if (!a_codes || !a_scales || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (M < 0 || N < 1) return fail(MACAQ_EINVAL, "%s: need M >= 0, N >= 1", who);
+  if (K < 32 || K % 32 != 0) return fail(MACAQ_EINVAL, "%s: K is not a positive multiple of 32", who);
+  macaq_status st = check_out(Y, y_dtype, N, ldy, who);
+  if (st != MACAQ_OK) return st;
+  if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 16) || !aligned(w_scales, 16))
+    return fail(MACAQ_EALIGN, "%s: code and scale arrays must be 16-byte aligned", who);
+  if (M == 0) return MACAQ_OK;
+  const size_t need = macaq_gemm_workspace_size(M, K, N);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign)))
+    return fail(MACAQ_EWORKSPACE, "%s: need %zu workspace bytes, 256-byte aligned", who, need);
+  st = check_device();
+  if (st != MACAQ_OK) return st;
+  return gemm_common(a_codes, a_scales, M, K, w_codes, w_scales, N, Y, y_dtype, ldy, static_cast<float*>(workspace),
+                     reinterpret_cast<hipStream_t>(stream), who);
+}
+
+macaq_status macaq_linear(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
+                          const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, void* Y, macaq_dtype y_dtype,
+                          int64_t ldy, void* workspace, size_t workspace_bytes, macaq_stream_t stream) {
+  const char* who = "macaq_linear";
+  if (!X || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  macaq_status st = check_quant_shape(M, K, ldx, b, who);
+  if (st != MACAQ_OK) return st;
+  if (N < 1) return fail(MACAQ_EINVAL, "%s: N < 1", who);
+  st = check_out(Y, y_dtype, N, ldy, who);
+  if (st != MACAQ_OK) return st;
+  if (!aligned(X, 16) || ldx % 8 != 0 || (a && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 16))
+    return fail(MACAQ_EALIGN, "%s: X, a, w_codes, w_scales must be 16-byte aligned and ldx a multiple of 8", who);
+  if (M == 0) return MACAQ_OK;
+  const GemmPlan p = plan_gemm(M, N, K);
+  const LinearWs w = linear_ws(M, K, p.partial_bytes);
+  if (!workspace || workspace_bytes < w.total || !aligned(workspace, kWsAlign))
+    return fail(MACAQ_EWORKSPACE, "%s: need %zu workspace bytes, 256-byte aligned", who, w.total);
+  st = check_device();
+  if (st != MACAQ_OK) return st;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  QuantArgs q{};
+  q.x = X;
+  q.M = M;
+  q.K = K;
+  q.ldx = ldx;
+  q.mult = a;
+  q.codes = ws + w.codes_off;
+  q.scales = ws + w.scales_off;
+  hipError_t e = launch_quant_rows(q, b, false, s);
+  if (e != hipSuccess) return hip_fail(e, "macaq_linear quantize launch");
+  return gemm_common(q.codes, q.scales, M, K, w_codes, w_scales, N, Y, y_dtype, ldy,
+                     reinterpret_cast<float*>(ws + w.extra_off), s, who);
+}
+
+size_t macaq_linear_grouped_workspace_size(int64_t T, int32_t E, int64_t K, int64_t N) {
+  if (T <= 0 || E < 1 || K <= 0 || N <= 0) return 0;
+  const GemmPlan p = plan_gemm_grouped(T, E, N, K);
+  const int64_t max_mtiles = (T + p.bm - 1) / p.bm + E;
+  return linear_ws(T, K, (size_t)max_mtiles * 2 * sizeof(int32_t)).total;
+}
+
+macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t E, int64_t T, int64_t K,
+                                  const float* a, int32_t b, const uint8_t* w_codes, const uint8_t* w_scales,
+                                  int64_t N, void* Y, macaq_dtype y_dtype, void* workspace, size_t workspace_bytes,
+                                  macaq_stream_t stream) {
+  const char* who = "macaq_linear_grouped";
+  if (!X || !offsets || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (E < 1) return fail(MACAQ_EINVAL, "%s: E < 1", who);
+  macaq_status st = check_quant_shape(T, K, K, b, who);
+  if (st != MACAQ_OK) return st;
+  if (N < 1) return fail(MACAQ_EINVAL, "%s: N < 1", who);
+  st = check_out(Y, y_dtype, N, N, who);
+  if (st != MACAQ_OK) return st;
+  if (!aligned(X, 16) || (a && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 16) ||
+      !aligned(offsets, 4) || (K * (int64_t)sizeof(float)) % 16 != 0)
+    return fail(MACAQ_EALIGN, "%s: X, a, w_codes, w_scales must be 16-byte aligned", who);
+  if (T == 0) return MACAQ_OK;
+  const size_t need = macaq_linear_grouped_workspace_size(T, E, K, N);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign))
+    return fail(MACAQ_EWORKSPACE, "%s: need %zu workspace bytes, 256-byte aligned", who, need);
+  st = check_device();
+  if (st != MACAQ_OK) return st;
+  const GemmPlan p = plan_gemm_grouped(T, E, N, K);
+  const int64_t max_mtiles = (T + p.bm - 1) / p.bm + E;
+  const LinearWs w = linear_ws(T, K, (size_t)max_mtiles * 2 * sizeof(int32_t));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  QuantArgs q{};
+  q.x = X;
+  q.M = T;
+  q.K = K;
+  q.ldx = K;
+  q.mult = a;
+  q.offsets = a ? offsets : nullptr;
+  q.E = E;
+  q.codes = ws + w.codes_off;
+  q.scales = ws + w.scales_off;
+  hipError_t e = launch_quant_rows(q, b, false, s);
+  if (e != hipSuccess) return hip_fail(e, "macaq_linear_grouped quantize launch");
+  GemmArgs g{};
+  g.a_codes = q.codes;
+  g.a_scales = q.scales;
+  g.b_codes = w_codes;
+  g.b_scales = w_scales;
+  g.M = T;
+  g.N = N;
+  g.K = K;
+  g.y = Y;
+  g.ldy = N;
+  g.y_bf16 = y_dtype == MACAQ_BF16;
+  g.splits = 1;
+  g.offsets = offsets;
+  g.tile_map = reinterpret_cast<int32_t*>(ws + w.extra_off);
+  g.E = E;
+  g.max_mtiles = max_mtiles;
+  e = launch_gemm_grouped(g, p, s);
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_linear_grouped GEMM launch");
+}
+
+}  // extern "C"

@@ -151,8 +151,9 @@ static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
    neighbour with the even code (even mantissa bit). Above 6 saturates. */
 static unsigned e2m1_round_magnitude(double u) {
   if (u >= kE2M1[7]) return 7;
+  if (!(u >= 0.0)) return 0; /* NaN: inputs must be finite; any code, no crash */
   unsigned c = 0;
-  while (!(u < kE2M1[c + 1])) ++c; /* kE2M1[c] <= u < kE2M1[c+1] */
+  while (c < 6 && !(u < kE2M1[c + 1])) ++c; /* kE2M1[c] <= u < kE2M1[c+1] */
   double mid = 0.5 * (kE2M1[c] + kE2M1[c + 1]);
   if (u < mid) return c;
   if (u > mid) return c + 1;

@@ -1,0 +1,70 @@
+"""Comparison helpers for the GPU parity tests (HIP path vs the CPU oracle)."""
+import sys
+
+import numpy as np
+import torch
+
+# Output tolerance: relative L2 error of the fp32 output against the oracle's
+# fp64 accumulation of the same codes.
+REL_L2_TOL = 1e-3
+# Code tolerance: at most this fraction of codes may differ, each by one step
+# of magnitude at a rounding tie within one fp32 ulp of the oracle's value.
+CODE_SLIP_FRACTION = 1e-5
+
+
+def log(msg: str):
+    print("[parity] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def np_u8(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def rel_l2(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def unpack(codes: np.ndarray) -> np.ndarray:
+    return np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(codes.shape[0], -1)
+
+
+_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def assert_quant_equal(g_codes, g_scales, o_codes, o_scales, t_oracle=None, what=""):
+    """Scales bit-exact; codes bit-exact except for the allowed tie slips."""
+    g_codes, o_codes = np.asarray(g_codes), np.asarray(o_codes)
+    assert np.array_equal(np.asarray(g_scales), np.asarray(o_scales)), "%s: E8M0 scales differ" % what
+    if np.array_equal(g_codes, o_codes):
+        return
+    gu, ou = unpack(g_codes), unpack(o_codes)
+    bad = np.argwhere(gu != ou)
+    frac = len(bad) / gu.size
+    assert t_oracle is not None, "%s: %d codes differ and no pre-quant values to judge ties" % (what, len(bad))
+    assert frac <= CODE_SLIP_FRACTION, "%s: %d codes differ (%.2e of all)" % (what, len(bad), frac)
+    sc = np.asarray(o_scales).astype(np.int64)
+    for r, k in bad:
+        gcode, ocode = int(gu[r, k]), int(ou[r, k])
+        assert (gcode & 8) == (ocode & 8) and abs((gcode & 7) - (ocode & 7)) == 1, \
+            "%s: code %d vs %d at (%d, %d) not adjacent" % (what, gcode, ocode, r, k)
+        t = np.float32(t_oracle[r, k])
+        u = abs(float(t)) * 2.0 ** (127 - sc[r, k // 32])
+        ulp = float(np.spacing(np.float32(abs(t)))) * 2.0 ** (127 - sc[r, k // 32])
+        assert np.min(np.abs(_MIDS - u)) <= ulp, "%s: slip at (%d, %d) is not at a tie" % (what, r, k)
+
+
+def assert_bf16_close(y_bf16: torch.Tensor, y_ref: np.ndarray, what=""):
+    """bf16 output within one bf16 ulp of the oracle value rounded to bf16."""
+    got = y_bf16.detach().float().cpu().numpy().astype(np.float64)
+    ref = torch.from_numpy(np.asarray(y_ref, np.float64)).float().to(torch.bfloat16).float().numpy().astype(np.float64)
+    ulp = np.maximum(np.abs(ref), 1e-30) * 2.0 ** -7
+    assert np.all(np.abs(got - ref) <= ulp + 1e-30), "%s: bf16 output off by more than one ulp" % what
+    assert rel_l2(got, y_ref) < 1e-2, what

@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports what include/macaq.h declares, and rejects
+bad arguments on the host, before touching any device (no GPU needed: only
+argument checks run, no kernel is launched and no pointer is dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mxfp4_w4a4_post_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "macaq.h")
+
+OK, EINVAL, EALIGN, EWORKSPACE, EUNSUPPORTED, EHIP = range(6)
+FAKE = 0x10000  # an aligned address that is never dereferenced: every call below fails its host checks first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(macaq_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 12, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding._SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        s = lib.macaq_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.macaq_status_string(99).decode() == "unknown status"
+
+
+def _last(lib):
+    return lib.macaq_last_error().decode()
+
+
+def test_quant_act_rejects(lib):
+    f = lib.macaq_quant_act
+    assert f(None, 4, 64, 64, None, 32, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, 4, 48, 48, None, 0, FAKE, FAKE, None) == EINVAL  # K % 32
+    assert "multiple of 32" in _last(lib)
+    assert f(FAKE, 4, 96, 96, None, 64, FAKE, FAKE, None) == EINVAL  # K % b
+    assert f(FAKE, 4, 64, 64, None, 16, FAKE, FAKE, None) == EINVAL  # b not allowed
+    assert f(FAKE, 4, 64, 32, None, 32, FAKE, FAKE, None) == EINVAL  # ldx < K
+    assert f(FAKE, -1, 64, 64, None, 32, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE + 2, 4, 64, 64, None, 32, FAKE, FAKE, None) == EALIGN
+    assert f(FAKE, 4, 64, 68, None, 32, FAKE, FAKE, None) == EALIGN  # ldx not a multiple of 8
+    assert f(FAKE, 4, 64, 64, FAKE + 4, 32, FAKE, FAKE, None) == EALIGN
+    assert f(FAKE, 0, 64, 64, None, 32, FAKE, FAKE, None) == OK  # empty: nothing to do
+
+
+def test_prepare_weights_rejects(lib):
+    f = lib.macaq_prepare_weights
+    assert f(FAKE, 7, 8, 64, 64, None, 32, FAKE, FAKE, None) == EINVAL  # dtype
+    assert f(FAKE, 1, 8, 64, 66, None, 32, FAKE, FAKE, None) == EALIGN  # fp32 rows not 16-byte multiples
+    assert f(FAKE, 0, 8, 64, 64, None, 32, None, FAKE, None) == EINVAL
+    assert f(FAKE, 0, 0, 64, 64, None, 32, FAKE, FAKE, None) == OK
+
+
+def test_linear_rejects(lib):
+    f = lib.macaq_linear
+    good = dict(X=FAKE, M=4, K=64, ldx=64, a=None, b=32, wc=FAKE, ws=FAKE, N=16, Y=FAKE, dt=0, ldy=16)
+
+    def call(**kw):
+        d = dict(good)
+        d.update(kw)
+        return f(d["X"], d["M"], d["K"], d["ldx"], d["a"], d["b"], d["wc"], d["ws"], d["N"], d["Y"], d["dt"],
+                 d["ldy"], kw.get("wsp", FAKE), kw.get("wsb", 0), None)
+
+    assert call(N=0) == EINVAL
+    assert call(ldy=8) == EINVAL
+    assert call(dt=3) == EINVAL
+    assert call(Y=None) == EINVAL
+    assert call(ldy=18) == EALIGN
+    assert call(Y=FAKE + 8) == EALIGN
+    need = lib.macaq_linear_workspace_size(4, 64, 16)
+    assert need > 0
+    assert call(wsb=need - 1) == EWORKSPACE
+    assert call(wsp=FAKE + 16, wsb=need) == EWORKSPACE  # workspace must be 256-byte aligned
+    assert call(wsp=None, wsb=need) == EWORKSPACE
+    assert call(M=0) == OK
+
+
+def test_gemm_and_grouped_reject(lib):
+    assert lib.macaq_gemm(FAKE, FAKE, 4, 40, FAKE, FAKE, 16, FAKE, 0, 16, FAKE, 0, None) == EINVAL
+    assert lib.macaq_gemm(FAKE, FAKE, 4, 64, FAKE + 1, FAKE, 16, FAKE, 0, 16, FAKE, 0, None) == EALIGN
+    g = lib.macaq_linear_grouped
+    assert g(FAKE, FAKE, 0, 16, 64, None, 0, FAKE, FAKE, 8, FAKE, 0, FAKE, 0, None) == EINVAL  # E < 1
+    assert g(FAKE, None, 2, 16, 64, None, 0, FAKE, FAKE, 8, FAKE, 0, FAKE, 0, None) == EINVAL
+    assert g(FAKE, FAKE, 2, 16, 64, None, 0, FAKE, FAKE, 8, FAKE, 0, FAKE, 0, None) == EWORKSPACE
+    assert g(FAKE, FAKE, 2, 0, 64, None, 0, FAKE, FAKE, 8, FAKE, 0, FAKE, 0, None) == OK
+
+
+def test_calibrate_and_multipliers_reject(lib):
+    assert lib.macaq_calibrate(FAKE, 0, 8, 8, FAKE, None) == EINVAL
+    assert lib.macaq_calibrate(FAKE, 4, 8, 4, FAKE, None) == EINVAL
+    assert lib.macaq_calibrate(FAKE + 1, 4, 8, 8, FAKE, None) == EALIGN
+    assert lib.macaq_make_multipliers(FAKE, 8, 48, FAKE, FAKE, None) == EINVAL
+    assert lib.macaq_make_multipliers(FAKE, 8, 32, None, None, None) == EINVAL
+    assert lib.macaq_make_multipliers(FAKE, 0, 32, FAKE, None, None) == EINVAL
+
+
+def test_workspace_sizes_cover_staging(lib):
+    # quantized activations staged in the workspace: codes + scales, 256-byte padded
+    for M, K, N in [(16, 256, 256), (2048, 4096, 4096), (1, 25600, 5120), (8192, 28672, 8192)]:
+        need = lib.macaq_linear_workspace_size(M, K, N)
+        assert need >= M * K // 2 + M * K // 32
+        assert need % 256 == 0
+    assert lib.macaq_linear_workspace_size(0, 64, 16) == 0
+    T, E, K, N = 32768, 128, 2048, 1536
+    assert lib.macaq_linear_grouped_workspace_size(T, E, K, N) >= T * K // 2 + T * K // 32
+
+
+def test_binding_has_no_cpu_fallback():
+    """The product path refuses CPU tensors instead of computing elsewhere."""
+    import torch
+    with pytest.raises(ValueError):
+        binding.quant_act(torch.zeros(4, 64, dtype=torch.bfloat16), None, 0)
