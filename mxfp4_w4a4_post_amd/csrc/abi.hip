@@ -90,7 +90,7 @@ macaq_status check_out(const void* Y, macaq_dtype dt, int64_t N, int64_t ldy, co
   if (!Y) return fail(MACAQ_EINVAL, "%s: Y is NULL", who);
   if (dt != MACAQ_BF16 && dt != MACAQ_F32) return fail(MACAQ_EINVAL, "%s: bad output dtype %d", who, (int)dt);
   if (ldy < N) return fail(MACAQ_EINVAL, "%s: ldy = %lld < N = %lld", who, (long long)ldy, (long long)N);
-  if (!aligned(Y, 16) || ldy % 4 != 0) return fail(MACAQ_EALIGN, "%s: Y must be 16-byte aligned, ldy a multiple of 4", who);
+  if (!aligned(Y, dt == MACAQ_F32 ? 4 : 2)) return fail(MACAQ_EALIGN, "%s: Y not aligned to its element size", who);
   return MACAQ_OK;
 }
 
@@ -140,10 +140,11 @@ macaq_status macaq_prepare_weights(const void* W, macaq_dtype w_dtype, int64_t N
                                    const float* r, int32_t b, uint8_t* w_codes, uint8_t* w_scales,
                                    macaq_stream_t stream) {
   const char* who = "macaq_prepare_weights";
-  if (!W || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
   if (w_dtype != MACAQ_BF16 && w_dtype != MACAQ_F32) return fail(MACAQ_EINVAL, "%s: bad weight dtype", who);
   macaq_status st = check_quant_shape(N, K, ldw, b, who);
   if (st != MACAQ_OK) return st;
+  if (N == 0) return MACAQ_OK;
+  if (!W || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
   const size_t esz = w_dtype == MACAQ_F32 ? 4 : 2;
   if (!aligned(W, 16) || (ldw * (int64_t)esz) % 16 != 0 || !aligned(w_codes, 16) || !aligned(w_scales, 16) ||
       (r && !aligned(r, 16)))
@@ -166,9 +167,10 @@ macaq_status macaq_prepare_weights(const void* W, macaq_dtype w_dtype, int64_t N
 macaq_status macaq_quant_act(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
                              uint8_t* a_codes, uint8_t* a_scales, macaq_stream_t stream) {
   const char* who = "macaq_quant_act";
-  if (!X || !a_codes || !a_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
   macaq_status st = check_quant_shape(M, K, ldx, b, who);
   if (st != MACAQ_OK) return st;
+  if (M == 0) return MACAQ_OK;
+  if (!X || !a_codes || !a_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
   if (!aligned(X, 16) || ldx % 8 != 0 || !aligned(a_codes, 16) || !aligned(a_scales, 16) || (a && !aligned(a, 16)))
     return fail(MACAQ_EALIGN, "%s: X, a, a_codes, a_scales must be 16-byte aligned and ldx a multiple of 8", who);
   if (M == 0) return MACAQ_OK;
@@ -221,9 +223,10 @@ macaq_status macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t
                         const uint8_t* w_scales, int64_t N, void* Y, macaq_dtype y_dtype, int64_t ldy,
                         void* workspace, size_t workspace_bytes, macaq_stream_t stream) {
   const char* who = "macaq_gemm";
-  if (!a_codes || !a_scales || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
   if (M < 0 || N < 1) return fail(MACAQ_EINVAL, "%s: need M >= 0, N >= 1", who);
   if (K < 32 || K % 32 != 0) return fail(MACAQ_EINVAL, "%s: K is not a positive multiple of 32", who);
+  if (M == 0) return MACAQ_OK;
+  if (!a_codes || !a_scales || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
   macaq_status st = check_out(Y, y_dtype, N, ldy, who);
   if (st != MACAQ_OK) return st;
   if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 16) || !aligned(w_scales, 16))
@@ -242,10 +245,11 @@ macaq_status macaq_linear(const void* X, int64_t M, int64_t K, int64_t ldx, cons
                           const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, void* Y, macaq_dtype y_dtype,
                           int64_t ldy, void* workspace, size_t workspace_bytes, macaq_stream_t stream) {
   const char* who = "macaq_linear";
-  if (!X || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
   macaq_status st = check_quant_shape(M, K, ldx, b, who);
   if (st != MACAQ_OK) return st;
   if (N < 1) return fail(MACAQ_EINVAL, "%s: N < 1", who);
+  if (M == 0) return MACAQ_OK;
+  if (!X || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
   st = check_out(Y, y_dtype, N, ldy, who);
   if (st != MACAQ_OK) return st;
   if (!aligned(X, 16) || ldx % 8 != 0 || (a && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 16))
@@ -285,11 +289,12 @@ macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t
                                   int64_t N, void* Y, macaq_dtype y_dtype, void* workspace, size_t workspace_bytes,
                                   macaq_stream_t stream) {
   const char* who = "macaq_linear_grouped";
-  if (!X || !offsets || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
   if (E < 1) return fail(MACAQ_EINVAL, "%s: E < 1", who);
   macaq_status st = check_quant_shape(T, K, K, b, who);
   if (st != MACAQ_OK) return st;
   if (N < 1) return fail(MACAQ_EINVAL, "%s: N < 1", who);
+  if (T == 0) return MACAQ_OK;
+  if (!X || !offsets || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
   st = check_out(Y, y_dtype, N, N, who);
   if (st != MACAQ_OK) return st;
   if (!aligned(X, 16) || (a && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 16) ||
