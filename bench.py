@@ -83,21 +83,24 @@ def build_layers(torch, binding, inputs, cfg, shapes, M, b, dev):
         w = case.w.to(dev)
         s = binding.calibrate(case.xcal.to(dev))
         a, r = binding.make_multipliers(s, b)
-        wc, ws = binding.prepare_weights(w, r, b)
-        pc, ps = binding.prepare_weights(w, None, 0)
+        w_fused = binding.prepare_weights(w, r, b)
+        w_plain = binding.prepare_weights(w, None, 0)
         del w
-        copies = []
-        for i in range(ROTATE):
-            copies.append(dict(x=x.clone(), wc=wc.clone(), ws=ws.clone(), pc=pc.clone(), ps=ps.clone()))
-        del x, wc, ws, pc, ps
+
+        def clone(p):
+            return binding.Packed(p.codes.clone(), p.scales.clone(), p.rows, p.K)
+
+        copies = [dict(x=x.clone(), w=clone(w_fused), wp=clone(w_plain)) for _ in range(ROTATE)]
+        del x, w_fused, w_plain
         ws_bytes = binding.linear_workspace_size(M, K, N)
+        qa = binding.Packed(torch.empty(binding.packed_codes_bytes(M, K), dtype=torch.uint8, device=dev),
+                            torch.empty(binding.packed_scales_bytes(M, K), dtype=torch.uint8, device=dev), M, K)
         layers.append(dict(K=K, N=N, M=M, a=a, b=b, case=case, copies=copies,
                            y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
                            work=torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev),
                            gwork=torch.empty(max(binding.gemm_workspace_size(M, K, N), 1), dtype=torch.uint8,
                                              device=dev),
-                           qa=torch.empty(M, K // 2, dtype=torch.uint8, device=dev),
-                           qs=torch.empty(M, K // 32, dtype=torch.uint8, device=dev)))
+                           qa=qa))
     return layers
 
 
@@ -106,9 +109,9 @@ def run_steps(torch, binding, layers, steps, offset, plain=False):
         for L in layers:
             c = L["copies"][(offset + i) % ROTATE]
             if plain:
-                binding.linear(c["x"], None, 0, c["pc"], c["ps"], out=L["y"], workspace=L["work"])
+                binding.linear(c["x"], None, 0, c["wp"], out=L["y"], workspace=L["work"])
             else:
-                binding.linear(c["x"], L["a"], L["b"], c["wc"], c["ws"], out=L["y"], workspace=L["work"])
+                binding.linear(c["x"], L["a"], L["b"], c["w"], out=L["y"], workspace=L["work"])
 
 
 def timed(torch, fn, steps, warmup):
@@ -131,9 +134,9 @@ def kernel_breakdown(torch, binding, layers, steps):
         for li, L in enumerate(layers):
             c = L["copies"][i % ROTATE]
             with Timer(torch) as tq:
-                binding.quant_act(c["x"], L["a"], L["b"], codes=L["qa"], scales=L["qs"])
+                binding.quant_act(c["x"], L["a"], L["b"], layout="gemm", codes=L["qa"].codes, scales=L["qa"].scales)
             with Timer(torch) as tg:
-                binding.linear_plain_gemm(L["qa"], L["qs"], c["wc"], c["ws"], out=L["y"], workspace=L["gwork"])
+                binding.linear_plain_gemm(L["qa"], c["w"], out=L["y"], workspace=L["gwork"])
             torch.cuda.synchronize()
             q_ms[li] += tq.ms()
             g_ms[li] += tg.ms()

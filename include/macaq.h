@@ -25,8 +25,19 @@
  *     scale 2^(floor(log2 amax) - 2), clamped to >= 2^-127; elements are E2M1
  *     codes (sign bit 3; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6) rounded to
  *     nearest, ties to the even code, saturating at 6.
- *   - Packed codes: uint8 [rows, K/2], row-major, element 2i in the low nibble
- *     of byte i. Scales: uint8 [rows, K/32], row-major, E8M0 (bias 127).
+ *   - Packed operands come in one of two layouts. Codes hold element 2i in
+ *     the low nibble and 2i+1 in the high nibble of a byte; scales are E8M0
+ *     bytes (bias 127), one per 32 elements along K.
+ *       MACAQ_ROW_MAJOR: codes uint8 [rows, K/2], scales uint8 [rows, K/32].
+ *       MACAQ_GEMM_LAYOUT (what the GEMM reads): rows padded to RP =
+ *         ceil(rows/64)*64 and K to KP = ceil(K/128)*128, the padding all
+ *         zero bytes; with KB = KP/128,
+ *           code byte of (r, k): ((r/16)*KB + k/128)*1024 + (r%16)*64 + (k%128)/2
+ *           scale of (r, g = k/32): ((r/64)*KB + g/4)*256 + (r%64)*4 + g%4
+ *         so one step of 128 elements of 16 rows is a contiguous 1 KiB block
+ *         and the scales of 64 rows a contiguous 256-byte block. Sizes:
+ *         macaq_packed_codes_bytes / macaq_packed_scales_bytes; each packed
+ *         operand must stay under 2 GiB.
  *   - Activations X are bf16 [M, ldx] row-major. Outputs Y are [M, ldy]
  *     row-major, fp32 or bf16 (round-to-nearest-even).
  *
@@ -66,6 +77,13 @@ typedef enum {
 
 typedef enum { MACAQ_BF16 = 0, MACAQ_F32 = 1 } macaq_dtype;
 
+typedef enum { MACAQ_ROW_MAJOR = 0, MACAQ_GEMM_LAYOUT = 1 } macaq_layout;
+
+/* Bytes of the codes / scales of a rows x K operand in MACAQ_GEMM_LAYOUT
+   (0 for an empty operand). */
+size_t macaq_packed_codes_bytes(int64_t rows, int64_t K);
+size_t macaq_packed_scales_bytes(int64_t rows, int64_t K);
+
 /* Text for a status code (static storage). */
 const char* macaq_status_string(macaq_status s);
 
@@ -96,9 +114,10 @@ macaq_status macaq_make_multipliers(const float* s, int64_t K, int32_t b, float*
  * weights; round-to-nearest MXFP4): W' = MXFP4(rows of S_b (r .* W[n, :])).
  * W: device [N, ldw] of w_dtype (bf16 or fp32), row n = output channel n.
  * r: device fp32 [K] from macaq_make_multipliers, or NULL with b = 0 for
- * plain MXFP4 weights. w_codes: device [N, K/2]; w_scales: device [N, K/32].
+ * plain MXFP4 weights. w_codes / w_scales: device, MACAQ_GEMM_LAYOUT,
+ * macaq_packed_codes_bytes(N, K) / macaq_packed_scales_bytes(N, K) bytes.
  * Requires K % 32 == 0, K % b == 0, ldw >= K; W, w_codes and w_scales 16-byte
- * aligned and ldw a multiple of 8 elements.
+ * aligned and rows of W a multiple of 16 bytes.
  */
 macaq_status macaq_prepare_weights(const void* W, macaq_dtype w_dtype, int64_t N, int64_t K, int64_t ldw,
                                    const float* r, int32_t b, uint8_t* w_codes, uint8_t* w_scales,
@@ -109,11 +128,12 @@ macaq_status macaq_prepare_weights(const void* W, macaq_dtype w_dtype, int64_t N
  * scale and block-Hadamard applied online to the activations, then MXFP4):
  * a_codes/a_scales = MXFP4(rows of S_b (a .* X[m, :])).
  * X: device bf16 [M, ldx]; a: device fp32 [K] or NULL (no scale); b in
- * {0, 32, 64, 128}. a_codes: device [M, K/2]; a_scales: device [M, K/32].
- * Alignment as macaq_prepare_weights. M = 0 is allowed and does nothing.
+ * {0, 32, 64, 128}. a_codes / a_scales: device, in `layout` (row-major
+ * [M, K/2] / [M, K/32], or the GEMM layout). Alignment as
+ * macaq_prepare_weights. M = 0 does nothing (pointers are not checked).
  */
 macaq_status macaq_quant_act(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
-                             uint8_t* a_codes, uint8_t* a_scales, macaq_stream_t stream);
+                             macaq_layout layout, uint8_t* a_codes, uint8_t* a_scales, macaq_stream_t stream);
 
 /* Bytes of workspace that macaq_linear needs for these sizes. */
 size_t macaq_linear_workspace_size(int64_t M, int64_t K, int64_t N);
@@ -126,7 +146,7 @@ size_t macaq_linear_workspace_size(int64_t M, int64_t K, int64_t N);
  * MXFP4); w_codes/w_scales: device, from macaq_prepare_weights with the
  * matching r and b; Y: device [M, ldy] of y_dtype; workspace: device, at least
  * macaq_linear_workspace_size(M, K, N) bytes, 256-byte aligned.
- * Requires ldy >= N, ldy a multiple of 4 elements, Y 16-byte aligned.
+ * Requires ldy >= N and Y aligned to its element size. M = 0 does nothing.
  */
 macaq_status macaq_linear(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
                           const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, void* Y,
@@ -137,7 +157,8 @@ macaq_status macaq_linear(const void* X, int64_t M, int64_t K, int64_t ldx, cons
  * The GEMM alone on operands already in MXFP4 (the contraction step of
  * macaq_linear; also the baseline for the cost of the activation transform):
  * Y[m, n] = sum_k dq(A[m, k]) dq(W'[n, k]).
- * a_codes/a_scales: device [M, K/2] / [M, K/32]; other arguments as
+ * a_codes/a_scales: device, MACAQ_GEMM_LAYOUT for M rows (macaq_quant_act
+ * with that layout); w_codes/w_scales as macaq_linear; other arguments as
  * macaq_linear.
  */
 size_t macaq_gemm_workspace_size(int64_t M, int64_t K, int64_t N);
@@ -157,8 +178,9 @@ size_t macaq_linear_grouped_workspace_size(int64_t T, int32_t E, int64_t K, int6
  * X: device bf16 [T, K] (contiguous, expert-major); offsets: device int32
  * [E+1], non-decreasing, offsets[0] = 0, offsets[E] = T (not checked on the
  * host: it lives on the device); a: device fp32 [E, K] or NULL with b = 0;
- * w_codes: device [E, N, K/2]; w_scales: device [E, N, K/32]; Y: device
- * [T, N] of y_dtype (row t is written for every t < T).
+ * w_codes / w_scales: E prepared weights one after another, expert e at
+ * e * macaq_packed_codes_bytes(N, K) / e * macaq_packed_scales_bytes(N, K);
+ * Y: device [T, N] of y_dtype (row t is written for every t < T).
  */
 macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t E, int64_t T, int64_t K,
                                   const float* a, int32_t b, const uint8_t* w_codes, const uint8_t* w_scales,

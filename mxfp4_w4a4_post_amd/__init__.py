@@ -7,7 +7,8 @@ use so that the input generators load without the HIP library.
 """
 
 _BINDING_NAMES = {
-    "MacaqError", "Layer", "calibrate", "make_multipliers", "prepare_weights", "prepare_layer", "quant_act",
+    "MacaqError", "Layer", "Packed", "packed_codes_bytes", "packed_scales_bytes", "empty_grouped_weights", "expert",
+    "calibrate", "make_multipliers", "prepare_weights", "prepare_layer", "quant_act",
     "linear", "linear_plain_gemm", "linear_grouped", "linear_workspace_size", "gemm_workspace_size",
     "linear_grouped_workspace_size", "load_library", "library_path",
 }

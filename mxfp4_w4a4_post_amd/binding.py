@@ -10,6 +10,7 @@ from __future__ import annotations
 import ctypes
 import os
 import threading
+from typing import NamedTuple
 
 import torch
 
@@ -20,18 +21,22 @@ _lock = threading.Lock()
 
 MACAQ_BF16 = 0
 MACAQ_F32 = 1
+MACAQ_ROW_MAJOR = 0
+MACAQ_GEMM_LAYOUT = 1
 _STATUS_NAMES = {0: "MACAQ_OK", 1: "MACAQ_EINVAL", 2: "MACAQ_EALIGN", 3: "MACAQ_EWORKSPACE",
                  4: "MACAQ_EUNSUPPORTED", 5: "MACAQ_EHIP"}
 
 # name -> (restype, argtypes), in the order of include/macaq.h
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _SIGNATURES = {
+    "macaq_packed_codes_bytes": (_sz, [_i64, _i64]),
+    "macaq_packed_scales_bytes": (_sz, [_i64, _i64]),
     "macaq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "macaq_last_error": (ctypes.c_char_p, []),
     "macaq_calibrate": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
     "macaq_make_multipliers": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
     "macaq_prepare_weights": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp]),
-    "macaq_quant_act": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp]),
+    "macaq_quant_act": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, ctypes.c_int, _vp, _vp, _vp]),
     "macaq_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
     "macaq_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64, _vp, ctypes.c_int, _i64,
                                     _vp, _sz, _vp]),
@@ -41,6 +46,17 @@ _SIGNATURES = {
     "macaq_linear_grouped": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _i64, _vp,
                                             ctypes.c_int, _vp, _sz, _vp]),
 }
+
+
+class Packed(NamedTuple):
+    """An MXFP4 operand in the GEMM layout: `rows` x `K` elements (padded to 64
+    rows and a multiple of 128 in K inside the buffers). codes / scales are
+    uint8 tensors of packed_codes_bytes / packed_scales_bytes bytes (with a
+    leading expert dimension for grouped weights)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rows: int
+    K: int
 
 
 class MacaqError(RuntimeError):
@@ -127,32 +143,47 @@ def make_multipliers(s: torch.Tensor, b: int):
     return a, r
 
 
-def prepare_weights(w: torch.Tensor, r: torch.Tensor | None, b: int):
-    """W' = MXFP4(W D^-1 H^T): (codes uint8 [N, K/2], scales uint8 [N, K/32])."""
+def packed_codes_bytes(rows: int, K: int) -> int:
+    return int(load_library().macaq_packed_codes_bytes(rows, K))
+
+
+def packed_scales_bytes(rows: int, K: int) -> int:
+    return int(load_library().macaq_packed_scales_bytes(rows, K))
+
+
+def prepare_weights(w: torch.Tensor, r: torch.Tensor | None, b: int, out: Packed | None = None) -> Packed:
+    """W' = MXFP4(W D^-1 H^T) in the GEMM layout."""
     _need_cuda(w, r)
     assert w.dim() == 2 and w.stride(1) == 1
     N, K = w.shape
-    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=w.device)
-    scales = torch.empty(N, K // 32, dtype=torch.uint8, device=w.device)
+    if out is None:
+        out = Packed(torch.empty(packed_codes_bytes(N, K), dtype=torch.uint8, device=w.device),
+                     torch.empty(packed_scales_bytes(N, K), dtype=torch.uint8, device=w.device), N, K)
     _check(load_library().macaq_prepare_weights(_ptr(w), _dtype_code(w.dtype), N, K, w.stride(0), _ptr(r), b,
-                                                _ptr(codes), _ptr(scales), _stream(w)), "macaq_prepare_weights")
-    return codes, scales
+                                                _ptr(out.codes), _ptr(out.scales), _stream(w)), "macaq_prepare_weights")
+    return out
 
 
-def quant_act(x: torch.Tensor, a: torch.Tensor | None, b: int, codes: torch.Tensor | None = None,
+def quant_act(x: torch.Tensor, a: torch.Tensor | None, b: int, layout: str = "row", codes: torch.Tensor | None = None,
               scales: torch.Tensor | None = None):
-    """MXFP4(H D x) of bf16 rows: (codes uint8 [M, K/2], scales uint8 [M, K/32])."""
+    """MXFP4(H D x) of bf16 rows. layout "row": (codes [M, K/2], scales [M, K/32]);
+    layout "gemm": a Packed operand in the GEMM layout."""
     _need_cuda(x, a, codes, scales)
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
     M, K = x.shape
+    gemm = layout == "gemm"
+    if not gemm and layout != "row":
+        raise ValueError("layout is 'row' or 'gemm'")
     if codes is None:
-        codes = torch.empty(M, K // 2, dtype=torch.uint8, device=x.device)
+        codes = (torch.empty(packed_codes_bytes(M, K), dtype=torch.uint8, device=x.device) if gemm
+                 else torch.empty(M, K // 2, dtype=torch.uint8, device=x.device))
     if scales is None:
-        scales = torch.empty(M, K // 32, dtype=torch.uint8, device=x.device)
-    assert codes.is_contiguous() and codes.shape == (M, K // 2) and scales.is_contiguous() and scales.shape == (M, K // 32)
-    _check(load_library().macaq_quant_act(_ptr(x), M, K, x.stride(0), _ptr(a), b, _ptr(codes), _ptr(scales),
+        scales = (torch.empty(packed_scales_bytes(M, K), dtype=torch.uint8, device=x.device) if gemm
+                  else torch.empty(M, K // 32, dtype=torch.uint8, device=x.device))
+    _check(load_library().macaq_quant_act(_ptr(x), M, K, x.stride(0), _ptr(a), b,
+                                          MACAQ_GEMM_LAYOUT if gemm else MACAQ_ROW_MAJOR, _ptr(codes), _ptr(scales),
                                           _stream(x)), "macaq_quant_act")
-    return codes, scales
+    return Packed(codes, scales, M, K) if gemm else (codes, scales)
 
 
 def linear_workspace_size(M: int, K: int, N: int) -> int:
@@ -173,65 +204,74 @@ def _workspace(nbytes: int, device, given: torch.Tensor | None):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def linear(x: torch.Tensor, a: torch.Tensor | None, b: int, w_codes: torch.Tensor, w_scales: torch.Tensor,
-           out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
-           workspace: torch.Tensor | None = None) -> torch.Tensor:
+def linear(x: torch.Tensor, a: torch.Tensor | None, b: int, w: Packed, out_dtype: torch.dtype = torch.bfloat16,
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """y = W' MXFP4(H D x) for bf16 rows x [M, K]; returns [M, N] of out_dtype."""
-    _need_cuda(x, a, w_codes, w_scales)
+    _need_cuda(x, a, w.codes, w.scales)
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
     M, K = x.shape
-    N = w_codes.shape[0]
+    assert K == w.K, "activation K %d does not match the weights' %d" % (K, w.K)
+    N = w.rows
     y = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=x.device)
-    ws_bytes = linear_workspace_size(M, K, N)
-    ws = _workspace(ws_bytes, x.device, workspace)
-    _check(load_library().macaq_linear(_ptr(x), M, K, x.stride(0), _ptr(a), b, _ptr(w_codes), _ptr(w_scales), N,
+    ws = _workspace(linear_workspace_size(M, K, N), x.device, workspace)
+    _check(load_library().macaq_linear(_ptr(x), M, K, x.stride(0), _ptr(a), b, _ptr(w.codes), _ptr(w.scales), N,
                                        _ptr(y), _dtype_code(y.dtype), y.stride(0), _ptr(ws), ws.numel(), _stream(x)),
            "macaq_linear")
     return y
 
 
-def linear_plain_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
-                      out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+def linear_plain_gemm(a: Packed, w: Packed, out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
                       workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """The GEMM alone on MXFP4 operands: y = dq(A) dq(W')^T."""
-    _need_cuda(a_codes, a_scales, w_codes, w_scales)
-    M, K = a_codes.shape[0], 2 * a_codes.shape[1]
-    N = w_codes.shape[0]
-    y = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
-    ws = _workspace(gemm_workspace_size(M, K, N), a_codes.device, workspace)
-    _check(load_library().macaq_gemm(_ptr(a_codes), _ptr(a_scales), M, K, _ptr(w_codes), _ptr(w_scales), N, _ptr(y),
+    """The GEMM alone on MXFP4 operands in the GEMM layout: y = dq(A) dq(W')^T."""
+    _need_cuda(a.codes, a.scales, w.codes, w.scales)
+    assert a.K == w.K
+    M, K, N = a.rows, a.K, w.rows
+    y = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=a.codes.device)
+    ws = _workspace(gemm_workspace_size(M, K, N), a.codes.device, workspace)
+    _check(load_library().macaq_gemm(_ptr(a.codes), _ptr(a.scales), M, K, _ptr(w.codes), _ptr(w.scales), N, _ptr(y),
                                      _dtype_code(y.dtype), y.stride(0), _ptr(ws), ws.numel(),
-                                     _stream(a_codes)), "macaq_gemm")
+                                     _stream(a.codes)), "macaq_gemm")
     return y
 
 
-def linear_grouped(x: torch.Tensor, offsets: torch.Tensor, a: torch.Tensor | None, b: int, w_codes: torch.Tensor,
-                   w_scales: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+def linear_grouped(x: torch.Tensor, offsets: torch.Tensor, a: torch.Tensor | None, b: int, w: Packed,
+                   out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
                    workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Per expert e: rows [off[e], off[e+1]) of x through a[e] and W'_e [N, K]."""
-    _need_cuda(x, offsets, a, w_codes, w_scales)
+    """Per expert e: rows [off[e], off[e+1]) of x through a[e] and W'_e; w holds
+    the E experts' prepared weights stacked along dimension 0."""
+    _need_cuda(x, offsets, a, w.codes, w.scales)
     assert x.dtype == torch.bfloat16 and x.is_contiguous() and offsets.dtype == torch.int32
     T, K = x.shape
     E = offsets.numel() - 1
-    N = w_codes.shape[1]
+    N = w.rows
+    assert w.codes.shape[0] == E and w.codes[0].numel() == packed_codes_bytes(N, K)
     y = out if out is not None else torch.empty(T, N, dtype=out_dtype, device=x.device)
     ws = _workspace(linear_grouped_workspace_size(T, E, K, N), x.device, workspace)
-    _check(load_library().macaq_linear_grouped(_ptr(x), _ptr(offsets), E, T, K, _ptr(a), b, _ptr(w_codes),
-                                               _ptr(w_scales), N, _ptr(y), _dtype_code(y.dtype), _ptr(ws),
+    _check(load_library().macaq_linear_grouped(_ptr(x), _ptr(offsets), E, T, K, _ptr(a), b, _ptr(w.codes),
+                                               _ptr(w.scales), N, _ptr(y), _dtype_code(y.dtype), _ptr(ws),
                                                ws.numel(), _stream(x)), "macaq_linear_grouped")
     return y
+
+
+def empty_grouped_weights(E: int, N: int, K: int, device) -> Packed:
+    """Storage for E experts' prepared weights (fill with prepare_weights(out=expert(w, e)))."""
+    return Packed(torch.empty(E, packed_codes_bytes(N, K), dtype=torch.uint8, device=device),
+                  torch.empty(E, packed_scales_bytes(N, K), dtype=torch.uint8, device=device), N, K)
+
+
+def expert(w: Packed, e: int) -> Packed:
+    return Packed(w.codes[e], w.scales[e], w.rows, w.K)
 
 
 class Layer:
     """A prepared layer: the activation multiplier a and W' codes/scales from
     the same calibration scale s and Hadamard block b."""
 
-    def __init__(self, a, r, b, w_codes, w_scales, s=None):
-        self.a, self.r, self.b = a, r, b
-        self.w_codes, self.w_scales, self.s = w_codes, w_scales, s
+    def __init__(self, a, r, b, w: Packed, s=None):
+        self.a, self.r, self.b, self.w, self.s = a, r, b, w, s
 
     def __call__(self, x, out_dtype=torch.bfloat16, out=None, workspace=None):
-        return linear(x, self.a, self.b, self.w_codes, self.w_scales, out_dtype, out, workspace)
+        return linear(x, self.a, self.b, self.w, out_dtype, out, workspace)
 
 
 def prepare_layer(w: torch.Tensor, xcal: torch.Tensor | None, b: int) -> Layer:
@@ -240,9 +280,7 @@ def prepare_layer(w: torch.Tensor, xcal: torch.Tensor | None, b: int) -> Layer:
     if xcal is None:
         if b != 0:
             raise ValueError("a Hadamard block without a calibration scale is not a MACaQ layer")
-        codes, scales = prepare_weights(w, None, 0)
-        return Layer(None, None, 0, codes, scales)
+        return Layer(None, None, 0, prepare_weights(w, None, 0))
     s = calibrate(xcal)
     a, r = make_multipliers(s, b)
-    codes, scales = prepare_weights(w, r, b)
-    return Layer(a, r, b, codes, scales, s)
+    return Layer(a, r, b, prepare_weights(w, r, b), s)

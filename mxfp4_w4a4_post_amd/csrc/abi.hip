@@ -64,6 +64,8 @@ macaq_status check_device() {
 constexpr size_t kWsAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Workspace of the layer calls: the quantized activations in the GEMM layout,
+// then call-specific extra space (split-K partial sums or the MoE tile map).
 struct LinearWs {
   size_t codes_off, scales_off, extra_off, total;
 };
@@ -71,11 +73,15 @@ struct LinearWs {
 LinearWs linear_ws(int64_t M, int64_t K, size_t extra_bytes) {
   LinearWs w;
   w.codes_off = 0;
-  w.scales_off = round_up((size_t)M * (size_t)(K / 2), kWsAlign);
-  w.extra_off = w.scales_off + round_up((size_t)M * (size_t)(K / 32), kWsAlign);
+  w.scales_off = round_up((size_t)tiled_codes_bytes(M, K), kWsAlign);
+  w.extra_off = w.scales_off + round_up((size_t)tiled_scales_bytes(M, K), kWsAlign);
   w.total = w.extra_off + round_up(extra_bytes, kWsAlign);
   return w;
 }
+
+// The GEMM addresses each packed operand through a 32-bit buffer range.
+constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - (int64_t(1) << 20);
+bool operand_fits(int64_t rows, int64_t K) { return tiled_codes_bytes(rows, K) <= kMaxOperandBytes; }
 
 macaq_status check_quant_shape(int64_t M, int64_t K, int64_t ld, int32_t b, const char* who) {
   if (M < 0) return fail(MACAQ_EINVAL, "%s: M = %lld < 0", who, (long long)M);
@@ -145,6 +151,7 @@ macaq_status macaq_prepare_weights(const void* W, macaq_dtype w_dtype, int64_t N
   if (st != MACAQ_OK) return st;
   if (N == 0) return MACAQ_OK;
   if (!W || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (!operand_fits(N, K)) return fail(MACAQ_EINVAL, "%s: packed weights over 2 GiB", who);
   const size_t esz = w_dtype == MACAQ_F32 ? 4 : 2;
   if (!aligned(W, 16) || (ldw * (int64_t)esz) % 16 != 0 || !aligned(w_codes, 16) || !aligned(w_scales, 16) ||
       (r && !aligned(r, 16)))
@@ -160,15 +167,30 @@ macaq_status macaq_prepare_weights(const void* W, macaq_dtype w_dtype, int64_t N
   q.mult = r;
   q.codes = w_codes;
   q.scales = w_scales;
+  q.tiled = true;
+  q.kpad = pad_k(K);
   hipError_t e = launch_quant_rows(q, b, w_dtype == MACAQ_F32, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_prepare_weights launch");
 }
 
+size_t macaq_packed_codes_bytes(int64_t rows, int64_t K) {
+  if (rows <= 0 || K <= 0) return 0;
+  return (size_t)tiled_codes_bytes(rows, K);
+}
+
+size_t macaq_packed_scales_bytes(int64_t rows, int64_t K) {
+  if (rows <= 0 || K <= 0) return 0;
+  return (size_t)tiled_scales_bytes(rows, K);
+}
+
 macaq_status macaq_quant_act(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
-                             uint8_t* a_codes, uint8_t* a_scales, macaq_stream_t stream) {
+                             macaq_layout layout, uint8_t* a_codes, uint8_t* a_scales, macaq_stream_t stream) {
   const char* who = "macaq_quant_act";
   macaq_status st = check_quant_shape(M, K, ldx, b, who);
   if (st != MACAQ_OK) return st;
+  if (layout != MACAQ_ROW_MAJOR && layout != MACAQ_GEMM_LAYOUT) return fail(MACAQ_EINVAL, "%s: bad layout", who);
+  if (layout == MACAQ_GEMM_LAYOUT && !operand_fits(M, K))
+    return fail(MACAQ_EINVAL, "%s: packed operand over 2 GiB", who);
   if (M == 0) return MACAQ_OK;
   if (!X || !a_codes || !a_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
   if (!aligned(X, 16) || ldx % 8 != 0 || !aligned(a_codes, 16) || !aligned(a_scales, 16) || (a && !aligned(a, 16)))
@@ -184,6 +206,8 @@ macaq_status macaq_quant_act(const void* X, int64_t M, int64_t K, int64_t ldx, c
   q.mult = a;
   q.codes = a_codes;
   q.scales = a_scales;
+  q.tiled = layout == MACAQ_GEMM_LAYOUT;
+  q.kpad = pad_k(K);
   hipError_t e = launch_quant_rows(q, b, false, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_quant_act launch");
 }
@@ -227,6 +251,7 @@ macaq_status macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t
   if (K < 32 || K % 32 != 0) return fail(MACAQ_EINVAL, "%s: K is not a positive multiple of 32", who);
   if (M == 0) return MACAQ_OK;
   if (!a_codes || !a_scales || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (!operand_fits(M, K) || !operand_fits(N, K)) return fail(MACAQ_EINVAL, "%s: packed operand over 2 GiB", who);
   macaq_status st = check_out(Y, y_dtype, N, ldy, who);
   if (st != MACAQ_OK) return st;
   if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 16) || !aligned(w_scales, 16))
@@ -250,6 +275,7 @@ macaq_status macaq_linear(const void* X, int64_t M, int64_t K, int64_t ldx, cons
   if (N < 1) return fail(MACAQ_EINVAL, "%s: N < 1", who);
   if (M == 0) return MACAQ_OK;
   if (!X || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (!operand_fits(M, K) || !operand_fits(N, K)) return fail(MACAQ_EINVAL, "%s: packed operand over 2 GiB", who);
   st = check_out(Y, y_dtype, N, ldy, who);
   if (st != MACAQ_OK) return st;
   if (!aligned(X, 16) || ldx % 8 != 0 || (a && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 16))
@@ -271,6 +297,8 @@ macaq_status macaq_linear(const void* X, int64_t M, int64_t K, int64_t ldx, cons
   q.mult = a;
   q.codes = ws + w.codes_off;
   q.scales = ws + w.scales_off;
+  q.tiled = true;
+  q.kpad = pad_k(K);
   hipError_t e = launch_quant_rows(q, b, false, s);
   if (e != hipSuccess) return hip_fail(e, "macaq_linear quantize launch");
   return gemm_common(q.codes, q.scales, M, K, w_codes, w_scales, N, Y, y_dtype, ldy,
@@ -295,6 +323,7 @@ macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t
   if (N < 1) return fail(MACAQ_EINVAL, "%s: N < 1", who);
   if (T == 0) return MACAQ_OK;
   if (!X || !offsets || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (!operand_fits(T, K) || !operand_fits(N, K)) return fail(MACAQ_EINVAL, "%s: packed operand over 2 GiB", who);
   st = check_out(Y, y_dtype, N, N, who);
   if (st != MACAQ_OK) return st;
   if (!aligned(X, 16) || (a && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 16) ||
@@ -321,6 +350,8 @@ macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t
   q.E = E;
   q.codes = ws + w.codes_off;
   q.scales = ws + w.scales_off;
+  q.tiled = true;
+  q.kpad = pad_k(K);
   hipError_t e = launch_quant_rows(q, b, false, s);
   if (e != hipSuccess) return hip_fail(e, "macaq_linear_grouped quantize launch");
   GemmArgs g{};

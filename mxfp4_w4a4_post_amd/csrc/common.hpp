@@ -21,14 +21,35 @@ constexpr int kFmtFp4 = 4;
 // over them, and each XCD has its own L2.
 constexpr int kNumXcd = 8;
 
+// GEMM layout of a packed MXFP4 operand (rows x K elements): rows padded to
+// a multiple of 64, K to a multiple of 128, padding all zero.
+//   codes: 16 rows x 128 elements per 1024-byte block, blocks ordered
+//          (row block, k block); inside a block row r at r * 64, element
+//          pair (2j, 2j+1) at byte j (low nibble first).
+//   scales: 64 rows x 4 groups per 256-byte block, blocks ordered
+//          (64-row block, k block); inside a block row r at r * 4 + g.
+constexpr int kTileRows = 16;
+constexpr int kTileK = 128;
+constexpr int kCodeBlock = kTileRows * kTileK / 2;     // 1024
+constexpr int kScaleRows = 64;
+constexpr int kScaleBlock = kScaleRows * kTileK / 32;  // 256
+constexpr int kRowPad = 64;
+
+__host__ __device__ inline int64_t pad_rows(int64_t r) { return (r + kRowPad - 1) / kRowPad * kRowPad; }
+__host__ __device__ inline int64_t pad_k(int64_t k) { return (k + kTileK - 1) / kTileK * kTileK; }
+__host__ __device__ inline int64_t tiled_codes_bytes(int64_t rows, int64_t K) { return pad_rows(rows) * pad_k(K) / 2; }
+__host__ __device__ inline int64_t tiled_scales_bytes(int64_t rows, int64_t K) { return pad_rows(rows) * pad_k(K) / 32; }
+
 struct QuantArgs {
   const void* x;         // bf16 or fp32 rows [M, ldx]
   int64_t M, K, ldx;
   const float* mult;     // [K] or [E, K] (grouped); nullptr = no multiply
   const int32_t* offsets;  // grouped only: [E+1], rows of expert e
   int E;
-  uint8_t* codes;        // [M, K/2]
-  uint8_t* scales;       // [M, K/32]
+  uint8_t* codes;        // [M, K/2] row-major, or the GEMM layout
+  uint8_t* scales;       // [M, K/32] row-major, or the GEMM layout
+  bool tiled;            // write the GEMM layout (with its zero padding)
+  int64_t kpad;          // pad_k(K)
 };
 
 hipError_t launch_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx, float* s, hipStream_t stream);

@@ -15,9 +15,10 @@
 // A is the activation operand (output rows m), B the weights (output cols n),
 // so consecutive lanes store consecutive n.
 //
-// A workgroup owns a BM x BN output tile and walks K in steps of BK = 128
-// elements (64 bytes of codes and 4 scale bytes per row). Buffer loads
-// (out-of-range reads return zero) run PD steps ahead of the matrix cores,
+// Both operands come in the GEMM layout (16-row x 128-element blocks of 1 KiB,
+// 64-row scale blocks of 256 bytes, zero padding). A workgroup owns a
+// BM x BN output tile and walks K in steps of BK = 128 elements. Buffer loads,
+// each one contiguous block per wave, run PD steps ahead of the matrix cores,
 // held in registers; each step's codes and scales are then written to one of
 // three LDS buffers, and its MFMA fragments are read back one step ahead of
 // their use. The four 16-byte chunks of each LDS row are XOR-swizzled so that
@@ -91,8 +92,8 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * RB + ((chunk ^ f) << 4);
 }
 
-// Buffer resources over the operand arrays: loads beyond num_records return
-// zero, which pads rows past M (N) and, for a ragged K, bytes past K.
+// Buffer resources over the operand arrays (GEMM layout, zero padded to 64
+// rows and a multiple of 128 in K): loads beyond num_records return zero.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer on gfx9
 constexpr uint32_t kOob = 0x80000000u;  // an offset past every buffer (all are < 2 GiB)
@@ -107,92 +108,65 @@ struct Operands {
 };
 
 // Per-thread byte offsets of the rows this thread loads, fixed for the tile
-// (kOob for rows outside the operand); the step adds kt * RB (kt * SB).
+// (kOob for rows past the padded operand). In the GEMM layout a k-step of 16
+// rows is one 1 KiB block and of 64 rows' scales one 256-byte block, so a
+// wave's 16-byte loads of 16 rows read one contiguous block, and the step
+// adds kt * 1024 (kt * 256) through the scalar offset.
 template <class C>
 struct LoadOffsets {
   uint32_t a[C::A_PER_T], b[C::B_PER_T], as[C::A_SC_PER_T], bs[C::B_SC_PER_T];
-  int kc_a[C::A_PER_T], kc_b[C::B_PER_T];
 };
+
+__device__ __forceinline__ uint32_t code_offset(int64_t row, int kc, int64_t ktp, int64_t rows_pad) {
+  if (row >= rows_pad) return kOob;
+  return (uint32_t)(((row / kTileRows) * ktp) * kCodeBlock + (row % kTileRows) * RB + kc * 16);
+}
+__device__ __forceinline__ uint32_t scale_offset(int64_t row, int64_t ktp, int64_t rows_pad) {
+  if (row >= rows_pad) return kOob;
+  return (uint32_t)(((row / kScaleRows) * ktp) * kScaleBlock + (row % kScaleRows) * 4);
+}
 
 template <class C>
 __device__ __forceinline__ void make_offsets(LoadOffsets<C>& lo, const TileCoord& tc, int64_t a_rows, int64_t N,
                                              int64_t K) {
   const int tid = threadIdx.x;
-  const int64_t lda = K >> 1, ldas = K >> 5;
+  const int64_t ktp = pad_k(K) / BK, a_pad = pad_rows(a_rows), n_pad = pad_rows(N);
 #pragma unroll
   for (int i = 0; i < C::A_PER_T; ++i) {
     const int c = tid + i * C::NT;
-    const int64_t gm = tc.m0 + c / CPR;
-    lo.kc_a[i] = c % CPR;
-    lo.a[i] = (c < C::A_CHUNKS && gm < a_rows) ? (uint32_t)(gm * lda + (c % CPR) * 16) : kOob;
+    lo.a[i] = c < C::A_CHUNKS ? code_offset(tc.m0 + c / CPR, c % CPR, ktp, a_pad) : kOob;
   }
 #pragma unroll
   for (int i = 0; i < C::B_PER_T; ++i) {
     const int c = tid + i * C::NT;
-    const int64_t gn = tc.n0 + c / CPR;
-    lo.kc_b[i] = c % CPR;
-    lo.b[i] = (c < C::B_CHUNKS && gn < N) ? (uint32_t)(gn * lda + (c % CPR) * 16) : kOob;
+    lo.b[i] = c < C::B_CHUNKS ? code_offset(tc.n0 + c / CPR, c % CPR, ktp, n_pad) : kOob;
   }
 #pragma unroll
   for (int i = 0; i < C::A_SC_PER_T; ++i) {
     const int row = tid + i * C::NT;
-    const int64_t gm = tc.m0 + row;
-    lo.as[i] = (row < C::BM && gm < a_rows) ? (uint32_t)(gm * ldas) : kOob;
+    lo.as[i] = row < C::BM ? scale_offset(tc.m0 + row, ktp, a_pad) : kOob;
   }
 #pragma unroll
   for (int i = 0; i < C::B_SC_PER_T; ++i) {
     const int row = tid + i * C::NT;
-    const int64_t gn = tc.n0 + row;
-    lo.bs[i] = (row < C::BN && gn < N) ? (uint32_t)(gn * ldas) : kOob;
+    lo.bs[i] = row < C::BN ? scale_offset(tc.n0 + row, ktp, n_pad) : kOob;
   }
 }
 
-// Loads of one k-step, branch-free. RAGGED (K % BK != 0): chunks and scale
-// bytes past K are redirected out of range, so they read as zero.
-template <class C, bool RAGGED>
+// Loads of one k-step, branch-free.
+template <class C>
 __device__ __forceinline__ void load_stage(Stage<C>& st, const Operands& o, const LoadOffsets<C>& lo, int64_t kt) {
-  const uint32_t kb = (uint32_t)(kt * RB), ks = (uint32_t)(kt * SB);
-  const int64_t lda = o.K >> 1, ldas = o.K >> 5;
+  const int kb = (int)(kt * kCodeBlock), ks = (int)(kt * kScaleBlock);
 #pragma unroll
-  for (int i = 0; i < C::A_PER_T; ++i) {
-    uint32_t off = lo.a[i];
-    if (RAGGED && (int64_t)kb + lo.kc_a[i] * 16 >= lda) off = kOob;
-    st.a[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(o.ac, (int)off, (int)kb, 0));
-  }
+  for (int i = 0; i < C::A_PER_T; ++i)
+    st.a[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(o.ac, (int)lo.a[i], kb, 0));
 #pragma unroll
-  for (int i = 0; i < C::B_PER_T; ++i) {
-    uint32_t off = lo.b[i];
-    if (RAGGED && (int64_t)kb + lo.kc_b[i] * 16 >= lda) off = kOob;
-    st.b[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(o.bc, (int)off, (int)kb, 0));
-  }
-  if constexpr (!RAGGED) {
+  for (int i = 0; i < C::B_PER_T; ++i)
+    st.b[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(o.bc, (int)lo.b[i], kb, 0));
 #pragma unroll
-    for (int i = 0; i < C::A_SC_PER_T; ++i) st.as[i] = __builtin_amdgcn_raw_buffer_load_b32(o.as, (int)lo.as[i], (int)ks, 0);
+  for (int i = 0; i < C::A_SC_PER_T; ++i) st.as[i] = __builtin_amdgcn_raw_buffer_load_b32(o.as, (int)lo.as[i], ks, 0);
 #pragma unroll
-    for (int i = 0; i < C::B_SC_PER_T; ++i) st.bs[i] = __builtin_amdgcn_raw_buffer_load_b32(o.bs, (int)lo.bs[i], (int)ks, 0);
-  } else {
-    // byte by byte: a step's 4 scale bytes may run past the end of the row
-#pragma unroll
-    for (int i = 0; i < C::A_SC_PER_T; ++i) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int j = 0; j < SB; ++j) {
-        const uint32_t off = ((int64_t)ks + j < ldas) ? lo.as[i] : kOob;
-        w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(o.as, (int)off, (int)(ks + j), 0) << (8 * j);
-      }
-      st.as[i] = w;
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_SC_PER_T; ++i) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int j = 0; j < SB; ++j) {
-        const uint32_t off = ((int64_t)ks + j < ldas) ? lo.bs[i] : kOob;
-        w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(o.bs, (int)off, (int)(ks + j), 0) << (8 * j);
-      }
-      st.bs[i] = w;
-    }
-  }
+  for (int i = 0; i < C::B_SC_PER_T; ++i) st.bs[i] = __builtin_amdgcn_raw_buffer_load_b32(o.bs, (int)lo.bs[i], ks, 0);
 }
 
 // Per-lane LDS byte offsets, fixed for the kernel. The swizzle depends only
@@ -431,7 +405,7 @@ __device__ __forceinline__ void store_out(const Acc<C>& acc, const GemmArgs& g, 
 // and is visible after that barrier. The loop is unrolled U times so the
 // register slot (s+2) % PD, the fragment set and the scale set are static, and
 // its steady state has no branches, so each wait covers only what it needs.
-template <class C, bool RAGGED>
+template <class C>
 struct Pipe {
   Acc<C> acc;
   Stage<C> st[C::PD];
@@ -458,7 +432,7 @@ struct Pipe {
   template <int P>
   __device__ __forceinline__ void prologue_loads() {
     if constexpr (P < C::PD) {
-      if (P < nsteps) load_stage<C, RAGGED>(st[P], o, lo, kt0 + P);
+      if (P < nsteps) load_stage<C>(st[P], o, lo, kt0 + P);
       prologue_loads<P + 1>();
     }
   }
@@ -496,7 +470,7 @@ struct Pipe {
       read_half<C, 0, B_NEXT>(hf[FL ^ 1], smem, lds);
       read_scales<C, B_NEXT>(sc[SC ^ 1], smem, lds, lane);
     }
-    if (FULL || s + 2 + C::PD < nsteps) load_stage<C, RAGGED>(st[SLOT], o, lo, kt0 + s + 2 + C::PD);
+    if (FULL || s + 2 + C::PD < nsteps) load_stage<C>(st[SLOT], o, lo, kt0 + s + 2 + C::PD);
     mfma_half<C, C::NSUB - 1>(acc, hf[FL], sc[SC]);
     if constexpr (FULL) {
       if constexpr (C::NSUB == 2) interleave<0, C::N_MFMA, C::N_DSR + C::FM + C::FN, 0, C::N_VMEM>();
@@ -524,8 +498,8 @@ struct Pipe {
     prologue_loads<0>();                                  // steps 0 .. PD-1 in slots 0 .. PD-1
     store_stage<C, 0>(st[0], smem, lds);
     if (1 < nsteps) store_stage<C, 1>(st[1], smem, lds);
-    if (C::PD < nsteps) load_stage<C, RAGGED>(st[0], o, lo, kt0 + C::PD);        // slot PD % PD
-    if (C::PD + 1 < nsteps) load_stage<C, RAGGED>(st[1], o, lo, kt0 + C::PD + 1);  // slot (PD+1) % PD
+    if (C::PD < nsteps) load_stage<C>(st[0], o, lo, kt0 + C::PD);        // slot PD % PD
+    if (C::PD + 1 < nsteps) load_stage<C>(st[1], o, lo, kt0 + C::PD + 1);  // slot (PD+1) % PD
     __syncthreads();
     read_half<C, 0, 0>(hf[0], smem, lds);
     read_scales<C, 0>(sc[0], smem, lds, lane);
@@ -535,19 +509,15 @@ struct Pipe {
   }
 };
 
-// RAGGED (K % BK != 0) is a separate kernel: in one kernel with the aligned
-// path, the register allocation of the two would be shared and the aligned
-// loop would spill.
-template <class C, bool RAGGED>
+template <class C>
 __device__ __forceinline__ void run_tile(const GemmArgs& g, const TileCoord& tc, int64_t a_rows, const uint8_t* bc,
                                          const uint8_t* bs, uint8_t* smem) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int64_t lda = g.K >> 1, ldas = g.K >> 5;
-  Operands o{make_rsrc(g.a_codes, a_rows * lda), make_rsrc(g.a_scales, a_rows * ldas), make_rsrc(bc, g.N * lda),
-             make_rsrc(bs, g.N * ldas), g.N, g.K};
-  Pipe<C, RAGGED> p(o, tc, a_rows, smem, wm, wn, lane);
+  Operands o{make_rsrc(g.a_codes, tiled_codes_bytes(a_rows, g.K)), make_rsrc(g.a_scales, tiled_scales_bytes(a_rows, g.K)),
+             make_rsrc(bc, tiled_codes_bytes(g.N, g.K)), make_rsrc(bs, tiled_scales_bytes(g.N, g.K)), g.N, g.K};
+  Pipe<C> p(o, tc, a_rows, smem, wm, wn, lane);
   p.run();
   store_out<C>(p.acc, g, tc, wm, wn, lane);
 }
@@ -561,7 +531,7 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t id, int64_t total) {
   return (id % kNumXcd) * per + id / kNumXcd;
 }
 
-template <class C, bool RAGGED>
+template <class C>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
   const int64_t mt = (g.M + C::BM - 1) / C::BM;
@@ -579,7 +549,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   const int64_t in_group = t - group * GROUP_M * nt;
   const int64_t tm = first_m + in_group % gsize;
   const int64_t tn = in_group / gsize;
-  const int64_t KT = (g.K + BK - 1) / BK;
+  const int64_t KT = pad_k(g.K) / BK;
   TileCoord tc;
   tc.m0 = tm * C::BM;
   tc.m_end = g.M;
@@ -587,12 +557,12 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   tc.split = split;
   tc.kt_begin = KT * split / g.splits;
   tc.kt_end = KT * (split + 1) / g.splits;
-  run_tile<C, RAGGED>(g, tc, g.M, g.b_codes, g.b_scales, smem);
+  run_tile<C>(g, tc, g.M, g.b_codes, g.b_scales, smem);
 }
 
 // Grouped: the tile map (built by build_tile_map_kernel) lists, per m-tile,
 // the expert and the first row; tiles past the used count exit at once.
-template <class C, bool RAGGED>
+template <class C>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_grouped_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
   const int64_t nt = (g.N + C::BN - 1) / C::BN;
@@ -609,10 +579,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   tc.n0 = tn * C::BN;
   tc.split = 0;
   tc.kt_begin = 0;
-  tc.kt_end = (g.K + BK - 1) / BK;
-  const int64_t lda = g.K >> 1, ldas = g.K >> 5;
-  run_tile<C, RAGGED>(g, tc, g.M, g.b_codes + (int64_t)expert * g.N * lda, g.b_scales + (int64_t)expert * g.N * ldas,
-                      smem);
+  tc.kt_end = pad_k(g.K) / BK;
+  run_tile<C>(g, tc, g.M, g.b_codes + (int64_t)expert * tiled_codes_bytes(g.N, g.K),
+              g.b_scales + (int64_t)expert * tiled_scales_bytes(g.N, g.K), smem);
 }
 
 // One thread walks the experts: m-tile j of expert e gets entry (tiles of
@@ -662,8 +631,7 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
   const int64_t nt = (g.N + C::BN - 1) / C::BN;
   const int64_t total = mt * nt * g.splits;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (g.K % BK == 0) hipLaunchKernelGGL((gemm_kernel<C, false>), dim3((unsigned)total), dim3(C::NT), 0, stream, g);
-  else hipLaunchKernelGGL((gemm_kernel<C, true>), dim3((unsigned)total), dim3(C::NT), 0, stream, g);
+  hipLaunchKernelGGL(gemm_kernel<C>, dim3((unsigned)total), dim3(C::NT), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -676,10 +644,7 @@ hipError_t launch_grouped_cfg(const GemmArgs& g, hipStream_t stream) {
   const int64_t nt = (g.N + C::BN - 1) / C::BN;
   const int64_t total = g.max_mtiles * nt;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (g.K % BK == 0)
-    hipLaunchKernelGGL((gemm_grouped_kernel<C, false>), dim3((unsigned)total), dim3(C::NT), 0, stream, g);
-  else
-    hipLaunchKernelGGL((gemm_grouped_kernel<C, true>), dim3((unsigned)total), dim3(C::NT), 0, stream, g);
+  hipLaunchKernelGGL(gemm_grouped_kernel<C>, dim3((unsigned)total), dim3(C::NT), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -699,7 +664,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     p.bm = 256;
   }
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * nt;
-  const int64_t KT = (K + BK - 1) / BK;
+  const int64_t KT = pad_k(K) / BK;
   int splits = 1;
   // split K only for skinny (decode) shapes whose tiles leave most CUs idle
   if (M <= 64)

@@ -6,14 +6,15 @@
 // activations at inference and quantizes to MXFP4; the same row transform with
 // the weight-side multiplier produces the absorbed weights offline.
 //
-// Layout of the work: one lane owns 8 consecutive elements of a row (one
-// 16-byte bf16 load, coalesced across the wave); an MX group of 32 is 4
-// adjacent lanes and a Hadamard block of b elements is b/8 adjacent lanes.
-// Butterflies of span 1, 2, 4 stay inside the lane; spans 8 .. b/2 pair lanes
-// 1 .. b/16 apart through cross-lane shuffles. The E2M1 encode and nibble
-// packing use the hardware scaled FP4 convert, which rounds to nearest-even,
-// saturates at 6 and keeps the sign (it only reads the exponent of its fp32
-// scale operand).
+// Layout of the work: a workgroup of 256 lanes covers 16 rows x 128
+// elements (one block of the GEMM layout); each lane owns 8 consecutive
+// elements of a row (one 16-byte bf16 load), 16 lanes a row. An MX group of 32
+// is 4 adjacent lanes and a Hadamard block of b elements is b/8 adjacent
+// lanes. Butterflies of span 1, 2, 4 stay inside the lane; spans 8 .. b/2 pair
+// lanes 1 .. b/16 apart through cross-lane shuffles. The E2M1 encode and
+// nibble packing use the hardware scaled FP4 convert, which rounds to
+// nearest-even, saturates at 6 and keeps the sign (it only reads the exponent
+// of its fp32 scale operand).
 #include "common.hpp"
 
 namespace macaq {
@@ -35,27 +36,25 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ off, in
   return lo;
 }
 
-template <bool F32_IN, int B, bool SCALE, bool GROUPED>
+// TILED: write the GEMM layout (including its zero padding); otherwise
+// row-major [M, K/2] codes and [M, K/32] scales.
+template <bool F32_IN, int B, bool SCALE, bool GROUPED, bool TILED>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
-  const int64_t cpr = q.K >> 3;  // 8-element chunks per row
-  const int64_t total = q.M * cpr;
-  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const bool active = t < total;
-  const int64_t row = active ? t / cpr : 0;
-  const int64_t chunk = active ? t - row * cpr : 0;
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int64_t row = (int64_t)blockIdx.x * kTileRows + (tid >> 4);
+  const int64_t k = (int64_t)blockIdx.y * kTileK + (tid & 15) * 8;
+  const bool valid = row < q.M && k < q.K;
 
   float v[8];
-  if (active) {
+  if (valid) {
     if constexpr (F32_IN) {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q.x) + row * q.ldx + chunk * 8);
-      float4 u0 = p[0];
-      float4 u1 = p[1];
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q.x) + row * q.ldx + k);
+      const float4 u0 = p[0], u1 = p[1];
       v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
       v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
     } else {
-      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.x) + row * q.ldx + chunk * 8);
-      uint4 w = *p;
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.x) + row * q.ldx + k);
       v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
       v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
       v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
@@ -64,8 +63,8 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
     if constexpr (SCALE) {
       const float* m = q.mult;
       if constexpr (GROUPED) m += (int64_t)expert_of_row(q.offsets, q.E, row) * q.K;
-      const float4* mp = reinterpret_cast<const float4*>(m + chunk * 8);
-      float4 m0 = mp[0], m1 = mp[1];
+      const float4* mp = reinterpret_cast<const float4*>(m + k);
+      const float4 m0 = mp[0], m1 = mp[1];
       v[0] *= m0.x; v[1] *= m0.y; v[2] *= m0.z; v[3] *= m0.w;
       v[4] *= m1.x; v[5] *= m1.y; v[6] *= m1.z; v[7] *= m1.w;
     }
@@ -81,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if (i & h) continue;
-        float u = v[i], w = v[i + h];
+        const float u = v[i], w = v[i + h];
         v[i] = u + w;
         v[i + h] = u - w;
       }
@@ -94,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
       const float sgn = (lane & d) ? -1.0f : 1.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float p = __shfl_xor(v[i], d);
+        const float p = __shfl_xor(v[i], d);
         v[i] = __builtin_fmaf(sgn, v[i], p);
       }
     }
@@ -119,9 +118,20 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
   packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[4], v[5], scale, 2);
   packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[6], v[7], scale, 3);
 
-  if (active) {
-    *reinterpret_cast<uint32_t*>(q.codes + row * (q.K >> 1) + chunk * 4) = packed;
-    if ((chunk & 3) == 0) q.scales[row * (q.K >> 5) + (chunk >> 2)] = (uint8_t)sc;
+  if constexpr (TILED) {
+    // every lane of the padded grid writes (zeros outside M x K)
+    const int64_t kt = k / kTileK, ktp = q.kpad / kTileK;
+    const int64_t cofs = ((row / kTileRows) * ktp + kt) * kCodeBlock + (row % kTileRows) * (kTileK / 2) +
+                         (k % kTileK) / 2;
+    *reinterpret_cast<uint32_t*>(q.codes + cofs) = packed;
+    if ((k & 31) == 0) {
+      const int64_t g = k / 32;
+      const int64_t sofs = ((row / kScaleRows) * ktp + g / 4) * kScaleBlock + (row % kScaleRows) * 4 + (g % 4);
+      q.scales[sofs] = (uint8_t)sc;
+    }
+  } else if (valid) {
+    *reinterpret_cast<uint32_t*>(q.codes + row * (q.K >> 1) + (k >> 1)) = packed;
+    if ((k & 31) == 0) q.scales[row * (q.K >> 5) + (k >> 5)] = (uint8_t)sc;
   }
 }
 
@@ -179,40 +189,47 @@ __global__ __launch_bounds__(kThreads) void multipliers_kernel(const float* __re
   if (r) r[k] = cb * sk;
 }
 
-template <bool F32_IN, int B, bool SCALE, bool GROUPED>
+template <bool F32_IN, int B, bool SCALE, bool GROUPED, bool TILED>
 hipError_t launch_one(const QuantArgs& q, hipStream_t stream) {
-  const int64_t total = q.M * (q.K >> 3);
-  const int64_t blocks = (total + kThreads - 1) / kThreads;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((quant_rows_kernel<F32_IN, B, SCALE, GROUPED>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     stream, q);
+  // tiled: cover the padded rows and K; row-major: just M x K
+  const int64_t rows = TILED ? pad_rows(q.M) : q.M;
+  const int64_t kk = TILED ? q.kpad : q.K;
+  const int64_t gx = (rows + kTileRows - 1) / kTileRows, gy = (kk + kTileK - 1) / kTileK;
+  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((quant_rows_kernel<F32_IN, B, SCALE, GROUPED, TILED>), dim3((unsigned)gx, (unsigned)gy),
+                     dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 
-template <bool F32_IN, bool SCALE, bool GROUPED>
+template <bool F32_IN, bool SCALE, bool GROUPED, bool TILED>
 hipError_t launch_b(const QuantArgs& q, int b, hipStream_t stream) {
   switch (b) {
-    case 0: return launch_one<F32_IN, 0, SCALE, GROUPED>(q, stream);
-    case 32: return launch_one<F32_IN, 32, SCALE, GROUPED>(q, stream);
-    case 64: return launch_one<F32_IN, 64, SCALE, GROUPED>(q, stream);
-    case 128: return launch_one<F32_IN, 128, SCALE, GROUPED>(q, stream);
+    case 0: return launch_one<F32_IN, 0, SCALE, GROUPED, TILED>(q, stream);
+    case 32: return launch_one<F32_IN, 32, SCALE, GROUPED, TILED>(q, stream);
+    case 64: return launch_one<F32_IN, 64, SCALE, GROUPED, TILED>(q, stream);
+    case 128: return launch_one<F32_IN, 128, SCALE, GROUPED, TILED>(q, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <bool TILED>
+hipError_t launch_layout(const QuantArgs& q, int b, bool x_is_f32, hipStream_t stream) {
+  const bool scale = q.mult != nullptr;
+  const bool grouped = q.offsets != nullptr;
+  if (x_is_f32) {
+    if (grouped) return hipErrorInvalidValue;
+    return scale ? launch_b<true, true, false, TILED>(q, b, stream) : launch_b<true, false, false, TILED>(q, b, stream);
+  }
+  if (grouped)
+    return scale ? launch_b<false, true, true, TILED>(q, b, stream) : launch_b<false, false, true, TILED>(q, b, stream);
+  return scale ? launch_b<false, true, false, TILED>(q, b, stream) : launch_b<false, false, false, TILED>(q, b, stream);
 }
 
 }  // namespace
 
 hipError_t launch_quant_rows(const QuantArgs& q, int b, bool x_is_f32, hipStream_t stream) {
   if (q.M == 0) return hipSuccess;
-  const bool scale = q.mult != nullptr;
-  const bool grouped = q.offsets != nullptr;
-  if (x_is_f32) {
-    if (grouped) return hipErrorInvalidValue;
-    return scale ? launch_b<true, true, false>(q, b, stream) : launch_b<true, false, false>(q, b, stream);
-  }
-  if (grouped)
-    return scale ? launch_b<false, true, true>(q, b, stream) : launch_b<false, false, true>(q, b, stream);
-  return scale ? launch_b<false, true, false>(q, b, stream) : launch_b<false, false, false>(q, b, stream);
+  return q.tiled ? launch_layout<true>(q, b, x_is_f32, stream) : launch_layout<false>(q, b, x_is_f32, stream);
 }
 
 hipError_t launch_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx, float* s, hipStream_t stream) {

@@ -17,7 +17,9 @@ def log(msg: str):
     sys.stdout.flush()
 
 
-def np_u8(t: torch.Tensor) -> np.ndarray:
+def np_u8(t) -> np.ndarray:
+    if isinstance(t, np.ndarray):
+        return t
     return t.detach().cpu().numpy()
 
 
@@ -68,3 +70,50 @@ def assert_bf16_close(y_bf16: torch.Tensor, y_ref: np.ndarray, what=""):
     ulp = np.maximum(np.abs(ref), 1e-30) * 2.0 ** -7
     assert np.all(np.abs(got - ref) <= ulp + 1e-30), "%s: bf16 output off by more than one ulp" % what
     assert rel_l2(got, y_ref) < 1e-2, what
+
+
+# ---------------------------------------------------------------------------
+# The GEMM layout of packed operands, restated from include/macaq.h: rows
+# padded to a multiple of 64, K to a multiple of 128, padding all zero;
+# code byte (r, k) at ((r/16)*KB + k/128)*1024 + (r%16)*64 + (k%128)/2 and
+# scale (r, g) at ((r/64)*KB + g/4)*256 + (r%64)*4 + g%4, KB = KP/128.
+# ---------------------------------------------------------------------------
+
+def padded(rows: int, K: int):
+    return -(-rows // 64) * 64, -(-K // 128) * 128
+
+
+def gemm_layout_to_row_major(codes, scales, rows: int, K: int, check_padding: bool = True):
+    """Row-major (codes [rows, K/2], scales [rows, K/32]) of a GEMM-layout operand."""
+    RP, KP = padded(rows, K)
+    KB = KP // 128
+    c = np.asarray(codes).reshape(-1)
+    s = np.asarray(scales).reshape(-1)
+    assert c.size == RP * KP // 2 and s.size == RP * KP // 32, (c.size, s.size, RP, KP)
+    cf = c.reshape(RP // 16, KB, 16, 64).transpose(0, 2, 1, 3).reshape(RP, KP // 2)
+    sf = s.reshape(RP // 64, KB, 64, 4).transpose(0, 2, 1, 3).reshape(RP, KP // 32)
+    if check_padding:
+        assert not cf[rows:].any() and not cf[:, K // 2:].any(), "code padding is not zero"
+        assert not sf[rows:].any() and not sf[:, K // 32:].any(), "scale padding is not zero"
+    return np.ascontiguousarray(cf[:rows, :K // 2]), np.ascontiguousarray(sf[:rows, :K // 32])
+
+
+def row_major_to_gemm_layout(codes, scales):
+    """Inverse of gemm_layout_to_row_major (numpy, zero padding)."""
+    codes = np.asarray(codes, np.uint8)
+    scales = np.asarray(scales, np.uint8)
+    rows, K = codes.shape[0], codes.shape[1] * 2
+    RP, KP = padded(rows, K)
+    KB = KP // 128
+    cf = np.zeros((RP, KP // 2), np.uint8)
+    sf = np.zeros((RP, KP // 32), np.uint8)
+    cf[:rows, :K // 2] = codes
+    sf[:rows, :K // 32] = scales
+    c = cf.reshape(RP // 16, 16, KB, 64).transpose(0, 2, 1, 3).reshape(-1)
+    s = sf.reshape(RP // 64, 64, KB, 4).transpose(0, 2, 1, 3).reshape(-1)
+    return np.ascontiguousarray(c), np.ascontiguousarray(s)
+
+
+def packed_to_row_major(p, check_padding: bool = True):
+    """(codes, scales) row-major numpy arrays of a binding.Packed operand."""
+    return gemm_layout_to_row_major(p.codes.cpu().numpy(), p.scales.cpu().numpy(), p.rows, p.K, check_padding)

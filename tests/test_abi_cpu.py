@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding._SIGNATURES), "binding signatures out of sync with the header"
@@ -47,7 +47,9 @@ def _last(lib):
 
 
 def test_quant_act_rejects(lib):
-    f = lib.macaq_quant_act
+    def f(X, M, K, ldx, a, b, codes, scales, stream, layout=0):
+        return lib.macaq_quant_act(X, M, K, ldx, a, b, layout, codes, scales, stream)
+
     assert f(None, 4, 64, 64, None, 32, FAKE, FAKE, None) == EINVAL
     assert f(FAKE, 4, 48, 48, None, 0, FAKE, FAKE, None) == EINVAL  # K % 32
     assert "multiple of 32" in _last(lib)
@@ -55,10 +57,12 @@ def test_quant_act_rejects(lib):
     assert f(FAKE, 4, 64, 64, None, 16, FAKE, FAKE, None) == EINVAL  # b not allowed
     assert f(FAKE, 4, 64, 32, None, 32, FAKE, FAKE, None) == EINVAL  # ldx < K
     assert f(FAKE, -1, 64, 64, None, 32, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, 4, 64, 64, None, 32, FAKE, FAKE, None, layout=7) == EINVAL
+    assert f(FAKE, 1 << 24, 1 << 10, 1 << 10, None, 32, FAKE, FAKE, None, layout=1) == EINVAL  # over 2 GiB packed
     assert f(FAKE + 2, 4, 64, 64, None, 32, FAKE, FAKE, None) == EALIGN
     assert f(FAKE, 4, 64, 68, None, 32, FAKE, FAKE, None) == EALIGN  # ldx not a multiple of 8
     assert f(FAKE, 4, 64, 64, FAKE + 4, 32, FAKE, FAKE, None) == EALIGN
-    assert f(FAKE, 0, 64, 64, None, 32, FAKE, FAKE, None) == OK  # empty: nothing to do
+    assert f(None, 0, 64, 64, None, 32, None, None, None) == OK  # empty: nothing to do
 
 
 def test_prepare_weights_rejects(lib):
@@ -83,8 +87,8 @@ def test_linear_rejects(lib):
     assert call(ldy=8) == EINVAL
     assert call(dt=3) == EINVAL
     assert call(Y=None) == EINVAL
-    assert call(ldy=18) == EALIGN
-    assert call(Y=FAKE + 8) == EALIGN
+    assert call(Y=FAKE + 1) == EALIGN  # bf16 output must be 2-byte aligned
+    assert call(Y=FAKE + 2, dt=1) == EALIGN  # fp32 output must be 4-byte aligned
     need = lib.macaq_linear_workspace_size(4, 64, 16)
     assert need > 0
     assert call(wsb=need - 1) == EWORKSPACE
@@ -112,11 +116,20 @@ def test_calibrate_and_multipliers_reject(lib):
     assert lib.macaq_make_multipliers(FAKE, 0, 32, FAKE, None, None) == EINVAL
 
 
+def test_packed_sizes(lib):
+    """GEMM layout: rows padded to 64, K to 128; codes K/2 and scales K/32 bytes a row."""
+    for rows, K in [(1, 32), (16, 256), (65, 96), (2048, 4096), (8192, 28672)]:
+        RP, KP = -(-rows // 64) * 64, -(-K // 128) * 128
+        assert lib.macaq_packed_codes_bytes(rows, K) == RP * KP // 2
+        assert lib.macaq_packed_scales_bytes(rows, K) == RP * KP // 32
+    assert lib.macaq_packed_codes_bytes(0, 64) == 0
+
+
 def test_workspace_sizes_cover_staging(lib):
-    # quantized activations staged in the workspace: codes + scales, 256-byte padded
+    # quantized activations staged in the workspace in the GEMM layout, 256-byte padded
     for M, K, N in [(16, 256, 256), (2048, 4096, 4096), (1, 25600, 5120), (8192, 28672, 8192)]:
         need = lib.macaq_linear_workspace_size(M, K, N)
-        assert need >= M * K // 2 + M * K // 32
+        assert need >= lib.macaq_packed_codes_bytes(M, K) + lib.macaq_packed_scales_bytes(M, K)
         assert need % 256 == 0
     assert lib.macaq_linear_workspace_size(0, 64, 16) == 0
     T, E, K, N = 32768, 128, 2048, 1536

@@ -16,7 +16,8 @@ import torch
 
 import oracle
 from mxfp4_w4a4_post_amd import binding, inputs
-from parity_util import (REL_L2_TOL, assert_bf16_close, assert_quant_equal, bits, log, np_u8, rel_l2)
+from parity_util import (REL_L2_TOL, assert_bf16_close, assert_quant_equal, bits, log, np_u8, packed_to_row_major,
+                         rel_l2, row_major_to_gemm_layout)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,10 +93,15 @@ def test_quant_act_bit_exact(dev, cfg, shape, M, b):
     _, a_g, _ = gpu_layer(case, dev)
     _, a_o, _ = oracle_layer(case)
     use_scale = b != 0
-    c_g, s_g = binding.quant_act(case.x.to(dev), a_g if use_scale else None, b)
+    x_d = case.x.to(dev)
+    c_g, s_g = binding.quant_act(x_d, a_g if use_scale else None, b)
     c_o, s_o = oracle.quant_rows(bits(case.x), a_o if use_scale else None, b)
     t_o = oracle.transform_rows(bits(case.x), a_o if use_scale else None, b)
     assert_quant_equal(np_u8(c_g), np_u8(s_g), c_o, s_o, t_o, case.name)
+    # the GEMM layout holds the same codes, with zero padding
+    pk = binding.quant_act(x_d, a_g if use_scale else None, b, layout="gemm")
+    c_t, s_t = packed_to_row_major(pk)
+    assert np.array_equal(c_t, np_u8(c_g)) and np.array_equal(s_t, np_u8(s_g))
 
 
 def test_quant_act_hand_worked_groups(dev):
@@ -103,7 +109,7 @@ def test_quant_act_hand_worked_groups(dev):
     transform), against the stored expected bytes."""
     cases = json.load(open(os.path.join(GOLDEN, "mx_hand_worked.json")))["cases"]
     w = torch.tensor([c["values"] for c in cases], dtype=torch.float32, device=dev)
-    codes, scales = binding.prepare_weights(w, None, 0)
+    codes, scales = packed_to_row_major(binding.prepare_weights(w, None, 0))
     for i, c in enumerate(cases):
         assert int(scales[i, 0]) == c["scale"], c["what"]
         assert list(np_u8(codes[i])) == c["bytes"], c["what"]
@@ -125,7 +131,7 @@ def test_quant_edge_values(dev):
     x = np.stack(rows).astype(np.float32)
     for b in (0, 32, 128):
         log("quant edge b=%d" % b)
-        c_g, s_g = binding.prepare_weights(torch.from_numpy(x).to(dev), None, b)
+        c_g, s_g = packed_to_row_major(binding.prepare_weights(torch.from_numpy(x).to(dev), None, b))
         c_o, s_o = oracle.quant_rows(x, None, b)
         t_o = oracle.transform_rows(x, None, b)
         finite = np.all(np.isfinite(t_o), axis=1)
@@ -146,7 +152,7 @@ def test_prepare_weights_bit_exact(dev, cfg, shape, N, b, f32):
     _, _, r_g = gpu_layer(case, dev)
     _, _, r_o = oracle_layer(case)
     w = case.w.float() if f32 else case.w
-    c_g, s_g = binding.prepare_weights(w.to(dev), r_g, b)
+    c_g, s_g = packed_to_row_major(binding.prepare_weights(w.to(dev), r_g, b))
     w_np = w.numpy() if f32 else bits(w)
     c_o, s_o = oracle.prepare_weights(w_np, r_o, b)
     t_o = oracle.transform_rows(w_np, r_o, b)
@@ -169,12 +175,16 @@ def test_gemm_random_codes(dev, M, N, K):
     as_ = rng.integers(118, 136, size=(M, K // 32), dtype=np.uint8)
     wc = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     ws = rng.integers(118, 136, size=(N, K // 32), dtype=np.uint8)
-    t = lambda a: torch.from_numpy(a).to(dev)
-    y = binding.linear_plain_gemm(t(ac), t(as_), t(wc), t(ws), out_dtype=torch.float32)
+    def packed(c, sc):
+        tc, ts = row_major_to_gemm_layout(c, sc)
+        return binding.Packed(torch.from_numpy(tc).to(dev), torch.from_numpy(ts).to(dev), c.shape[0], 2 * c.shape[1])
+
+    pa, pw = packed(ac, as_), packed(wc, ws)
+    y = binding.linear_plain_gemm(pa, pw, out_dtype=torch.float32)
     y_o = oracle.gemm_codes(ac, as_, wc, ws)
     err = rel_l2(y.cpu().numpy(), y_o)
     assert err <= REL_L2_TOL, err
-    y16 = binding.linear_plain_gemm(t(ac), t(as_), t(wc), t(ws), out_dtype=torch.bfloat16)
+    y16 = binding.linear_plain_gemm(pa, pw, out_dtype=torch.bfloat16)
     assert_bf16_close(y16, y.cpu().numpy().astype(np.float64), "gemm bf16 %d %d %d" % (M, N, K))
 
 
@@ -189,16 +199,17 @@ def check_linear(case, dev, rows=None, cols=None, b=None):
     _, a_o, r_o = oracle_layer(case, b)
     x_d = case.x.to(dev)
     w_d = case.w.to(dev)
-    wc_g, ws_g = binding.prepare_weights(w_d, r_g, b)
-    y_g = binding.linear(x_d, a_g, b, wc_g, ws_g, out_dtype=torch.float32)
-    y_g16 = binding.linear(x_d, a_g, b, wc_g, ws_g, out_dtype=torch.bfloat16)
+    pw = binding.prepare_weights(w_d, r_g, b)
+    wc_g, ws_g = packed_to_row_major(pw)
+    y_g = binding.linear(x_d, a_g, b, pw, out_dtype=torch.float32)
+    y_g16 = binding.linear(x_d, a_g, b, pw, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     rows = np.arange(case.M) if rows is None else np.asarray(rows)
     cols = np.arange(case.N) if cols is None else np.asarray(cols)
     xb = bits(case.x)[rows]
     wb = bits(case.w)[cols]
     wc_o, ws_o = oracle.prepare_weights(wb, r_o, b)
-    assert_quant_equal(np_u8(wc_g)[cols], np_u8(ws_g)[cols], wc_o, ws_o, oracle.transform_rows(wb, r_o, b),
+    assert_quant_equal(wc_g[cols], ws_g[cols], wc_o, ws_o, oracle.transform_rows(wb, r_o, b),
                        case.name + " W'")
     y_o = oracle.linear(xb, a_o, b, wc_o, ws_o)
     got = y_g.cpu().numpy()[np.ix_(rows, cols)]
@@ -216,8 +227,8 @@ def test_linear_tiny_full(dev):
     y1 = check_linear(case, dev)
     # determinism: the same call twice is bit-identical
     _, a_g, r_g = gpu_layer(case, dev)
-    wc, ws = binding.prepare_weights(case.w.to(dev), r_g, case.b)
-    y2 = binding.linear(case.x.to(dev), a_g, case.b, wc, ws, out_dtype=torch.float32)
+    pw = binding.prepare_weights(case.w.to(dev), r_g, case.b)
+    y2 = binding.linear(case.x.to(dev), a_g, case.b, pw, out_dtype=torch.float32)
     assert torch.equal(y1, y2)
 
 
@@ -228,11 +239,11 @@ def test_linear_tiny_blocks(dev, b):
     if b == 0:
         # plain MXFP4: no multiply, no Hadamard on either side
         x_d, w_d = case.x.to(dev), case.w.to(dev)
-        wc, ws = binding.prepare_weights(w_d, None, 0)
-        y = binding.linear(x_d, None, 0, wc, ws, out_dtype=torch.float32)
+        pw = binding.prepare_weights(w_d, None, 0)
+        y = binding.linear(x_d, None, 0, pw, out_dtype=torch.float32)
         wc_o, ws_o = oracle.prepare_weights(bits(case.w), None, 0)
         y_o = oracle.linear(bits(case.x), None, 0, wc_o, ws_o)
-        assert np.array_equal(np_u8(wc), wc_o)
+        assert np.array_equal(packed_to_row_major(pw)[0], wc_o)
         assert rel_l2(y.cpu().numpy(), y_o) <= REL_L2_TOL
     else:
         check_linear(case, dev, b=b)
@@ -249,15 +260,15 @@ def test_linear_ragged(dev, M, K, N):
 def test_linear_strided_and_empty(dev):
     case = inputs.linear_case(1, 0, M=20, K=256, N=48)
     _, a_g, r_g = gpu_layer(case, dev)
-    wc, ws = binding.prepare_weights(case.w.to(dev), r_g, case.b)
+    pw = binding.prepare_weights(case.w.to(dev), r_g, case.b)
     xpad = torch.zeros(20, 256 + 64, dtype=torch.bfloat16, device=dev)
     xpad[:, :256] = case.x.to(dev)
     ypad = torch.full((20, 48 + 16), 7.0, dtype=torch.float32, device=dev)
-    binding.linear(xpad[:, :256], a_g, case.b, wc, ws, out=ypad[:, :48])
-    y = binding.linear(case.x.to(dev), a_g, case.b, wc, ws, out_dtype=torch.float32)
+    binding.linear(xpad[:, :256], a_g, case.b, pw, out=ypad[:, :48])
+    y = binding.linear(case.x.to(dev), a_g, case.b, pw, out_dtype=torch.float32)
     assert torch.equal(ypad[:, :48], y)
     assert torch.all(ypad[:, 48:] == 7.0)
-    empty = binding.linear(torch.empty(0, 256, dtype=torch.bfloat16, device=dev), a_g, case.b, wc, ws)
+    empty = binding.linear(torch.empty(0, 256, dtype=torch.bfloat16, device=dev), a_g, case.b, pw)
     assert empty.shape == (0, 48)
 
 
@@ -305,13 +316,12 @@ def grouped_gpu(mc, dev, b, out_dtype=torch.float32):
         s = binding.calibrate(xcal[e])
         a[e], r[e] = binding.make_multipliers(s, b)
     w = mc.w.to(dev)
-    wc = torch.empty(E, mc.N, K // 2, dtype=torch.uint8, device=dev)
-    ws = torch.empty(E, mc.N, K // 32, dtype=torch.uint8, device=dev)
+    pw = binding.empty_grouped_weights(E, mc.N, K, dev)
     for e in range(E):
-        wc[e], ws[e] = binding.prepare_weights(w[e], r[e], b)
+        binding.prepare_weights(w[e], r[e], b, out=binding.expert(pw, e))
     off = torch.from_numpy(mc.offsets).to(dev)
-    y = binding.linear_grouped(mc.x.to(dev), off, a, b, wc, ws, out_dtype=out_dtype)
-    return y, a, wc, ws
+    y = binding.linear_grouped(mc.x.to(dev), off, a, b, pw, out_dtype=out_dtype)
+    return y, a, pw
 
 
 def oracle_expert(mc, e, b):
@@ -324,13 +334,14 @@ def oracle_expert(mc, e, b):
 def test_linear_grouped_small_full(dev):
     mc = inputs.moe_case("gate_up", tokens=64, experts=8)
     log("grouped small T=%d E=%d counts=%s" % (mc.T, mc.E, list(mc.counts)))
-    y, a, wc, ws = grouped_gpu(mc, dev, 32)
+    y, a, pw = grouped_gpu(mc, dev, 32)
     a_o = np.zeros((mc.E, mc.K), np.float32)
     wc_o = np.zeros((mc.E, mc.N, mc.K // 2), np.uint8)
     ws_o = np.zeros((mc.E, mc.N, mc.K // 32), np.uint8)
     for e in range(mc.E):
         a_o[e], wc_o[e], ws_o[e] = oracle_expert(mc, e, 32)
-    assert np.array_equal(np_u8(wc), wc_o) and np.array_equal(np_u8(ws), ws_o)
+        c_e, s_e = packed_to_row_major(binding.expert(pw, e))
+        assert np.array_equal(c_e, wc_o[e]) and np.array_equal(s_e, ws_o[e]), e
     y_o = oracle.linear_grouped(bits(mc.x), mc.offsets, a_o, 32, wc_o, ws_o)
     assert rel_l2(y.cpu().numpy(), y_o) <= REL_L2_TOL
 
@@ -345,8 +356,10 @@ def test_linear_grouped_empty_experts(dev):
     a_o = (rng.random((E, K)) + 0.5).astype(np.float32)
     wc_o = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
     ws_o = rng.integers(118, 134, size=(E, N, K // 32), dtype=np.uint8)
-    y = binding.linear_grouped(x.to(dev), torch.from_numpy(off).to(dev), torch.from_numpy(a_o).to(dev), 32,
-                               torch.from_numpy(wc_o).to(dev), torch.from_numpy(ws_o).to(dev),
+    tiles = [row_major_to_gemm_layout(wc_o[e], ws_o[e]) for e in range(E)]
+    pw = binding.Packed(torch.from_numpy(np.stack([t[0] for t in tiles])).to(dev),
+                        torch.from_numpy(np.stack([t[1] for t in tiles])).to(dev), N, K)
+    y = binding.linear_grouped(x.to(dev), torch.from_numpy(off).to(dev), torch.from_numpy(a_o).to(dev), 32, pw,
                                out_dtype=torch.float32)
     y_o = oracle.linear_grouped(bits(x), off, a_o, 32, wc_o, ws_o)
     assert rel_l2(y.cpu().numpy(), y_o) <= REL_L2_TOL
@@ -356,7 +369,7 @@ def test_linear_grouped_empty_experts(dev):
 def test_linear_grouped_moe_full(dev, proj):
     mc = inputs.moe_case(proj)
     log("grouped MoE %s T=%d E=%d K=%d N=%d" % (proj, mc.T, mc.E, mc.K, mc.N))
-    y, a, wc, ws = grouped_gpu(mc, dev, 32, out_dtype=torch.float32)
+    y, a, pw = grouped_gpu(mc, dev, 32, out_dtype=torch.float32)
     torch.cuda.synchronize()
     counts = mc.counts
     experts = sorted(set([int(np.argmax(counts)), int(np.argmin(counts))] +
@@ -368,7 +381,7 @@ def test_linear_grouped_moe_full(dev, proj):
             continue
         rows = np.unique(np.concatenate([[lo, hi - 1], np.random.default_rng(e).integers(lo, hi, 4)]))
         a_o, wc_o, ws_o = oracle_expert(mc, e, 32)
-        assert np.array_equal(np_u8(wc[e]), wc_o), e
+        assert np.array_equal(packed_to_row_major(binding.expert(pw, e))[0], wc_o), e
         y_o = oracle.linear(bits(mc.x)[rows], a_o, 32, wc_o, ws_o)
         err = rel_l2(yc[rows], y_o)
         assert err <= REL_L2_TOL, (e, err)
