@@ -8,9 +8,11 @@ Weights are prepared beforehand (offline). Inputs are resident in HBM; the
 timed steps rotate through several copies of activations and weights so that
 no step finds its operands in the 256 MB last-level cache.
 
-Prints one JSON line with the metric, the plain-MXFP4 overhead, the GEMM
-kernel's roofline (HIP events around each GEMM launch on the launch stream)
-and the CPU oracle's throughput on a bounded sample of the same work.
+Steps are captured into HIP graphs (one per operand copy) and replayed, so
+the timed region has no host launch gaps. Prints one JSON line with the
+metric, the plain-MXFP4 overhead, the GEMM kernel's roofline (HIP events on
+the launch stream around graph replays of that kernel alone, per layer) and
+the CPU oracle's throughput on a bounded sample of the same work.
 """
 from __future__ import annotations
 
@@ -44,6 +46,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="if > 0: only run this many steps of the fused path (for rocprofv3) and exit")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="if > 0: only copy a MIB-MiB device buffer 3 times (the known-size reference for the "
+                        "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
 
 
@@ -104,43 +109,68 @@ def build_layers(torch, binding, inputs, cfg, shapes, M, b, dev):
     return layers
 
 
-def run_steps(torch, binding, layers, steps, offset, plain=False):
-    for i in range(steps):
-        for L in layers:
-            c = L["copies"][(offset + i) % ROTATE]
-            if plain:
-                binding.linear(c["x"], None, 0, c["wp"], out=L["y"], workspace=L["work"])
-            else:
-                binding.linear(c["x"], L["a"], L["b"], c["w"], out=L["y"], workspace=L["work"])
+def enqueue_step(binding, layers, copy, plain=False):
+    for L in layers:
+        c = L["copies"][copy]
+        if plain:
+            binding.linear(c["x"], None, 0, c["wp"], out=L["y"], workspace=L["work"])
+        else:
+            binding.linear(c["x"], L["a"], L["b"], c["w"], out=L["y"], workspace=L["work"])
 
 
-def timed(torch, fn, steps, warmup):
-    fn(warmup, 0)
+def capture(torch, fn):
+    """A HIP graph of the kernels that fn enqueues on the current stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager once on the capture stream (argument checks, warm caches)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def timed_graphs(torch, graphs, steps, warmup):
+    """Replay graphs[i % len] for warmup untimed and `steps` timed steps."""
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with Timer(torch) as t:
-        fn(steps, warmup)
+        for i in range(steps):
+            graphs[(warmup + i) % len(graphs)].replay()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return t.ms() / steps, wall
+    return t.ms() / steps, time.perf_counter() - t0
 
 
-def kernel_breakdown(torch, binding, layers, steps):
-    """The two kernels of macaq_linear called one by one (same kernels, same
-    launch configuration), HIP events around each launch."""
-    q_ms = [0.0] * len(layers)
-    g_ms = [0.0] * len(layers)
-    for i in range(steps):
-        for li, L in enumerate(layers):
-            c = L["copies"][i % ROTATE]
-            with Timer(torch) as tq:
+def kernel_breakdown(torch, binding, layers, reps):
+    """Per layer: the two kernels of macaq_linear (quantize, GEMM) each alone,
+    `reps` launches captured in one graph, timed with HIP events on the launch
+    stream around the replay; returns average ms per launch."""
+    q_ms, g_ms = [], []
+    for L in layers:
+        def quant():
+            for i in range(reps):
+                c = L["copies"][i % ROTATE]
                 binding.quant_act(c["x"], L["a"], L["b"], layout="gemm", codes=L["qa"].codes, scales=L["qa"].scales)
-            with Timer(torch) as tg:
+
+        def gemm():
+            for i in range(reps):
+                c = L["copies"][i % ROTATE]
                 binding.linear_plain_gemm(L["qa"], c["w"], out=L["y"], workspace=L["gwork"])
+
+        for fn, acc in ((quant, q_ms), (gemm, g_ms)):
+            g = capture(torch, fn)
+            g.replay()
             torch.cuda.synchronize()
-            q_ms[li] += tq.ms()
-            g_ms[li] += tg.ms()
-    return [v / steps for v in q_ms], [v / steps for v in g_ms]
+            with Timer(torch) as t:
+                g.replay()
+            torch.cuda.synchronize()
+            acc.append(t.ms() / reps)
+    return q_ms, g_ms
 
 
 def cpu_baseline(layers, target_s):
@@ -174,9 +204,19 @@ def cpu_baseline(layers, target_s):
                        % (rows, layers[0]["M"], len(layers), dt))
 
 
+def copy_mb(layers):
+    total = 0
+    for L in layers:
+        c = L["copies"][0]
+        total += c["x"].numel() * 2 + c["w"].codes.numel() + c["w"].scales.numel()
+    return total / 1e6
+
+
 def load_traffic(kernel_digest):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source."""
+    """HBM bytes (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known
+    size) per GEMM launch, the mean over the step's layers, from the committed
+    rocprofv3 counter summary; None unless it was taken on the current kernel
+    source."""
     path = os.path.join(ROOT, "profiles", "gemm_prefill_8b_pmc.json")
     if not os.path.exists(path):
         return None
@@ -184,7 +224,7 @@ def load_traffic(kernel_digest):
         d = json.load(f)
     if d.get("kernel_source_digest") != kernel_digest:
         return None
-    return d.get("hbm_bytes_per_step")
+    return d.get("hbm_bytes_per_launch_mean")
 
 
 def main():
@@ -199,6 +239,15 @@ def main():
 
     binding.load_library()
     dev = torch.device("cuda:0")
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copied_bytes": n, "copies": 3}), flush=True)
+        return
     wl = {"tiny": 1, "prefill-8b": 2, "decode-32b": 3, "moe-128e": 4, "prefill-large": 5}[args.workload]
     if wl in (3, 4):
         print("workload %s: not wired into bench.py yet" % args.workload, file=sys.stderr)
@@ -211,16 +260,18 @@ def main():
     torch.cuda.synchronize()
 
     if args.profile_steps > 0:
-        run_steps(torch, binding, layers, args.profile_steps, 0)
+        for i in range(args.profile_steps):
+            enqueue_step(binding, layers, i % ROTATE)
         torch.cuda.synchronize()
         print(json.dumps({"profiled_steps": args.profile_steps, "workload": spec["name"]}), flush=True)
         return
 
     flops = sum(2 * M * K * N for K, N in shapes)
-    ms, wall = timed(torch, lambda n, o: run_steps(torch, binding, layers, n, o), args.steps, args.warmup)
-    ms_plain, _ = timed(torch, lambda n, o: run_steps(torch, binding, layers, n, o, plain=True), args.steps,
-                        args.warmup)
-    q_ms, g_ms = kernel_breakdown(torch, binding, layers, max(10, args.steps // 2))
+    fused = [capture(torch, lambda c=c: enqueue_step(binding, layers, c)) for c in range(ROTATE)]
+    plain = [capture(torch, lambda c=c: enqueue_step(binding, layers, c, plain=True)) for c in range(ROTATE)]
+    ms, wall = timed_graphs(torch, fused, args.steps, args.warmup)
+    ms_plain, _ = timed_graphs(torch, plain, args.steps, args.warmup)
+    q_ms, g_ms = kernel_breakdown(torch, binding, layers, 20)
     tflops = flops / (ms * 1e-3) / 1e12
     gemm_ms = sum(g_ms)
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
@@ -246,6 +297,8 @@ def main():
         "plain_mxfp4_ms_per_step": round(ms_plain, 5),
         "transform_overhead_pct": round(100 * (ms / ms_plain - 1), 2),
         "wall_s_timed": round(wall, 4),
+        "timing": "HIP graphs of one step per operand copy (%d copies, %.0f MB each, cycled past the 256 MB "
+                  "last-level cache), HIP events on the launch stream" % (ROTATE, copy_mb(layers)),
         "kernels_ms": {"quant": [round(v, 5) for v in q_ms], "gemm": [round(v, 5) for v in g_ms]},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
