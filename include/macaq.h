@@ -30,14 +30,17 @@
  *     bytes (bias 127), one per 32 elements along K.
  *       MACAQ_ROW_MAJOR: codes uint8 [rows, K/2], scales uint8 [rows, K/32].
  *       MACAQ_GEMM_LAYOUT (what the GEMM reads): rows padded to RP =
- *         ceil(rows/64)*64 and K to KP = ceil(K/128)*128, the padding all
- *         zero bytes; with KB = KP/128,
- *           code byte of (r, k): ((r/16)*KB + k/128)*1024 + (r%16)*64 + (k%128)/2
- *           scale of (r, g = k/32): ((r/64)*KB + g/4)*256 + (r%64)*4 + g%4
- *         so one step of 128 elements of 16 rows is a contiguous 1 KiB block
- *         and the scales of 64 rows a contiguous 256-byte block. Sizes:
- *         macaq_packed_codes_bytes / macaq_packed_scales_bytes; each packed
- *         operand must stay under 2 GiB.
+ *         ceil(rows/32)*32 and K to KP = ceil(K/256)*256, the padding all
+ *         zero bytes, cut into blocks of 32 rows x 256 elements ordered (row
+ *         group, k block); with KB = KP/256 and, for row r and element k,
+ *         blk = (r/32)*KB + k/256, chunk c = (k%256)/32, h = c/2, j = c%2:
+ *           code byte of (r, k): blk*4096 + h*1024 + (32j + r%32)*16 + (k%32)/2
+ *           scale of (r, k):     blk*256 + (32j + r%32)*4 + h
+ *         so each 1 KiB of codes is the operand of one 32x32x64 scaled-FP4
+ *         MFMA (lane 32j + r) and one dword per lane holds its 4 scale bytes
+ *         of the block. Sizes: macaq_packed_codes_bytes /
+ *         macaq_packed_scales_bytes; each packed operand must stay under
+ *         2 GiB.
  *   - Activations X are bf16 [M, ldx] row-major. Outputs Y are [M, ldy]
  *     row-major, fp32 or bf16 (round-to-nearest-even).
  *

@@ -21,24 +21,39 @@ constexpr int kFmtFp4 = 4;
 // over them, and each XCD has its own L2.
 constexpr int kNumXcd = 8;
 
-// GEMM layout of a packed MXFP4 operand (rows x K elements): rows padded to
-// a multiple of 64, K to a multiple of 128, padding all zero.
-//   codes: 16 rows x 128 elements per 1024-byte block, blocks ordered
-//          (row block, k block); inside a block row r at r * 64, element
-//          pair (2j, 2j+1) at byte j (low nibble first).
-//   scales: 64 rows x 4 groups per 256-byte block, blocks ordered
-//          (64-row block, k block); inside a block row r at r * 4 + g.
-constexpr int kTileRows = 16;
-constexpr int kTileK = 128;
-constexpr int kCodeBlock = kTileRows * kTileK / 2;     // 1024
-constexpr int kScaleRows = 64;
-constexpr int kScaleBlock = kScaleRows * kTileK / 32;  // 256
-constexpr int kRowPad = 64;
+// GEMM layout of a packed MXFP4 operand (rows x K elements): rows padded to a
+// multiple of 32, K to a multiple of 256, padding all zero. The operand is cut
+// into blocks of 32 rows x 256 elements, ordered (row group, k block). Inside
+// a block the 8 chunks of 32 elements of a row are numbered c = 2h + j
+// (h = 0..3, j = 0..1), and
+//   codes:  4096 bytes; chunk (r, c) holds 16 bytes at h*1024 + (32j + r)*16
+//           (element pair (2i, 2i+1) of the chunk at byte i, low nibble first);
+//   scales: 256 bytes; the E8M0 byte of chunk (r, c) at (32j + r)*4 + h.
+// So 1 KiB of codes (h fixed) is exactly the operand of one scaled-FP4 MFMA
+// 32x32x64 over K elements [64h, 64h + 64) of the block (lane l = 32j + r), and
+// one dword per lane holds the lane's scales for the 4 MFMAs of the block.
+constexpr int kGroupRows = 32;
+constexpr int kBlockK = 256;
+constexpr int kCodeBlock = kGroupRows * kBlockK / 2;      // 4096
+constexpr int kCodeHalf = kCodeBlock / 4;                 // 1024: one MFMA operand
+constexpr int kScaleBlock = kGroupRows * kBlockK / 32;    // 256
 
-__host__ __device__ inline int64_t pad_rows(int64_t r) { return (r + kRowPad - 1) / kRowPad * kRowPad; }
-__host__ __device__ inline int64_t pad_k(int64_t k) { return (k + kTileK - 1) / kTileK * kTileK; }
+__host__ __device__ inline int64_t pad_rows(int64_t r) { return (r + kGroupRows - 1) / kGroupRows * kGroupRows; }
+__host__ __device__ inline int64_t pad_k(int64_t k) { return (k + kBlockK - 1) / kBlockK * kBlockK; }
 __host__ __device__ inline int64_t tiled_codes_bytes(int64_t rows, int64_t K) { return pad_rows(rows) * pad_k(K) / 2; }
 __host__ __device__ inline int64_t tiled_scales_bytes(int64_t rows, int64_t K) { return pad_rows(rows) * pad_k(K) / 32; }
+
+// Byte offsets of element k's code byte and of its group's scale for row r.
+__host__ __device__ inline int64_t tiled_code_offset(int64_t r, int64_t k, int64_t kpad) {
+  const int64_t c = (k % kBlockK) / 32;
+  return ((r / kGroupRows) * (kpad / kBlockK) + k / kBlockK) * kCodeBlock + (c >> 1) * kCodeHalf +
+         ((c & 1) * kGroupRows + r % kGroupRows) * 16 + (k % 32) / 2;
+}
+__host__ __device__ inline int64_t tiled_scale_offset(int64_t r, int64_t k, int64_t kpad) {
+  const int64_t c = (k % kBlockK) / 32;
+  return ((r / kGroupRows) * (kpad / kBlockK) + k / kBlockK) * kScaleBlock +
+         ((c & 1) * kGroupRows + r % kGroupRows) * 4 + (c >> 1);
+}
 
 struct QuantArgs {
   const void* x;         // bf16 or fp32 rows [M, ldx]
@@ -58,10 +73,10 @@ hipError_t launch_multipliers(const float* s, int64_t K, float cb, float* a, flo
 hipError_t launch_quant_rows(const QuantArgs& q, int b, bool x_is_f32, hipStream_t stream);
 
 struct GemmArgs {
-  const uint8_t* a_codes;   // [M, K/2]
-  const uint8_t* a_scales;  // [M, K/32]
-  const uint8_t* b_codes;   // [N, K/2] (per expert when grouped)
-  const uint8_t* b_scales;  // [N, K/32]
+  const uint8_t* a_codes;   // GEMM layout, M rows (T rows when grouped)
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;   // GEMM layout, N rows (per expert when grouped)
+  const uint8_t* b_scales;
   int64_t M, N, K;
   void* y;                  // [M, ldy]
   int64_t ldy;
@@ -73,6 +88,8 @@ struct GemmArgs {
   int32_t* tile_map;        // workspace: per m-tile (expert, first row)
   int E;
   int64_t max_mtiles;
+  // set by the launcher: outputs may be stored as 4-element vectors
+  bool vec_y, vec_partial;
 };
 
 struct GemmPlan {

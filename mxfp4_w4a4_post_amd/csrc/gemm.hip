@@ -3,71 +3,73 @@
 // Y[m, n] = sum_k dq(A[m, k]) dq(W'[n, k]): the contraction of the MACaQ
 // layer ("MACaQ: Fast, Model Agnostic Calibrated Quantization for
 // Low-Precision Weights and Activations", paper card, Abstract: MXFP4 W4A4).
-// Both operands are K-major packed E2M1 with one E8M0 scale per 32 elements,
-// which is exactly the operand layout of V_MFMA_SCALE_F32_*_F8F6F4 in FP4
-// mode: each lane of an MFMA holds 32 consecutive K elements (16 bytes) of one
-// row plus that row's E8M0 byte for those 32 elements.
+// Both operands are packed E2M1 with one E8M0 scale per 32 elements along K,
+// in the GEMM layout (common.hpp): every 1 KiB of codes is one operand of
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 in FP4 mode (lane l = row l%32, 32 K
+// elements), and one scale dword per lane serves the 4 MFMAs of a 256-element
+// block through op_sel.
 //
-//   32x32x64: lane l holds row l%32, K elements [32*(l/32), +32); output
-//             register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, col l%32.
-//   16x16x128: lane l holds row l%16, K elements [32*(l/16), +32); output
-//             register r of lane l is row 4*(l/16) + r, col l%16.
-// A is the activation operand (output rows m), B the weights (output cols n),
-// so consecutive lanes store consecutive n.
+// The weights are the MFMA's first operand (output rows = n) and the
+// activations its second (output columns = m), so output register r of lane l
+// of a 32x32 tile is n = 8*(r/4) + 4*(l/32) + r%4, m = l%32: each lane holds
+// runs of 4 consecutive n of one output row, stored as 8- or 16-byte vectors.
 //
-// Both operands come in the GEMM layout (16-row x 128-element blocks of 1 KiB,
-// 64-row scale blocks of 256 bytes, zero padding). A workgroup owns a
-// BM x BN output tile and walks K in steps of BK = 128 elements. Buffer loads,
-// each one contiguous block per wave, run PD steps ahead of the matrix cores,
-// held in registers; each step's codes and scales are then written to one of
-// three LDS buffers, and its MFMA fragments are read back one step ahead of
-// their use. The four 16-byte chunks of each LDS row are XOR-swizzled so that
-// the fragment reads of 8 or 16 consecutive rows fall in distinct banks.
+// A workgroup of 4 waves owns a BM x BN output tile and walks K in steps of
+// one 256-element block. The waves split BN: each owns BN/4 weight rows and
+// all BM activation rows. The weights of a wave are used by that wave only, so
+// they go from memory straight into the registers the MFMAs read, PW steps
+// ahead. The activation block of a step is shared by all 4 waves: it is loaded
+// PA steps ahead into registers, written to one of three LDS buffers, and
+// each wave reads its MFMA fragments back one half-step ahead of their use.
+// LDS holds only the activations, with the layout's fragment order, so every
+// LDS access of a wave is 64 consecutive 16-byte (or 4-byte) words.
 #include "common.hpp"
 
 namespace macaq {
 namespace {
 
-constexpr int BK = 128;        // K elements per step
-constexpr int RB = BK / 2;     // code bytes per row per step (4 chunks of 16)
-constexpr int CPR = RB / 16;   // 16-byte chunks per row per step
-constexpr int SB = BK / 32;    // scale bytes per row per step (one dword)
+constexpr int NH = kBlockK / 64;  // MFMAs along K per step (4)
+constexpr int NT = 256;           // 4 waves
 constexpr int kNumCu = 256;
 
-template <int BM_, int BN_, int WM_, int WN_, int MF_, int PD_>
+constexpr int lcm2(int a, int b) {
+  int x = a, y = b;
+  while (y) {
+    const int t = x % y;
+    x = y;
+    y = t;
+  }
+  return a / x * b;
+}
+
+template <int BM_, int BN_, int PW_, int PA_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MF = MF_, PD = PD_;
-  static constexpr int NT = WM * WN * 64;
-  static constexpr int TM = BM / WM, TN = BN / WN;
-  static constexpr int FM = TM / MF, FN = TN / MF;
-  static constexpr int KSUB = (MF == 32) ? 64 : 128;  // K per MFMA
-  static constexpr int NSUB = BK / KSUB;              // MFMAs along K per step
-  static constexpr int A_CHUNKS = BM * CPR;
-  static constexpr int B_CHUNKS = BN * CPR;
-  static constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
-  static constexpr int B_PER_T = (B_CHUNKS + NT - 1) / NT;
-  static constexpr int A_SC_PER_T = (BM + NT - 1) / NT;
-  static constexpr int B_SC_PER_T = (BN + NT - 1) / NT;
-  static constexpr int LDS_A = BM * RB, LDS_B = BN * RB, LDS_AS = BM * SB, LDS_BS = BN * SB;
-  // writes of threads that have no chunk (small tiles) land in a trash area,
-  // so the stores of a step need no branches
-  static constexpr int LDS_TRASH = NT * 16;
-  static constexpr int LDS_STAGE = LDS_A + LDS_B + LDS_AS + LDS_BS + LDS_TRASH;
+  static constexpr int BM = BM_, BN = BN_, PW = PW_, PA = PA_;
+  static constexpr int FM = BM / kGroupRows;  // activation fragments (32 rows each)
+  static constexpr int WN = BN / 4;           // weight rows per wave
+  static constexpr int FN = WN / kGroupRows;  // weight fragments per wave
+  static constexpr int A_CODES = FM * kCodeBlock;
+  static constexpr int A_SCALES = FM * kScaleBlock;
+  static constexpr int A_SCALE_THREADS = FM * 64;  // one scale dword each
+  // scale writes of threads without a scale dword land in a trash area, so
+  // the stores of a step need no branches
+  static constexpr int LDS_TRASH = NT * 4;
+  static constexpr int STAGE = A_CODES + A_SCALES + LDS_TRASH;
   static constexpr int NBUF = 3;  // LDS buffers: compute s, read s+1, write s+2
-  static constexpr int LDS_BYTES = NBUF * LDS_STAGE;
-  static_assert(TM % MF == 0 && TN % MF == 0, "wave tile must be a multiple of the MFMA tile");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
-  static_assert(PD >= 2 && PD <= 4, "prefetch depth");
-  // main-loop unroll: LDS buffer, register slot and fragment set all static
-  static constexpr int U = (PD == 4) ? 12 : 6;
-  // instructions per step, for the interleaving of the schedule
+  static constexpr int LDS_BYTES = NBUF * STAGE;
+  // main-loop unroll: register slots static
+  static constexpr int U = lcm2(PW, PA);
   static constexpr int N_MFMA = FM * FN;  // per half step
-  static constexpr int N_DSR = FM + FN;
-  static constexpr int N_DSW = A_PER_T + B_PER_T + A_SC_PER_T + B_SC_PER_T;
-  static constexpr int N_VMEM = A_PER_T + B_PER_T + A_SC_PER_T + B_SC_PER_T;
+  static_assert(BM % kGroupRows == 0 && BN % (4 * kGroupRows) == 0, "tile shape");
+  static_assert(FM <= 4, "at most one scale dword per thread");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+  static_assert(PW >= 2 && PA >= 2, "prefetch depths");
+  // the leading zero steps that round the step count up to a multiple of U
+  // must all be loaded by the prologue
+  static_assert(U - 1 <= PW - 1 && U - 1 <= PA + 1, "prologue covers the padding steps");
 };
 
-// Rows [m0, m_end) of A against rows [n0, n0 + BN) of B over k-steps
+// Rows [m0, m_end) of A against rows [n0, n0 + BN) of B over k-blocks
 // [kt_begin, kt_end).
 struct TileCoord {
   int64_t m0, m_end, n0;
@@ -75,25 +77,7 @@ struct TileCoord {
   int split;
 };
 
-template <class C>
-struct Stage {
-  v4i a[C::A_PER_T];
-  v4i b[C::B_PER_T];
-  uint32_t as[C::A_SC_PER_T];
-  uint32_t bs[C::B_SC_PER_T];
-};
-
-// Byte offset of 16-byte chunk `chunk` of LDS row `row`. The chunk slot is
-// XORed with (r3 ^ r1, r2) of the row index: any 16 consecutive rows then
-// cover all 16 bank groups of 16 bytes for one chunk, and any 8 consecutive
-// rows cover all 8 groups of a 128-byte bank set.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  const int f = ((((row >> 3) ^ (row >> 1)) & 1) << 1) | ((row >> 2) & 1);
-  return row * RB + ((chunk ^ f) << 4);
-}
-
-// Buffer resources over the operand arrays (GEMM layout, zero padded to 64
-// rows and a multiple of 128 in K): loads beyond num_records return zero.
+// Buffer resources over the operand arrays: loads past num_records return 0.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer on gfx9
 constexpr uint32_t kOob = 0x80000000u;  // an offset past every buffer (all are < 2 GiB)
@@ -102,219 +86,50 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
 }
 
-struct Operands {
-  Rsrc ac, as, bc, bs;  // A codes / scales, B codes / scales (this expert's)
-  int64_t N, K;
+// soff is the k-block's offset, uniform over the workgroup; readfirstlane
+// states that, so it always travels in a scalar register.
+__device__ __forceinline__ v4i load16(Rsrc r, uint32_t voff, int soff) {
+  return __builtin_bit_cast(
+      v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, __builtin_amdgcn_readfirstlane(soff), 0));
+}
+__device__ __forceinline__ uint32_t load4(Rsrc r, uint32_t voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, __builtin_amdgcn_readfirstlane(soff), 0);
+}
+
+template <class C>
+struct WStage {  // one step of this wave's weights
+  v4i c[C::FN][NH];
+  uint32_t s[C::FN];
 };
-
-// Per-thread byte offsets of the rows this thread loads, fixed for the tile
-// (kOob for rows past the padded operand). In the GEMM layout a k-step of 16
-// rows is one 1 KiB block and of 64 rows' scales one 256-byte block, so a
-// wave's 16-byte loads of 16 rows read one contiguous block, and the step
-// adds kt * 1024 (kt * 256) through the scalar offset.
 template <class C>
-struct LoadOffsets {
-  uint32_t a[C::A_PER_T], b[C::B_PER_T], as[C::A_SC_PER_T], bs[C::B_SC_PER_T];
+struct AStage {  // this thread's share of one step of the activation block
+  v4i c[C::FM];
+  uint32_t s;
 };
-
-__device__ __forceinline__ uint32_t code_offset(int64_t row, int kc, int64_t ktp, int64_t rows_pad) {
-  if (row >= rows_pad) return kOob;
-  return (uint32_t)(((row / kTileRows) * ktp) * kCodeBlock + (row % kTileRows) * RB + kc * 16);
-}
-__device__ __forceinline__ uint32_t scale_offset(int64_t row, int64_t ktp, int64_t rows_pad) {
-  if (row >= rows_pad) return kOob;
-  return (uint32_t)(((row / kScaleRows) * ktp) * kScaleBlock + (row % kScaleRows) * 4);
-}
-
 template <class C>
-__device__ __forceinline__ void make_offsets(LoadOffsets<C>& lo, const TileCoord& tc, int64_t a_rows, int64_t N,
-                                             int64_t K) {
-  const int tid = threadIdx.x;
-  const int64_t ktp = pad_k(K) / BK, a_pad = pad_rows(a_rows), n_pad = pad_rows(N);
-#pragma unroll
-  for (int i = 0; i < C::A_PER_T; ++i) {
-    const int c = tid + i * C::NT;
-    lo.a[i] = c < C::A_CHUNKS ? code_offset(tc.m0 + c / CPR, c % CPR, ktp, a_pad) : kOob;
-  }
-#pragma unroll
-  for (int i = 0; i < C::B_PER_T; ++i) {
-    const int c = tid + i * C::NT;
-    lo.b[i] = c < C::B_CHUNKS ? code_offset(tc.n0 + c / CPR, c % CPR, ktp, n_pad) : kOob;
-  }
-#pragma unroll
-  for (int i = 0; i < C::A_SC_PER_T; ++i) {
-    const int row = tid + i * C::NT;
-    lo.as[i] = row < C::BM ? scale_offset(tc.m0 + row, ktp, a_pad) : kOob;
-  }
-#pragma unroll
-  for (int i = 0; i < C::B_SC_PER_T; ++i) {
-    const int row = tid + i * C::NT;
-    lo.bs[i] = row < C::BN ? scale_offset(tc.n0 + row, ktp, n_pad) : kOob;
-  }
-}
-
-// Loads of one k-step, branch-free.
-template <class C>
-__device__ __forceinline__ void load_stage(Stage<C>& st, const Operands& o, const LoadOffsets<C>& lo, int64_t kt) {
-  const int kb = (int)(kt * kCodeBlock), ks = (int)(kt * kScaleBlock);
-#pragma unroll
-  for (int i = 0; i < C::A_PER_T; ++i)
-    st.a[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(o.ac, (int)lo.a[i], kb, 0));
-#pragma unroll
-  for (int i = 0; i < C::B_PER_T; ++i)
-    st.b[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(o.bc, (int)lo.b[i], kb, 0));
-#pragma unroll
-  for (int i = 0; i < C::A_SC_PER_T; ++i) st.as[i] = __builtin_amdgcn_raw_buffer_load_b32(o.as, (int)lo.as[i], ks, 0);
-#pragma unroll
-  for (int i = 0; i < C::B_SC_PER_T; ++i) st.bs[i] = __builtin_amdgcn_raw_buffer_load_b32(o.bs, (int)lo.bs[i], ks, 0);
-}
-
-// Per-lane LDS byte offsets, fixed for the kernel. The swizzle depends only
-// on bits 1..3 of the row, and every other chunk, fragment or stage this lane
-// touches sits a multiple of 16 rows (or a whole buffer) away, so one base
-// offset plus a compile-time constant addresses each access.
-template <class C>
-struct LdsOffsets {
-  int wa[C::A_PER_T], wb[C::B_PER_T];           // store_stage: code chunks of this thread
-  int wsa[C::A_SC_PER_T], wsb[C::B_SC_PER_T];   // store_stage: scale words of this thread
-  int ra[C::NSUB], rb[C::NSUB];  // fragment reads of MFMA s along K, fragment 0
-  int rsa, rsb;                  // scale reads, fragment 0
+struct AFrag {  // activation MFMA operands of one half step
+  v4i c[C::FM];
 };
-
-template <class C>
-__device__ __forceinline__ void make_lds_offsets(LdsOffsets<C>& l, int wm, int wn, int lane) {
-  const int tid = threadIdx.x;
-  const int trash = C::LDS_A + C::LDS_B + C::LDS_AS + C::LDS_BS + 16 * tid;
-#pragma unroll
-  for (int i = 0; i < C::A_PER_T; ++i) {
-    const int c = tid + i * C::NT;
-    l.wa[i] = c < C::A_CHUNKS ? swz(c / CPR, c % CPR) : trash;
-  }
-#pragma unroll
-  for (int i = 0; i < C::B_PER_T; ++i) {
-    const int c = tid + i * C::NT;
-    l.wb[i] = c < C::B_CHUNKS ? C::LDS_A + swz(c / CPR, c % CPR) : trash;
-  }
-#pragma unroll
-  for (int i = 0; i < C::A_SC_PER_T; ++i) {
-    const int row = tid + i * C::NT;
-    l.wsa[i] = row < C::BM ? C::LDS_A + C::LDS_B + 4 * row : trash;
-  }
-#pragma unroll
-  for (int i = 0; i < C::B_SC_PER_T; ++i) {
-    const int row = tid + i * C::NT;
-    l.wsb[i] = row < C::BN ? C::LDS_A + C::LDS_B + C::LDS_AS + 4 * row : trash;
-  }
-  constexpr int LM = C::MF - 1;
-#pragma unroll
-  for (int s = 0; s < C::NSUB; ++s) {
-    const int chunk = (C::MF == 32) ? s * 2 + (lane >> 5) : (lane >> 4);
-    l.ra[s] = swz(wm * C::TM + (lane & LM), chunk);
-    l.rb[s] = C::LDS_A + swz(wn * C::TN + (lane & LM), chunk);
-  }
-  l.rsa = C::LDS_A + C::LDS_B + 4 * (wm * C::TM + (lane & LM));
-  l.rsb = C::LDS_A + C::LDS_B + C::LDS_AS + 4 * (wn * C::TN + (lane & LM));
-}
 
 template <class T>
 __device__ __forceinline__ T& lds_at(uint8_t* smem, int off) {
   return *reinterpret_cast<T*>(smem + off);
 }
 
-template <class C, int BUF>
-__device__ __forceinline__ void store_stage(const Stage<C>& st, uint8_t* smem, const LdsOffsets<C>& l) {
-  constexpr int B0 = BUF * C::LDS_STAGE;
-#pragma unroll
-  for (int i = 0; i < C::A_PER_T; ++i) lds_at<v4i>(smem, l.wa[i] + B0) = st.a[i];
-#pragma unroll
-  for (int i = 0; i < C::B_PER_T; ++i) lds_at<v4i>(smem, l.wb[i] + B0) = st.b[i];
-#pragma unroll
-  for (int i = 0; i < C::A_SC_PER_T; ++i) lds_at<uint32_t>(smem, l.wsa[i] + B0) = st.as[i];
-#pragma unroll
-  for (int i = 0; i < C::B_SC_PER_T; ++i) lds_at<uint32_t>(smem, l.wsb[i] + B0) = st.bs[i];
-}
-
-template <int OPSEL>
-__device__ __forceinline__ v16f mfma32(v4i a, v4i b, v16f c, int sa, int sb) {
+__device__ __forceinline__ v16f mfma(v4i a, v4i b, v16f c, int sa, int sb, int h) {
   v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
   v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, kFmtFp4, kFmtFp4, OPSEL, sa, OPSEL, sb);
-}
-
-template <int OPSEL>
-__device__ __forceinline__ v4f mfma16(v4i a, v4i b, v4f c, int sa, int sb) {
-  v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
-  v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, kFmtFp4, kFmtFp4, OPSEL, sa, OPSEL, sb);
-}
-
-template <class C, bool = (C::MF == 32)>
-struct Acc {
-  v16f v[C::FM][C::FN];
-};
-template <class C>
-struct Acc<C, false> {
-  v4f v[C::FM][C::FN];
-};
-
-// This lane's scale byte for each MFMA of the step, gathered into one dword
-// (byte s feeds MFMA s through op_sel). The step's 4 scale bytes of a row are
-// one dword; 32x32x64 MFMA s covers bytes 2s, 2s+1 and lane l uses byte
-// 2s + l/32; 16x16x128 covers all 4 and lane l uses byte l/16.
-template <int MF>
-__device__ __forceinline__ int gather_scales(uint32_t w, int lane) {
-  if constexpr (MF == 32) {
-    const uint32_t h = (uint32_t)(lane >> 5);
-    return (int)__builtin_amdgcn_perm(w, w, 0x0C0C0000u | ((2u + h) << 8) | h);
-  } else {
-    return (int)((w >> (8 * (lane >> 4))) & 0xFFu);
+  switch (h) {  // op_sel picks the scale byte of the half step: an immediate
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, kFmtFp4, kFmtFp4, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, kFmtFp4, kFmtFp4, 1, sa, 1, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, kFmtFp4, kFmtFp4, 2, sa, 2, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, kFmtFp4, kFmtFp4, 3, sa, 3, sb);
   }
 }
 
-// MFMA operands of this wave for one MFMA along K ("half" of a step when
-// NSUB == 2, the whole step when NSUB == 1), and a step's scale dwords.
-template <class C>
-struct Half {
-  v4i a[C::FM];
-  v4i b[C::FN];
-};
-template <class C>
-struct Scl {
-  int sa[C::FM], sb[C::FN];
-};
-
-template <class C, int SUB, int BUF>
-__device__ __forceinline__ void read_half(Half<C>& h, uint8_t* smem, const LdsOffsets<C>& l) {
-  constexpr int B0 = BUF * C::LDS_STAGE;
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) h.a[i] = lds_at<v4i>(smem, l.ra[SUB] + B0 + i * C::MF * RB);
-#pragma unroll
-  for (int j = 0; j < C::FN; ++j) h.b[j] = lds_at<v4i>(smem, l.rb[SUB] + B0 + j * C::MF * RB);
-}
-
-template <class C, int BUF>
-__device__ __forceinline__ void read_scales(Scl<C>& sc, uint8_t* smem, const LdsOffsets<C>& l, int lane) {
-  constexpr int B0 = BUF * C::LDS_STAGE;
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) sc.sa[i] = gather_scales<C::MF>(lds_at<uint32_t>(smem, l.rsa + B0 + 4 * i * C::MF), lane);
-#pragma unroll
-  for (int j = 0; j < C::FN; ++j) sc.sb[j] = gather_scales<C::MF>(lds_at<uint32_t>(smem, l.rsb + B0 + 4 * j * C::MF), lane);
-}
-
-template <class C, int SUB>
-__device__ __forceinline__ void mfma_half(Acc<C>& acc, const Half<C>& h, const Scl<C>& sc) {
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      if constexpr (C::MF == 32) acc.v[i][j] = mfma32<SUB>(h.a[i], h.b[j], acc.v[i][j], sc.sa[i], sc.sb[j]);
-      else acc.v[i][j] = mfma16<SUB>(h.a[i], h.b[j], acc.v[i][j], sc.sa[i], sc.sb[j]);
-    }
-}
-
-// Scheduling hints for one step: each MFMA is followed by a share of the
-// step's LDS reads (next fragments), LDS writes (step s+2) and buffer loads,
-// so the matrix core stays busy while the memory traffic is issued.
+// Scheduling hints: each MFMA is followed by a share of the half step's LDS
+// reads, LDS writes and buffer loads, so the matrix core stays busy while the
+// memory traffic is issued.
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
 
 template <int T, int NM, int NR, int NW, int NV>
@@ -331,181 +146,314 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return u >> 16;
 }
 
-// Tile-relative row / column of register r of fragment (i, j) of this lane.
 template <class C>
-__device__ __forceinline__ int frag_row(int i, int r, int lane) {
-  if constexpr (C::MF == 32) return i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-  else return i * 16 + 4 * (lane >> 4) + r;
-}
-template <class C>
-__device__ __forceinline__ int frag_col(int j, int lane) {
-  if constexpr (C::MF == 32) return j * 32 + (lane & 31);
-  else return j * 16 + (lane & 15);
-}
+struct Acc {
+  v16f v[C::FM][C::FN];
+};
 
 // OUT: 0 fp32 to Y, 1 bf16 to Y, 2 fp32 to the split-K partial buffer.
-template <class C, int OUT, bool FULL>
+// Fragment (i, jn), register 4q + e of lane l: m = 32i + l%32,
+// n = 32jn + 8q + 4(l/32) + e. VEC: every run of 4 n may be stored as one
+// vector (aligned rows, ld a multiple of 4); FULL: no bounds checks.
+template <class C, int OUT, bool VEC, bool FULL>
 __device__ __forceinline__ void store_frags(const Acc<C>& acc, void* base, int64_t ld, int64_t m_lim, int64_t n_lim,
                                             int lane) {
-  constexpr int NR = (C::MF == 32) ? 16 : 4;
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+  for (int i = 0; i < C::FM; ++i) {
+    const int m = i * 32 + (lane & 31);
+    if (!FULL && m >= m_lim) continue;
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int n = frag_col<C>(j, lane);
-      if (!FULL && n >= n_lim) continue;
+    for (int jn = 0; jn < C::FN; ++jn)
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int m = frag_row<C>(i, r, lane);
-        if (!FULL && m >= m_lim) continue;
-        const float v = acc.v[i][j][r];
-        if constexpr (OUT == 1) static_cast<uint16_t*>(base)[m * ld + n] = f32_to_bf16_rne(v);
-        else static_cast<float*>(base)[m * ld + n] = v;
+      for (int q = 0; q < 4; ++q) {
+        const int n = jn * 32 + 8 * q + 4 * (lane >> 5);
+        const v16f& a = acc.v[i][jn];
+        if (VEC && (FULL || n + 3 < n_lim)) {
+          if constexpr (OUT == 1) {
+            uint2 w;
+            w.x = f32_to_bf16_rne(a[4 * q]) | (f32_to_bf16_rne(a[4 * q + 1]) << 16);
+            w.y = f32_to_bf16_rne(a[4 * q + 2]) | (f32_to_bf16_rne(a[4 * q + 3]) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + m * ld + n) = w;
+          } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(base) + m * ld + n) =
+                make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (!FULL && n + e >= n_lim) continue;
+            if constexpr (OUT == 1) static_cast<uint16_t*>(base)[m * ld + n + e] = (uint16_t)f32_to_bf16_rne(a[4 * q + e]);
+            else static_cast<float*>(base)[m * ld + n + e] = a[4 * q + e];
+          }
+        }
       }
-    }
-}
-
-template <class C>
-__device__ __forceinline__ void store_out(const Acc<C>& acc, const GemmArgs& g, const TileCoord& tc, int wm, int wn,
-                                          int lane) {
-  const int64_t m0 = tc.m0 + wm * C::TM, n0 = tc.n0 + wn * C::TN;
-  const int64_t m_lim = tc.m_end - m0, n_lim = g.N - n0;
-  const bool full = m_lim >= C::TM && n_lim >= C::TN;
-  if (g.splits > 1) {
-    float* p = g.partial + (int64_t)tc.split * g.M * g.N + m0 * g.N + n0;
-    if (full) store_frags<C, 2, true>(acc, p, g.N, m_lim, n_lim, lane);
-    else store_frags<C, 2, false>(acc, p, g.N, m_lim, n_lim, lane);
-  } else if (g.y_bf16) {
-    uint16_t* p = static_cast<uint16_t*>(g.y) + m0 * g.ldy + n0;
-    if (full) store_frags<C, 1, true>(acc, p, g.ldy, m_lim, n_lim, lane);
-    else store_frags<C, 1, false>(acc, p, g.ldy, m_lim, n_lim, lane);
-  } else {
-    float* p = static_cast<float*>(g.y) + m0 * g.ldy + n0;
-    if (full) store_frags<C, 0, true>(acc, p, g.ldy, m_lim, n_lim, lane);
-    else store_frags<C, 0, false>(acc, p, g.ldy, m_lim, n_lim, lane);
   }
 }
 
-// The pipelined K loop. Per step s (0-based from kt_begin) and per half h
-// (one MFMA along K; NSUB halves per step):
-//   - the MFMAs of (s, h) run on fragments already in registers while the
-//     fragments of the next half are read from LDS into the other register
-//     set: (s, 1) from buffer s % 3, or (s+1, 0) from buffer (s+1) % 3;
-//   - in the last half, step s+2 goes from its register slot to LDS buffer
-//     (s+2) % 3 and the slot is refilled from memory with step s+2+PD;
+template <class C, int OUT>
+__device__ __forceinline__ void store_sel(const Acc<C>& acc, void* p, int64_t ld, int64_t m_lim, int64_t n_lim,
+                                          bool vec, int lane) {
+  const bool full = m_lim >= C::BM && n_lim >= C::WN;
+  if (vec) {
+    if (full) store_frags<C, OUT, true, true>(acc, p, ld, m_lim, n_lim, lane);
+    else store_frags<C, OUT, true, false>(acc, p, ld, m_lim, n_lim, lane);
+  } else {
+    store_frags<C, OUT, false, false>(acc, p, ld, m_lim, n_lim, lane);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void store_out(const Acc<C>& acc, const GemmArgs& g, const TileCoord& tc, int wave,
+                                          int lane) {
+  const int64_t m0 = tc.m0, n0 = tc.n0 + wave * C::WN;
+  const int64_t m_lim = tc.m_end - m0, n_lim = g.N - n0;
+  if (n_lim <= 0) return;
+  if (g.splits > 1) {
+    float* p = g.partial + (int64_t)tc.split * g.M * g.N + m0 * g.N + n0;
+    store_sel<C, 2>(acc, p, g.N, m_lim, n_lim, g.vec_partial, lane);
+  } else if (g.y_bf16) {
+    store_sel<C, 1>(acc, static_cast<uint16_t*>(g.y) + m0 * g.ldy + n0, g.ldy, m_lim, n_lim, g.vec_y, lane);
+  } else {
+    store_sel<C, 0>(acc, static_cast<float*>(g.y) + m0 * g.ldy + n0, g.ldy, m_lim, n_lim, g.vec_y, lane);
+  }
+}
+
+// The pipelined K loop over k-blocks [kt0, kt0 + nsteps). Per step s and
+// half step h (one MFMA along K, 4 per step):
+//   - the MFMAs of (s, h) read the weight registers of step s (slot s % PW)
+//     and the activation fragments of (s, h), read from LDS during the
+//     previous half step; meanwhile the fragments of the next half are read:
+//     (s, h+1) from buffer s % 3, or (s+1, 0) and step s+1's scales from
+//     buffer (s+1) % 3;
+//   - after the MFMAs of (s, h), the weight registers of half h are refilled
+//     with step s+PW (the scale dwords after the last half);
+//   - in half 0, the activation block of step s+2 goes from its register
+//     slot to LDS buffer (s+2) % 3; in half 1 the slot is refilled from
+//     memory with step s+2+PA;
 //   - one barrier ends the step.
-// Buffer (s+2) % 3 held step s-1, whose last reads were issued in step s-1
-// and completed at its barrier; buffer (s+1) % 3 was written during step s-1
-// and is visible after that barrier. The loop is unrolled U times so the
-// register slot (s+2) % PD, the fragment set and the scale set are static, and
-// its steady state has no branches, so each wait covers only what it needs.
+// Buffer (s+2) % 3 held step s-1, whose reads all completed before the MFMAs
+// of step s-1 were issued, that is before its closing barrier; buffer
+// (s+1) % 3 was written during step s-1 and is visible after that barrier.
+// Every load and LDS store is unconditional: those of the last steps reach
+// past the range and read the blocks that follow in memory, or zeros past the
+// end of the operand, and nothing uses what they bring. The loop is unrolled
+// U = lcm(PW, PA) times so the register slots are static, and the step count
+// is rounded up to a multiple of U by leading steps whose loads all return
+// zero (a resource of zero bytes), so their MFMAs add nothing. The loop thus
+// has one exit and no other branch, and each wait the compiler places covers
+// only what it needs.
 template <class C>
 struct Pipe {
   Acc<C> acc;
-  Stage<C> st[C::PD];
-  Half<C> hf[2];
-  Scl<C> sc[2];
-  LoadOffsets<C> lo;
-  LdsOffsets<C> lds;
-  const Operands& o;
-  int64_t kt0, nsteps;
+  WStage<C> w[C::PW];
+  AStage<C> a[C::PA];
+  AFrag<C> af[2];
+  uint32_t asc[C::FM], asc_next[C::FM];  // activation scale dwords, this / next step
+  Rsrc ac, as, bc, bs;
+  uint32_t a_off[C::FM], as_off;  // this thread's activation loads
+  uint32_t w_off[C::FN], ws_off[C::FN];  // this wave's weight loads
+  int la_w, la_ws;                // LDS: this thread's code / scale stores
+  int lr, lrs;                    // LDS: this lane's fragment / scale reads
+  int b_cur, b_next, b_fill;      // LDS byte offsets of the buffers of steps s, s+1, s+2
+  int64_t kt0, nsteps;            // k-block of step 0 (a zero step if pad > 0), steps
+  int pad;                        // leading zero steps
   uint8_t* smem;
-  int lane;
 
-  __device__ __forceinline__ Pipe(const Operands& o_, const TileCoord& tc, int64_t a_rows, uint8_t* smem_, int wm,
-                                  int wn, int lane_)
-      : o(o_), kt0(tc.kt_begin), nsteps(tc.kt_end - tc.kt_begin), smem(smem_), lane(lane_) {
-    make_offsets<C>(lo, tc, a_rows, o_.N, o_.K);
-    make_lds_offsets<C>(lds, wm, wn, lane_);
+  __device__ __forceinline__ Pipe(const GemmArgs& g, const TileCoord& tc, int64_t a_rows, const uint8_t* bcodes,
+                                  const uint8_t* bscales, uint8_t* smem_, int wave, int lane)
+      : smem(smem_) {
+    const int tid = threadIdx.x;
+    const int64_t n = tc.kt_end - tc.kt_begin;
+    pad = (int)((C::U - n % C::U) % C::U);
+    kt0 = tc.kt_begin - pad;
+    nsteps = n + pad;
+    const int64_t kpad = pad_k(g.K), a_pad = pad_rows(a_rows), n_pad = pad_rows(g.N);
+    ac = make_rsrc(g.a_codes, tiled_codes_bytes(a_rows, g.K));
+    as = make_rsrc(g.a_scales, tiled_scales_bytes(a_rows, g.K));
+    bc = make_rsrc(bcodes, tiled_codes_bytes(g.N, g.K));
+    bs = make_rsrc(bscales, tiled_scales_bytes(g.N, g.K));
+    // activations: thread t loads byte 16t of each 4 KiB fragment block, which
+    // belongs to lane t%64 of half t/64; the row is per thread, so a tile may
+    // start at any row (MoE experts)
+    const int hl = tid >> 6, ln = tid & 63;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      const int64_t row = tc.m0 + i * kGroupRows + (ln & 31);
+      a_off[i] = row < a_pad ? (uint32_t)(tiled_code_offset(row, (int64_t)(2 * hl + (ln >> 5)) * 32, kpad)) : kOob;
+    }
+    {
+      const int64_t row = tc.m0 + hl * kGroupRows + (ln & 31);
+      as_off = (tid < C::A_SCALE_THREADS && row < a_pad)
+                   ? (uint32_t)(tiled_scale_offset(row, (int64_t)(ln >> 5) * 32, kpad))
+                   : kOob;
+    }
+    // weights: wave-owned 32-row groups, aligned (n0 is a multiple of BN)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int64_t row = tc.n0 + wave * C::WN + j * kGroupRows;
+      const int64_t blk = (row / kGroupRows) * (kpad / kBlockK);
+      w_off[j] = row < n_pad ? (uint32_t)(blk * kCodeBlock + lane * 16) : kOob;
+      ws_off[j] = row < n_pad ? (uint32_t)(blk * kScaleBlock + lane * 4) : kOob;
+    }
+    la_w = tid * 16;
+    la_ws = tid < C::A_SCALE_THREADS ? C::A_CODES + tid * 4 : C::A_CODES + C::A_SCALES + tid * 4;
+    lr = lane * 16;
+    lrs = C::A_CODES + lane * 4;
+    b_cur = 0;
+    b_next = C::STAGE;
+    b_fill = 2 * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) acc.v[i][j] = {};
   }
 
-  template <int P>
-  __device__ __forceinline__ void prologue_loads() {
-    if constexpr (P < C::PD) {
-      if (P < nsteps) load_stage<C>(st[P], o, lo, kt0 + P);
-      prologue_loads<P + 1>();
-    }
+  // k-block of step s (past the range for the loads of the last steps).
+  __device__ __forceinline__ int64_t kt_at(int64_t s) const { return kt0 + s; }
+  // Resource for the loads of step s < U of the prologue: empty for a padding step.
+  __device__ __forceinline__ Rsrc pro(Rsrc r, int s) const { return s < pad ? make_rsrc(nullptr, 0) : r; }
+
+  // Weights of k-block kt into a slot: half h only, or the scale dwords.
+  __device__ __forceinline__ void load_w_half(WStage<C>& st, int64_t kt, int h, Rsrc rc) {
+    const int kb = (int)(kt * kCodeBlock);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) st.c[j][h] = load16(rc, w_off[j] + h * kCodeHalf, kb);
+  }
+  __device__ __forceinline__ void load_w_scales(WStage<C>& st, int64_t kt, Rsrc rs) {
+    const int ks = (int)(kt * kScaleBlock);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) st.s[j] = load4(rs, ws_off[j], ks);
+  }
+  __device__ __forceinline__ void load_w(WStage<C>& st, int64_t kt, Rsrc rc, Rsrc rs) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) load_w_half(st, kt, h, rc);
+    load_w_scales(st, kt, rs);
+  }
+  __device__ __forceinline__ void load_a(AStage<C>& st, int64_t kt, Rsrc rc, Rsrc rs) {
+    const int kb = (int)(kt * kCodeBlock), ks = (int)(kt * kScaleBlock);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) st.c[i] = load16(rc, a_off[i], kb);
+    st.s = load4(rs, as_off, ks);
+  }
+  __device__ __forceinline__ void store_a(const AStage<C>& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) lds_at<v4i>(smem, buf + la_w + i * kCodeBlock) = st.c[i];
+    lds_at<uint32_t>(smem, buf + la_ws) = st.s;
+  }
+  __device__ __forceinline__ void read_frag(AFrag<C>& f, int buf, int h) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) f.c[i] = lds_at<v4i>(smem, buf + lr + i * kCodeBlock + h * kCodeHalf);
+  }
+  __device__ __forceinline__ void read_scales(uint32_t (&s)[C::FM], int buf) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) s[i] = lds_at<uint32_t>(smem, buf + lrs + i * kScaleBlock);
   }
 
-  // Step s = s0 + J with s0 a multiple of U: LDS buffer s % 3 = J % 3,
-  // register slot (s+2) % PD, scale set s % 2, fragment set of half h
-  // (s * NSUB + h) % 2. FULL: steps s+1, s+2 and s+2+PD exist, no checks.
-  //
-  // LDS operations complete in order and the wait counter only tracks 15 of
-  // them, so the order is chosen so that no MFMA waits behind an LDS write:
-  //   phase 1: reads of this step's second half, then the first half's MFMAs
-  //            interleaved with the LDS writes of step s+2;
-  //   phase 2: the second half's MFMAs interleaved with the reads of step
-  //            s+1's first half and scales and with the buffer loads.
-  template <int J, bool FULL>
-  __device__ __forceinline__ void step(int64_t s) {
-    constexpr int SLOT = (J + 2) % C::PD, SC = J % 2;
-    constexpr int B_CUR = J % 3, B_NEXT = (J + 1) % 3, B_FILL = (J + 2) % 3;
-    constexpr int F0 = (J * C::NSUB) % 2;
-    constexpr int FL = (J * C::NSUB + C::NSUB - 1) % 2;  // set of the last half
-    const bool has_fill = FULL || s + 2 < nsteps;
-    if constexpr (C::NSUB == 2) {
-      read_half<C, 1, B_CUR>(hf[F0 ^ 1], smem, lds);
-      if (has_fill) store_stage<C, B_FILL>(st[SLOT], smem, lds);
-      mfma_half<C, 0>(acc, hf[F0], sc[SC]);
-      if constexpr (FULL) {
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::FM + C::FN, 0);
-        interleave<0, C::N_MFMA, 0, C::N_DSW, 0>();
-      }
-      __builtin_amdgcn_sched_barrier(0);
+  template <int H, int WS, int FS>
+  __device__ __forceinline__ void mfma_half() {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        acc.v[i][j] = mfma(w[WS].c[j][H], af[FS].c[i], acc.v[i][j], (int)w[WS].s[j], (int)asc[i], H);
+  }
+
+  // Half H of step s (J = s % U).
+  template <int J, int H>
+  __device__ __forceinline__ void half(int64_t s) {
+    constexpr int WS = J % C::PW, AS = (J + 2) % C::PA;
+    constexpr int FS = H & 1;
+    constexpr int NR = (H < NH - 1) ? C::FM : 2 * C::FM;
+    constexpr int NW = (H == 0) ? C::FM + 1 : 0;
+    constexpr int NV = C::FN + ((H == NH - 1) ? C::FN : 0) + ((H == 1) ? C::FM + 1 : 0);
+    if constexpr (H < NH - 1) {
+      read_frag(af[FS ^ 1], b_cur, H + 1);
     } else {
-      if (has_fill) store_stage<C, B_FILL>(st[SLOT], smem, lds);
+      read_frag(af[FS ^ 1], b_next, 0);
+      read_scales(asc_next, b_next);
     }
-    if (FULL || s + 1 < nsteps) {
-      read_half<C, 0, B_NEXT>(hf[FL ^ 1], smem, lds);
-      read_scales<C, B_NEXT>(sc[SC ^ 1], smem, lds, lane);
-    }
-    if (FULL || s + 2 + C::PD < nsteps) load_stage<C>(st[SLOT], o, lo, kt0 + s + 2 + C::PD);
-    mfma_half<C, C::NSUB - 1>(acc, hf[FL], sc[SC]);
-    if constexpr (FULL) {
-      if constexpr (C::NSUB == 2) interleave<0, C::N_MFMA, C::N_DSR + C::FM + C::FN, 0, C::N_VMEM>();
-      else interleave<0, C::N_MFMA, C::N_DSR + C::FM + C::FN, C::N_DSW, C::N_VMEM>();
-    }
-    // keep this step's MFMAs on this side of the barrier (they touch no memory,
-    // so the scheduler would otherwise sink them and keep every step's
-    // fragments live at once)
+    if constexpr (H == 0) store_a(a[AS], b_fill);
+    if constexpr (H == 1) load_a(a[AS], kt_at(s + 2 + C::PA), ac, as);
+    mfma_half<H, WS, FS>();
+    load_w_half(w[WS], kt_at(s + C::PW), H, bc);
+    if constexpr (H == NH - 1) load_w_scales(w[WS], kt_at(s + C::PW), bs);
+    // the next half's LDS reads go first (they complete under this half's
+    // MFMAs); the LDS writes and buffer loads are spread between the MFMAs
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NR, 0);
+    interleave<0, C::N_MFMA, 0, NW, NV>();
+    // keep this half's MFMAs on this side of the fence (they touch no memory,
+    // so the scheduler would otherwise sink them and keep every half's
+    // operands live at once)
     __builtin_amdgcn_sched_barrier(0);
+  }
+
+  template <int J>
+  __device__ __forceinline__ void step(int64_t s) {
+    half<J, 0>(s);
+    half<J, 1>(s);
+    half<J, 2>(s);
+    half<J, 3>(s);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) asc[i] = asc_next[i];
+    const int t = b_cur;
+    b_cur = b_next;
+    b_next = b_fill;
+    b_fill = t;
   }
 
-  template <int J, bool FULL>
+  template <int J>
   __device__ __forceinline__ void steps(int64_t s0) {
     if constexpr (J < C::U) {
-      if (!FULL && s0 + J >= nsteps) return;
-      step<J, FULL>(s0 + J);
-      steps<J + 1, FULL>(s0);
+      step<J>(s0 + J);
+      steps<J + 1>(s0);
+    }
+  }
+
+  template <int P>
+  __device__ __forceinline__ void prologue_a() {
+    if constexpr (P < C::PA) {
+      load_a(a[(2 + P) % C::PA], kt_at(2 + P), pro(ac, 2 + P), pro(as, 2 + P));
+      prologue_a<P + 1>();
+    }
+  }
+  template <int P>
+  __device__ __forceinline__ void prologue_w() {
+    if constexpr (P < C::PW) {
+      load_w(w[P], kt_at(P), pro(bc, P), pro(bs, P));
+      prologue_w<P + 1>();
     }
   }
 
   __device__ __forceinline__ void run() {
-    if (nsteps <= 0) return;
-    prologue_loads<0>();                                  // steps 0 .. PD-1 in slots 0 .. PD-1
-    store_stage<C, 0>(st[0], smem, lds);
-    if (1 < nsteps) store_stage<C, 1>(st[1], smem, lds);
-    if (C::PD < nsteps) load_stage<C>(st[0], o, lo, kt0 + C::PD);        // slot PD % PD
-    if (C::PD + 1 < nsteps) load_stage<C>(st[1], o, lo, kt0 + C::PD + 1);  // slot (PD+1) % PD
+    if (nsteps - pad <= 0) return;
+    // Issue order: activation steps 0 and 1 (to LDS buffers 0 and 1 through
+    // registers of their own), the activation slots of steps 2 .. PA+1, the
+    // weight slots of steps 0 .. PW-1. The fences keep that order, which is
+    // the order of the steady state, so the first waits of the loop cover
+    // only loads as old as they need.
+    AStage<C> t0, t1;
+    load_a(t0, kt_at(0), pro(ac, 0), pro(as, 0));
+    load_a(t1, kt_at(1), pro(ac, 1), pro(as, 1));
+    __builtin_amdgcn_sched_barrier(0);
+    prologue_a<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    prologue_w<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    store_a(t0, 0);
+    store_a(t1, C::STAGE);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    read_half<C, 0, 0>(hf[0], smem, lds);
-    read_scales<C, 0>(sc[0], smem, lds, lane);
-    int64_t s0 = 0;
-    for (; s0 + C::U + C::PD + 1 <= nsteps; s0 += C::U) steps<0, true>(s0);
-    for (; s0 < nsteps; s0 += C::U) steps<0, false>(s0);
+    read_frag(af[0], 0, 0);
+    read_scales(asc, 0);
+    for (int64_t s0 = 0; s0 < nsteps; s0 += C::U) steps<0>(s0);
   }
 };
 
@@ -514,12 +462,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, const TileCoord& tc,
                                          const uint8_t* bs, uint8_t* smem) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  Operands o{make_rsrc(g.a_codes, tiled_codes_bytes(a_rows, g.K)), make_rsrc(g.a_scales, tiled_scales_bytes(a_rows, g.K)),
-             make_rsrc(bc, tiled_codes_bytes(g.N, g.K)), make_rsrc(bs, tiled_scales_bytes(g.N, g.K)), g.N, g.K};
-  Pipe<C> p(o, tc, a_rows, smem, wm, wn, lane);
+  Pipe<C> p(g, tc, a_rows, bc, bs, smem, wave, lane);
   p.run();
-  store_out<C>(p.acc, g, tc, wm, wn, lane);
+  store_out<C>(p.acc, g, tc, wave, lane);
 }
 
 // Workgroup ids are dispatched round-robin over the 8 XCDs (id i runs on XCD
@@ -532,7 +477,7 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t id, int64_t total) {
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
   const int64_t mt = (g.M + C::BM - 1) / C::BM;
   const int64_t nt = (g.N + C::BN - 1) / C::BN;
@@ -549,7 +494,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   const int64_t in_group = t - group * GROUP_M * nt;
   const int64_t tm = first_m + in_group % gsize;
   const int64_t tn = in_group / gsize;
-  const int64_t KT = pad_k(g.K) / BK;
+  const int64_t KT = pad_k(g.K) / kBlockK;
   TileCoord tc;
   tc.m0 = tm * C::BM;
   tc.m_end = g.M;
@@ -563,7 +508,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
 // Grouped: the tile map (built by build_tile_map_kernel) lists, per m-tile,
 // the expert and the first row; tiles past the used count exit at once.
 template <class C>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_grouped_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_grouped_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
   const int64_t nt = (g.N + C::BN - 1) / C::BN;
   const int64_t id = xcd_remap(blockIdx.x, g.max_mtiles * nt);
@@ -579,7 +524,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   tc.n0 = tn * C::BN;
   tc.split = 0;
   tc.kt_begin = 0;
-  tc.kt_end = pad_k(g.K) / BK;
+  tc.kt_end = pad_k(g.K) / kBlockK;
   run_tile<C>(g, tc, g.M, g.b_codes + (int64_t)expert * tiled_codes_bytes(g.N, g.K),
               g.b_scales + (int64_t)expert * tiled_scales_bytes(g.N, g.K), smem);
 }
@@ -615,15 +560,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   float s = 0.0f;
   for (int k = 0; k < splits; ++k) s += part[(int64_t)k * M * N + i];
   const int64_t m = i / N, n = i - m * N;
-  if (bf16) static_cast<uint16_t*>(y)[m * ldy + n] = f32_to_bf16_rne(s);
+  if (bf16) static_cast<uint16_t*>(y)[m * ldy + n] = (uint16_t)f32_to_bf16_rne(s);
   else static_cast<float*>(y)[m * ldy + n] = s;
 }
 
-using CfgL = TileCfg<256, 256, 2, 2, 32, 2>;   // large prefill
-using CfgM = TileCfg<128, 256, 2, 2, 32, 3>;   // prefill
-using CfgS64 = TileCfg<64, 256, 1, 4, 32, 3>;  // decode, M <= 64
-using CfgS32 = TileCfg<32, 256, 1, 4, 32, 3>;
-using CfgS16 = TileCfg<16, 256, 1, 4, 16, 3>;
+using CfgM = TileCfg<128, 256, 2, 2>;  // prefill
+using CfgS64 = TileCfg<64, 256, 4, 2>; // decode, M <= 64
+using CfgS32 = TileCfg<32, 256, 4, 2>; // decode, M <= 32
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
@@ -631,7 +574,7 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
   const int64_t nt = (g.N + C::BN - 1) / C::BN;
   const int64_t total = mt * nt * g.splits;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_kernel<C>, dim3((unsigned)total), dim3(C::NT), 0, stream, g);
+  hipLaunchKernelGGL(gemm_kernel<C>, dim3((unsigned)total), dim3(NT), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -644,31 +587,32 @@ hipError_t launch_grouped_cfg(const GemmArgs& g, hipStream_t stream) {
   const int64_t nt = (g.N + C::BN - 1) / C::BN;
   const int64_t total = g.max_mtiles * nt;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_grouped_kernel<C>, dim3((unsigned)total), dim3(C::NT), 0, stream, g);
+  hipLaunchKernelGGL(gemm_grouped_kernel<C>, dim3((unsigned)total), dim3(NT), 0, stream, g);
   return hipGetLastError();
+}
+
+// Vector stores of 4 outputs need 4-element alignment of every row start.
+void set_vec_flags(GemmArgs& g) {
+  const size_t es = g.y_bf16 ? 2 : 4;
+  g.vec_y = (reinterpret_cast<uintptr_t>(g.y) % (4 * es)) == 0 && g.ldy % 4 == 0;
+  g.vec_partial = g.N % 4 == 0;  // the partial buffer is 256-byte aligned
 }
 
 }  // namespace
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   GemmPlan p{};
-  if (M <= 16) { p.cfg = 4; p.bm = 16; }
-  else if (M <= 32) { p.cfg = 3; p.bm = 32; }
+  if (M <= 32) { p.cfg = 3; p.bm = 32; }
   else if (M <= 64) { p.cfg = 2; p.bm = 64; }
   else { p.cfg = 1; p.bm = 128; }
   p.bn = 256;
   const int64_t nt = (N + p.bn - 1) / p.bn;
-  // the large tile only when it still gives every CU a tile
-  if (false && M > 1024 && ((M + 255) / 256) * nt >= kNumCu) {
-    p.cfg = 0;
-    p.bm = 256;
-  }
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * nt;
-  const int64_t KT = pad_k(K) / BK;
+  const int64_t KT = pad_k(K) / kBlockK;
   int splits = 1;
   // split K only for skinny (decode) shapes whose tiles leave most CUs idle
   if (M <= 64)
-    while (tiles * splits * 2 <= 2 * kNumCu && KT / (splits * 2) >= 8 && splits < 16) splits *= 2;
+    while (tiles * splits * 2 <= 2 * kNumCu && KT / (splits * 2) >= 4 && splits < 16) splits *= 2;
   p.splits = splits;
   p.partial_bytes = splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
   return p;
@@ -688,15 +632,15 @@ GemmPlan plan_gemm_grouped(int64_t T, int E, int64_t N, int64_t K) {
   return p;
 }
 
-hipError_t launch_gemm(const GemmArgs& g, const GemmPlan& p, hipStream_t stream) {
-  if (g.M == 0) return hipSuccess;
+hipError_t launch_gemm(const GemmArgs& g_in, const GemmPlan& p, hipStream_t stream) {
+  if (g_in.M == 0) return hipSuccess;
+  GemmArgs g = g_in;
+  set_vec_flags(g);
   hipError_t e;
   switch (p.cfg) {
-    case 0: e = launch_cfg<CfgL>(g, stream); break;
     case 1: e = launch_cfg<CfgM>(g, stream); break;
     case 2: e = launch_cfg<CfgS64>(g, stream); break;
-    case 3: e = launch_cfg<CfgS32>(g, stream); break;
-    default: e = launch_cfg<CfgS16>(g, stream); break;
+    default: e = launch_cfg<CfgS32>(g, stream); break;
   }
   if (e != hipSuccess || g.splits <= 1) return e;
   const int64_t n = g.M * g.N;
@@ -705,8 +649,10 @@ hipError_t launch_gemm(const GemmArgs& g, const GemmPlan& p, hipStream_t stream)
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_grouped(const GemmArgs& g, const GemmPlan& p, hipStream_t stream) {
+hipError_t launch_gemm_grouped(const GemmArgs& g_in, const GemmPlan& p, hipStream_t stream) {
   (void)p;
+  GemmArgs g = g_in;
+  set_vec_flags(g);
   return launch_grouped_cfg<CfgM>(g, stream);
 }
 

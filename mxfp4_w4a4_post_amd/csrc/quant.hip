@@ -7,7 +7,7 @@
 // the weight-side multiplier produces the absorbed weights offline.
 //
 // Layout of the work: a workgroup of 256 lanes covers 16 rows x 128
-// elements (one block of the GEMM layout); each lane owns 8 consecutive
+// elements; each lane owns 8 consecutive
 // elements of a row (one 16-byte bf16 load), 16 lanes a row. An MX group of 32
 // is 4 adjacent lanes and a Hadamard block of b elements is b/8 adjacent
 // lanes. Butterflies of span 1, 2, 4 stay inside the lane; spans 8 .. b/2 pair
@@ -21,6 +21,8 @@ namespace macaq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kTileRows = 16;   // rows per workgroup
+constexpr int kTileK = 128;     // elements per workgroup along K
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -120,15 +122,9 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
 
   if constexpr (TILED) {
     // every lane of the padded grid writes (zeros outside M x K)
-    const int64_t kt = k / kTileK, ktp = q.kpad / kTileK;
-    const int64_t cofs = ((row / kTileRows) * ktp + kt) * kCodeBlock + (row % kTileRows) * (kTileK / 2) +
-                         (k % kTileK) / 2;
-    *reinterpret_cast<uint32_t*>(q.codes + cofs) = packed;
-    if ((k & 31) == 0) {
-      const int64_t g = k / 32;
-      const int64_t sofs = ((row / kScaleRows) * ktp + g / 4) * kScaleBlock + (row % kScaleRows) * 4 + (g % 4);
-      q.scales[sofs] = (uint8_t)sc;
-    }
+    // a lane's 8 elements are 4 code bytes inside one 16-byte chunk
+    *reinterpret_cast<uint32_t*>(q.codes + tiled_code_offset(row, k, q.kpad)) = packed;
+    if ((k & 31) == 0) q.scales[tiled_scale_offset(row, k, q.kpad)] = (uint8_t)sc;
   } else if (valid) {
     *reinterpret_cast<uint32_t*>(q.codes + row * (q.K >> 1) + (k >> 1)) = packed;
     if ((k & 31) == 0) q.scales[row * (q.K >> 5) + (k >> 5)] = (uint8_t)sc;

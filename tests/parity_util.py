@@ -74,24 +74,26 @@ def assert_bf16_close(y_bf16: torch.Tensor, y_ref: np.ndarray, what=""):
 
 # ---------------------------------------------------------------------------
 # The GEMM layout of packed operands, restated from include/macaq.h: rows
-# padded to a multiple of 64, K to a multiple of 128, padding all zero;
-# code byte (r, k) at ((r/16)*KB + k/128)*1024 + (r%16)*64 + (k%128)/2 and
-# scale (r, g) at ((r/64)*KB + g/4)*256 + (r%64)*4 + g%4, KB = KP/128.
+# padded to a multiple of 32, K to a multiple of 256, padding all zero; blocks
+# of 32 rows x 256 elements ordered (row group, k block); inside a block, chunk
+# c = 2h + j (32 elements) of row r has its 16 code bytes at
+# h*1024 + (32j + r)*16 and its scale at (32j + r)*4 + h.
 # ---------------------------------------------------------------------------
 
 def padded(rows: int, K: int):
-    return -(-rows // 64) * 64, -(-K // 128) * 128
+    return -(-rows // 32) * 32, -(-K // 256) * 256
 
 
 def gemm_layout_to_row_major(codes, scales, rows: int, K: int, check_padding: bool = True):
     """Row-major (codes [rows, K/2], scales [rows, K/32]) of a GEMM-layout operand."""
     RP, KP = padded(rows, K)
-    KB = KP // 128
+    KB = KP // 256
     c = np.asarray(codes).reshape(-1)
     s = np.asarray(scales).reshape(-1)
     assert c.size == RP * KP // 2 and s.size == RP * KP // 32, (c.size, s.size, RP, KP)
-    cf = c.reshape(RP // 16, KB, 16, 64).transpose(0, 2, 1, 3).reshape(RP, KP // 2)
-    sf = s.reshape(RP // 64, KB, 64, 4).transpose(0, 2, 1, 3).reshape(RP, KP // 32)
+    # codes: (g, kb, h, j, r, b) -> (g, r, kb, h, j, b); scales: (g, kb, j, r, h) -> (g, r, kb, h, j)
+    cf = c.reshape(RP // 32, KB, 4, 2, 32, 16).transpose(0, 4, 1, 2, 3, 5).reshape(RP, KP // 2)
+    sf = s.reshape(RP // 32, KB, 2, 32, 4).transpose(0, 3, 1, 4, 2).reshape(RP, KP // 32)
     if check_padding:
         assert not cf[rows:].any() and not cf[:, K // 2:].any(), "code padding is not zero"
         assert not sf[rows:].any() and not sf[:, K // 32:].any(), "scale padding is not zero"
@@ -104,13 +106,13 @@ def row_major_to_gemm_layout(codes, scales):
     scales = np.asarray(scales, np.uint8)
     rows, K = codes.shape[0], codes.shape[1] * 2
     RP, KP = padded(rows, K)
-    KB = KP // 128
+    KB = KP // 256
     cf = np.zeros((RP, KP // 2), np.uint8)
     sf = np.zeros((RP, KP // 32), np.uint8)
     cf[:rows, :K // 2] = codes
     sf[:rows, :K // 32] = scales
-    c = cf.reshape(RP // 16, 16, KB, 64).transpose(0, 2, 1, 3).reshape(-1)
-    s = sf.reshape(RP // 64, 64, KB, 4).transpose(0, 2, 1, 3).reshape(-1)
+    c = cf.reshape(RP // 32, 32, KB, 4, 2, 16).transpose(0, 2, 3, 4, 1, 5).reshape(-1)
+    s = sf.reshape(RP // 32, 32, KB, 4, 2).transpose(0, 2, 4, 1, 3).reshape(-1)
     return np.ascontiguousarray(c), np.ascontiguousarray(s)
 
 

@@ -119,7 +119,7 @@ def test_calibrate_and_multipliers_reject(lib):
 def test_packed_sizes(lib):
     """GEMM layout: rows padded to 64, K to 128; codes K/2 and scales K/32 bytes a row."""
     for rows, K in [(1, 32), (16, 256), (65, 96), (2048, 4096), (8192, 28672)]:
-        RP, KP = -(-rows // 64) * 64, -(-K // 128) * 128
+        RP, KP = -(-rows // 32) * 32, -(-K // 256) * 256
         assert lib.macaq_packed_codes_bytes(rows, K) == RP * KP // 2
         assert lib.macaq_packed_scales_bytes(rows, K) == RP * KP // 32
     assert lib.macaq_packed_codes_bytes(0, 64) == 0
