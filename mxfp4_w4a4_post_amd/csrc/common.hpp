@@ -89,7 +89,7 @@ struct GemmArgs {
   int E;
   int64_t max_mtiles;
   // set by the launcher: outputs may be stored as 4-element vectors
-  bool vec_y, vec_partial;
+  bool vec_y, vec_partial, vec16_y;
 };
 
 struct GemmPlan {

@@ -29,6 +29,8 @@ namespace macaq {
 namespace {
 
 constexpr int NH = kBlockK / 64;  // MFMAs along K per step (4)
+constexpr int kEpiPitch = 64 * 2 + 16;  // epilogue staging: one row of 64 bf16, padded (16-byte aligned)
+constexpr int kEpiRegion = 32 * kEpiPitch;  // one wave's 32 staged rows
 constexpr int NT = 256;           // 4 waves
 constexpr int kNumCu = 256;
 
@@ -56,7 +58,8 @@ struct TileCfg {
   static constexpr int LDS_TRASH = NT * 4;
   static constexpr int STAGE = A_CODES + A_SCALES + LDS_TRASH;
   static constexpr int NBUF = 3;  // LDS buffers: compute s, read s+1, write s+2
-  static constexpr int LDS_BYTES = NBUF * STAGE;
+  // the epilogue reuses the LDS: one staging region per wave
+  static constexpr int LDS_BYTES = (NBUF * STAGE > 4 * kEpiRegion) ? NBUF * STAGE : 4 * kEpiRegion;
   // main-loop unroll: register slots static
   static constexpr int U = lcm2(PW, PA);
   static constexpr int N_MFMA = FM * FN;  // per half step
@@ -208,16 +211,65 @@ __device__ __forceinline__ void store_sel(const Acc<C>& acc, void* p, int64_t ld
   }
 }
 
+// bf16 output staged through a wave-private LDS region (kEpiRows rows of
+// kEpiPitch bytes): per 32-row fragment the wave writes its 32 x 64 tile in
+// the MFMA layout and reads it back by rows, so each store instruction writes
+// 8 whole 128-byte row segments instead of 16-byte pieces of 32 rows.
+
 template <class C>
+__device__ __forceinline__ void store_bf16_staged(const Acc<C>& acc, uint16_t* y, int64_t ld, int64_t m_lim,
+                                                  int64_t n_lim, uint8_t* region, int lane) {
+  static_assert(C::WN == 64, "one 128-byte row segment per wave");
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+    for (int jn = 0; jn < C::FN; ++jn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v16f& a = acc.v[i][jn];
+        const int n = jn * 32 + 8 * q + 4 * (lane >> 5);
+        uint2 w;
+        w.x = f32_to_bf16_rne(a[4 * q]) | (f32_to_bf16_rne(a[4 * q + 1]) << 16);
+        w.y = f32_to_bf16_rne(a[4 * q + 2]) | (f32_to_bf16_rne(a[4 * q + 3]) << 16);
+        lds_at<uint2>(region, (lane & 31) * kEpiPitch + n * 2) = w;
+      }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = p * 8 + (lane >> 3), c = (lane & 7) * 8;
+      const uint4 v = lds_at<uint4>(region, r * kEpiPitch + c * 2);
+      const int m = i * 32 + r;
+      if (m < m_lim) {
+        uint16_t* dst = y + m * ld + c;
+        if (c + 8 <= n_lim) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+          const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (c + e < n_lim) dst[e] = (uint16_t)(u[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  }
+}
+
+// Output modes, chosen on the host per launch: fp32 to Y, bf16 to Y (plain
+// stores), bf16 to Y staged through LDS (aligned rows), fp32 split-K partials.
+enum OutMode { kOutF32 = 0, kOutBf16 = 1, kOutBf16Staged = 2, kOutPartial = 3 };
+
+template <class C, int MODE>
 __device__ __forceinline__ void store_out(const Acc<C>& acc, const GemmArgs& g, const TileCoord& tc, int wave,
-                                          int lane) {
+                                          int lane, uint8_t* smem) {
   const int64_t m0 = tc.m0, n0 = tc.n0 + wave * C::WN;
   const int64_t m_lim = tc.m_end - m0, n_lim = g.N - n0;
   if (n_lim <= 0) return;
-  if (g.splits > 1) {
+  if constexpr (MODE == kOutPartial) {
     float* p = g.partial + (int64_t)tc.split * g.M * g.N + m0 * g.N + n0;
     store_sel<C, 2>(acc, p, g.N, m_lim, n_lim, g.vec_partial, lane);
-  } else if (g.y_bf16) {
+  } else if constexpr (MODE == kOutBf16Staged) {
+    store_bf16_staged<C>(acc, static_cast<uint16_t*>(g.y) + m0 * g.ldy + n0, g.ldy, m_lim, n_lim,
+                         smem + wave * kEpiRegion, lane);
+  } else if constexpr (MODE == kOutBf16) {
     store_sel<C, 1>(acc, static_cast<uint16_t*>(g.y) + m0 * g.ldy + n0, g.ldy, m_lim, n_lim, g.vec_y, lane);
   } else {
     store_sel<C, 0>(acc, static_cast<float*>(g.y) + m0 * g.ldy + n0, g.ldy, m_lim, n_lim, g.vec_y, lane);
@@ -240,9 +292,9 @@ __device__ __forceinline__ void store_out(const Acc<C>& acc, const GemmArgs& g, 
 // Buffer (s+2) % 3 held step s-1, whose reads all completed before the MFMAs
 // of step s-1 were issued, that is before its closing barrier; buffer
 // (s+1) % 3 was written during step s-1 and is visible after that barrier.
-// Every load and LDS store is unconditional: those of the last steps reach
-// past the range and read the blocks that follow in memory, or zeros past the
-// end of the operand, and nothing uses what they bring. The loop is unrolled
+// Every load and LDS store is unconditional: the loads of steps past the range
+// go through an empty buffer resource, so they return zeros without touching
+// memory, and nothing uses what they bring. The loop is unrolled
 // U = lcm(PW, PA) times so the register slots are static, and the step count
 // is rounded up to a multiple of U by leading steps whose loads all return
 // zero (a resource of zero bytes), so their MFMAs add nothing. The loop thus
@@ -265,9 +317,20 @@ struct Pipe {
   int pad;                        // leading zero steps
   uint8_t* smem;
 
-  __device__ __forceinline__ Pipe(const GemmArgs& g, const TileCoord& tc, int64_t a_rows, const uint8_t* bcodes,
-                                  const uint8_t* bscales, uint8_t* smem_, int wave, int lane)
-      : smem(smem_) {
+  AStage<C> t0, t1;  // activation steps 0 and 1 on their way to LDS buffers 0 and 1
+  int wave, lane;
+
+  __device__ __forceinline__ Pipe(uint8_t* smem_, int wave_, int lane_) : smem(smem_), wave(wave_), lane(lane_) {
+    const int tid = threadIdx.x;
+    la_w = tid * 16;
+    la_ws = tid < C::A_SCALE_THREADS ? C::A_CODES + tid * 4 : C::A_CODES + C::A_SCALES + tid * 4;
+    lr = lane * 16;
+    lrs = C::A_CODES + lane * 4;
+  }
+
+  // Offsets, resources and step count of one output tile.
+  __device__ __forceinline__ void set_tile(const GemmArgs& g, const TileCoord& tc, int64_t a_rows,
+                                           const uint8_t* bcodes, const uint8_t* bscales) {
     const int tid = threadIdx.x;
     const int64_t n = tc.kt_end - tc.kt_begin;
     pad = (int)((C::U - n % C::U) % C::U);
@@ -301,23 +364,15 @@ struct Pipe {
       w_off[j] = row < n_pad ? (uint32_t)(blk * kCodeBlock + lane * 16) : kOob;
       ws_off[j] = row < n_pad ? (uint32_t)(blk * kScaleBlock + lane * 4) : kOob;
     }
-    la_w = tid * 16;
-    la_ws = tid < C::A_SCALE_THREADS ? C::A_CODES + tid * 4 : C::A_CODES + C::A_SCALES + tid * 4;
-    lr = lane * 16;
-    lrs = C::A_CODES + lane * 4;
-    b_cur = 0;
-    b_next = C::STAGE;
-    b_fill = 2 * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) acc.v[i][j] = {};
   }
 
   // k-block of step s (past the range for the loads of the last steps).
   __device__ __forceinline__ int64_t kt_at(int64_t s) const { return kt0 + s; }
-  // Resource for the loads of step s < U of the prologue: empty for a padding step.
+  // Resource for the loads of step s: empty (loads return zero and touch no
+  // memory) for a leading padding step or a step past the range. A scalar
+  // select, so the loop keeps its single basic block.
   __device__ __forceinline__ Rsrc pro(Rsrc r, int s) const { return s < pad ? make_rsrc(nullptr, 0) : r; }
+  __device__ __forceinline__ Rsrc live(Rsrc r, int64_t s) const { return s < nsteps ? r : make_rsrc(nullptr, 0); }
 
   // Weights of k-block kt into a slot: half h only, or the scale dwords.
   __device__ __forceinline__ void load_w_half(WStage<C>& st, int64_t kt, int h, Rsrc rc) {
@@ -379,10 +434,10 @@ struct Pipe {
       read_scales(asc_next, b_next);
     }
     if constexpr (H == 0) store_a(a[AS], b_fill);
-    if constexpr (H == 1) load_a(a[AS], kt_at(s + 2 + C::PA), ac, as);
+    if constexpr (H == 1) load_a(a[AS], kt_at(s + 2 + C::PA), live(ac, s + 2 + C::PA), live(as, s + 2 + C::PA));
     mfma_half<H, WS, FS>();
-    load_w_half(w[WS], kt_at(s + C::PW), H, bc);
-    if constexpr (H == NH - 1) load_w_scales(w[WS], kt_at(s + C::PW), bs);
+    load_w_half(w[WS], kt_at(s + C::PW), H, live(bc, s + C::PW));
+    if constexpr (H == NH - 1) load_w_scales(w[WS], kt_at(s + C::PW), live(bs, s + C::PW));
     // the next half's LDS reads go first (they complete under this half's
     // MFMAs); the LDS writes and buffer loads are spread between the MFMAs
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NR, 0);
@@ -432,14 +487,12 @@ struct Pipe {
     }
   }
 
-  __device__ __forceinline__ void run() {
-    if (nsteps - pad <= 0) return;
-    // Issue order: activation steps 0 and 1 (to LDS buffers 0 and 1 through
-    // registers of their own), the activation slots of steps 2 .. PA+1, the
-    // weight slots of steps 0 .. PW-1. The fences keep that order, which is
-    // the order of the steady state, so the first waits of the loop cover
-    // only loads as old as they need.
-    AStage<C> t0, t1;
+  // Issue order: activation steps 0 and 1 (to LDS buffers 0 and 1 through
+  // registers of their own), the activation slots of steps 2 .. PA+1, the
+  // weight slots of steps 0 .. PW-1. The fences keep that order, which is
+  // the order of the steady state, so the first waits of the loop cover
+  // only loads as old as they need.
+  __device__ __forceinline__ void prologue_loads() {
     load_a(t0, kt_at(0), pro(ac, 0), pro(as, 0));
     load_a(t1, kt_at(1), pro(ac, 1), pro(as, 1));
     __builtin_amdgcn_sched_barrier(0);
@@ -447,86 +500,136 @@ struct Pipe {
     __builtin_amdgcn_sched_barrier(0);
     prologue_w<0>();
     __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // After prologue_loads, with the LDS idle in every wave.
+  __device__ __forceinline__ void prologue_lds() {
     store_a(t0, 0);
     store_a(t1, C::STAGE);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    b_cur = 0;
+    b_next = C::STAGE;
+    b_fill = 2 * C::STAGE;
     read_frag(af[0], 0, 0);
     read_scales(asc, 0);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) acc.v[i][j] = {};
+  }
+
+  // The K loop; its last barrier leaves every LDS buffer idle.
+  __device__ __forceinline__ void loop() {
     for (int64_t s0 = 0; s0 < nsteps; s0 += C::U) steps<0>(s0);
   }
 };
 
-template <class C>
-__device__ __forceinline__ void run_tile(const GemmArgs& g, const TileCoord& tc, int64_t a_rows, const uint8_t* bc,
-                                         const uint8_t* bs, uint8_t* smem) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  Pipe<C> p(g, tc, a_rows, bc, bs, smem, wave, lane);
-  p.run();
-  store_out<C>(p.acc, g, tc, wave, lane);
+// Tile t of the launch: coordinates and this expert's weights (grouped), or
+// false for an unused tile of the grouped launch.
+struct TileRef {
+  TileCoord tc;
+  const uint8_t* bc;
+  const uint8_t* bs;
+};
+
+template <class C, bool GROUPED>
+__device__ __forceinline__ bool tile_at(const GemmArgs& g, int64_t t, TileRef& r) {
+  const int64_t nt = (g.N + C::BN - 1) / C::BN;
+  const int64_t KT = pad_k(g.K) / kBlockK;
+  if constexpr (GROUPED) {
+    const int64_t tm = t / nt, tn = t - tm * nt;
+    const int32_t expert = g.tile_map[2 * tm];
+    if (expert < 0) return false;
+    const int64_t row0 = g.tile_map[2 * tm + 1];
+    const int64_t e_end = g.offsets[expert + 1];
+    r.tc.m0 = row0;
+    r.tc.m_end = (row0 + C::BM < e_end) ? row0 + C::BM : e_end;
+    r.tc.n0 = tn * C::BN;
+    r.tc.split = 0;
+    r.tc.kt_begin = 0;
+    r.tc.kt_end = KT;
+    r.bc = g.b_codes + (int64_t)expert * tiled_codes_bytes(g.N, g.K);
+    r.bs = g.b_scales + (int64_t)expert * tiled_scales_bytes(g.N, g.K);
+  } else {
+    const int64_t mt = (g.M + C::BM - 1) / C::BM;
+    const int64_t tiles = mt * nt;
+    const int split = (int)(t / tiles);
+    const int64_t u = t - (int64_t)split * tiles;
+    // walk tiles in groups of GROUP_M m-tiles, n fastest within a group column
+    constexpr int64_t GROUP_M = 8;
+    const int64_t group = u / (GROUP_M * nt);
+    const int64_t first_m = group * GROUP_M;
+    const int64_t gsize = (mt - first_m) < GROUP_M ? (mt - first_m) : GROUP_M;
+    const int64_t in_group = u - group * GROUP_M * nt;
+    const int64_t tm = first_m + in_group % gsize;
+    const int64_t tn = in_group / gsize;
+    r.tc.m0 = tm * C::BM;
+    r.tc.m_end = g.M;
+    r.tc.n0 = tn * C::BN;
+    r.tc.split = split;
+    r.tc.kt_begin = KT * split / g.splits;
+    r.tc.kt_end = KT * (split + 1) / g.splits;
+    r.bc = g.b_codes;
+    r.bs = g.b_scales;
+  }
+  return true;
 }
 
 // Workgroup ids are dispatched round-robin over the 8 XCDs (id i runs on XCD
 // i % 8). Renumber so that each XCD works through a contiguous run of tiles,
-// which the grouped order below makes share A and B panels in that XCD's L2.
+// which the grouped order above makes share A and B panels in that XCD's L2.
 __device__ __forceinline__ int64_t xcd_remap(int64_t id, int64_t total) {
   if (total % kNumXcd != 0) return id;
   const int64_t per = total / kNumXcd;
   return (id % kNumXcd) * per + id / kNumXcd;
 }
 
-template <class C>
+// Persistent workgroups: workgroup b takes tiles b, b + G, b + 2G, ... (G
+// workgroups). The next tile's loads are issued before the current tile's
+// epilogue, so its memory latency hides behind the output stores.
+template <class C, bool GROUPED, int MODE>
+__device__ __forceinline__ void gemm_tiles(const GemmArgs& g, int64_t total, uint8_t* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  Pipe<C> p(smem, wave, lane);
+  int64_t t = blockIdx.x;
+  TileRef cur;
+  while (t < total && !tile_at<C, GROUPED>(g, xcd_remap(t, total), cur)) t += gridDim.x;
+  if (t >= total) return;
+  p.set_tile(g, cur.tc, g.M, cur.bc, cur.bs);
+  p.prologue_loads();
+  for (;;) {
+    p.prologue_lds();
+    p.loop();
+    TileRef nxt;
+    int64_t tn = t + gridDim.x;
+    while (tn < total && !tile_at<C, GROUPED>(g, xcd_remap(tn, total), nxt)) tn += gridDim.x;
+    if (tn < total) {
+      p.set_tile(g, nxt.tc, g.M, nxt.bc, nxt.bs);
+      p.prologue_loads();
+    }
+    store_out<C, MODE>(p.acc, g, cur.tc, wave, lane, smem);
+    if (tn >= total) break;
+    __syncthreads();  // every wave is done with its epilogue staging in LDS
+    cur = nxt;
+    t = tn;
+  }
+}
+
+template <class C, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
-  const int64_t mt = (g.M + C::BM - 1) / C::BM;
-  const int64_t nt = (g.N + C::BN - 1) / C::BN;
-  const int64_t tiles = mt * nt;
-  const int64_t total = tiles * g.splits;
-  const int64_t id = xcd_remap(blockIdx.x, total);
-  const int split = (int)(id / tiles);
-  const int64_t t = id - (int64_t)split * tiles;
-  // walk tiles in groups of GROUP_M m-tiles, n fastest within a group column
-  constexpr int64_t GROUP_M = 8;
-  const int64_t group = t / (GROUP_M * nt);
-  const int64_t first_m = group * GROUP_M;
-  const int64_t gsize = (mt - first_m) < GROUP_M ? (mt - first_m) : GROUP_M;
-  const int64_t in_group = t - group * GROUP_M * nt;
-  const int64_t tm = first_m + in_group % gsize;
-  const int64_t tn = in_group / gsize;
-  const int64_t KT = pad_k(g.K) / kBlockK;
-  TileCoord tc;
-  tc.m0 = tm * C::BM;
-  tc.m_end = g.M;
-  tc.n0 = tn * C::BN;
-  tc.split = split;
-  tc.kt_begin = KT * split / g.splits;
-  tc.kt_end = KT * (split + 1) / g.splits;
-  run_tile<C>(g, tc, g.M, g.b_codes, g.b_scales, smem);
+  const int64_t tiles = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
+  gemm_tiles<C, false, MODE>(g, tiles * g.splits, smem);
 }
 
 // Grouped: the tile map (built by build_tile_map_kernel) lists, per m-tile,
-// the expert and the first row; tiles past the used count exit at once.
-template <class C>
+// the expert and the first row; unused entries are skipped.
+template <class C, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_grouped_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
-  const int64_t nt = (g.N + C::BN - 1) / C::BN;
-  const int64_t id = xcd_remap(blockIdx.x, g.max_mtiles * nt);
-  const int64_t tm = id / nt;
-  const int64_t tn = id - tm * nt;
-  const int32_t expert = g.tile_map[2 * tm];
-  if (expert < 0) return;
-  const int64_t row0 = g.tile_map[2 * tm + 1];
-  const int64_t e_end = g.offsets[expert + 1];
-  TileCoord tc;
-  tc.m0 = row0;
-  tc.m_end = (row0 + C::BM < e_end) ? row0 + C::BM : e_end;
-  tc.n0 = tn * C::BN;
-  tc.split = 0;
-  tc.kt_begin = 0;
-  tc.kt_end = pad_k(g.K) / kBlockK;
-  run_tile<C>(g, tc, g.M, g.b_codes + (int64_t)expert * tiled_codes_bytes(g.N, g.K),
-              g.b_scales + (int64_t)expert * tiled_scales_bytes(g.N, g.K), smem);
+  gemm_tiles<C, true, MODE>(g, g.max_mtiles * ((g.N + C::BN - 1) / C::BN), smem);
 }
 
 // One thread walks the experts: m-tile j of expert e gets entry (tiles of
@@ -574,7 +677,12 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
   const int64_t nt = (g.N + C::BN - 1) / C::BN;
   const int64_t total = mt * nt * g.splits;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_kernel<C>, dim3((unsigned)total), dim3(NT), 0, stream, g);
+  const int64_t grid = total < kNumCu ? total : kNumCu;  // one resident workgroup per CU
+  const dim3 gd((unsigned)grid), bd(NT);
+  if (g.splits > 1) hipLaunchKernelGGL((gemm_kernel<C, kOutPartial>), gd, bd, 0, stream, g);
+  else if (g.y_bf16 && g.vec16_y) hipLaunchKernelGGL((gemm_kernel<C, kOutBf16Staged>), gd, bd, 0, stream, g);
+  else if (g.y_bf16) hipLaunchKernelGGL((gemm_kernel<C, kOutBf16>), gd, bd, 0, stream, g);
+  else hipLaunchKernelGGL((gemm_kernel<C, kOutF32>), gd, bd, 0, stream, g);
   return hipGetLastError();
 }
 
@@ -587,7 +695,11 @@ hipError_t launch_grouped_cfg(const GemmArgs& g, hipStream_t stream) {
   const int64_t nt = (g.N + C::BN - 1) / C::BN;
   const int64_t total = g.max_mtiles * nt;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_grouped_kernel<C>, dim3((unsigned)total), dim3(NT), 0, stream, g);
+  const int64_t grid = total < kNumCu ? total : kNumCu;
+  const dim3 gd((unsigned)grid), bd(NT);
+  if (g.y_bf16 && g.vec16_y) hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutBf16Staged>), gd, bd, 0, stream, g);
+  else if (g.y_bf16) hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutBf16>), gd, bd, 0, stream, g);
+  else hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutF32>), gd, bd, 0, stream, g);
   return hipGetLastError();
 }
 
@@ -596,9 +708,15 @@ void set_vec_flags(GemmArgs& g) {
   const size_t es = g.y_bf16 ? 2 : 4;
   g.vec_y = (reinterpret_cast<uintptr_t>(g.y) % (4 * es)) == 0 && g.ldy % 4 == 0;
   g.vec_partial = g.N % 4 == 0;  // the partial buffer is 256-byte aligned
+  g.vec16_y = g.y_bf16 && (reinterpret_cast<uintptr_t>(g.y) % 16) == 0 && g.ldy % 8 == 0;
 }
 
 }  // namespace
+
+#ifndef MACAQ_DECODE_UNITS
+#define MACAQ_DECODE_UNITS 256
+#endif
+constexpr int64_t kDecodeUnits = MACAQ_DECODE_UNITS;
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   GemmPlan p{};
@@ -609,11 +727,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   const int64_t nt = (N + p.bn - 1) / p.bn;
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * nt;
   const int64_t KT = pad_k(K) / kBlockK;
-  int splits = 1;
-  // split K only for skinny (decode) shapes whose tiles leave most CUs idle
-  if (M <= 64)
-    while (tiles * splits * 2 <= 2 * kNumCu && KT / (splits * 2) >= 4 && splits < 16) splits *= 2;
-  p.splits = splits;
+  int64_t splits = 1;
+  // Skinny (decode) shapes stream the weights: split K so that about
+  // kDecodeUnits work units of at least 4 k-blocks keep every CU streaming
+  // (the persistent workgroups take about two units each).
+  if (M <= 64 && tiles < kDecodeUnits) {
+    splits = (kDecodeUnits + tiles / 2) / tiles;
+    if (splits > KT / 4) splits = KT / 4;
+    if (splits < 1) splits = 1;
+  }
+  p.splits = (int)splits;
   p.partial_bytes = splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
   return p;
 }
