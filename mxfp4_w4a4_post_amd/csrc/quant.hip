@@ -6,26 +6,25 @@
 // activations at inference and quantizes to MXFP4; the same row transform with
 // the weight-side multiplier produces the absorbed weights offline.
 //
-// Layout of the work: a workgroup of 256 lanes covers 16 rows x 128
-// elements; each lane owns 8 consecutive
-// elements of a row (one 16-byte bf16 load), 16 lanes a row. An MX group of 32
-// is 4 adjacent lanes and a Hadamard block of b elements is b/8 adjacent
-// lanes. Butterflies of span 1, 2, 4 stay inside the lane; spans 8 .. b/2 pair
-// lanes 1 .. b/16 apart through cross-lane shuffles. The E2M1 encode and
-// nibble packing use the hardware scaled FP4 convert, which rounds to
-// nearest-even, saturates at 6 and keeps the sign (it only reads the exponent
-// of its fp32 scale operand).
+// The encode and nibble packing use the hardware scaled FP4 convert, which
+// rounds to nearest-even, saturates at 6 and keeps the sign (it only reads
+// the exponent of its fp32 scale operand).
 #include "common.hpp"
 
 namespace macaq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTileRows = 16;   // rows per workgroup
-constexpr int kTileK = 128;     // elements per workgroup along K
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// The value of lane ^ d (d = 1 or 2, inside a quad of lanes) through a DPP
+// quad permutation: [1,0,3,2] for d = 1, [2,3,0,1] for d = 2.
+__device__ __forceinline__ float xor_lane(float x, int d) {
+  return __int_as_float(d == 1 ? __builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)
+                               : __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
 
 // Largest e in [0, E) with off[e] <= row (the expert that owns `row`).
 __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ off, int E, int64_t row) {
@@ -38,75 +37,109 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ off, in
   return lo;
 }
 
-// TILED: write the GEMM layout (including its zero padding); otherwise
+// One lane per MX group: a workgroup covers one block of the GEMM layout (32
+// rows x 256 elements); lane (r, c) = (tid / 8, tid % 8) owns elements
+// [32c, 32c + 32) of row r of the block. Butterflies of span 1 .. 16 stay in
+// the lane; spans 32 and 64 (Hadamard blocks of 64 and 128) pair the lanes of
+// chunks c ^ 1 and c ^ 2 of the same row. Eight lanes of a row load 512
+// contiguous bytes; eight lanes of a chunk store 128 contiguous bytes of the
+// GEMM layout (rows r .. r+7 of one chunk), or a row's 128 code bytes in the
+// row-major layout.
+// TILED: write the GEMM layout, including its zero padding; otherwise
 // row-major [M, K/2] codes and [M, K/32] scales.
 template <bool F32_IN, int B, bool SCALE, bool GROUPED, bool TILED>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int64_t row = (int64_t)blockIdx.x * kTileRows + (tid >> 4);
-  const int64_t k = (int64_t)blockIdx.y * kTileK + (tid & 15) * 8;
-  const bool valid = row < q.M && k < q.K;
+  const int c = tid & 7;
+  const int64_t row = (int64_t)blockIdx.x * kGroupRows + (tid >> 3);
+  const int64_t k0 = (int64_t)blockIdx.y * kBlockK + c * 32;
+  const bool valid = row < q.M && k0 < q.K;
 
-  float v[8];
+  // the block's 256 multipliers are shared by its 32 rows: stage them in LDS
+  // once (MoE rows may belong to different experts, so those read their own)
+  __shared__ __attribute__((aligned(16))) float msh[kBlockK];
+  if constexpr (SCALE && !GROUPED) {
+    const int64_t kk = (int64_t)blockIdx.y * kBlockK + tid;
+    msh[tid] = kk < q.K ? q.mult[kk] : 0.0f;
+    __syncthreads();
+  }
+
+  float v[32];
   if (valid) {
     if constexpr (F32_IN) {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q.x) + row * q.ldx + k);
-      const float4 u0 = p[0], u1 = p[1];
-      v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
-      v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q.x) + row * q.ldx + k0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 u = p[i];
+        v[4 * i] = u.x;
+        v[4 * i + 1] = u.y;
+        v[4 * i + 2] = u.z;
+        v[4 * i + 3] = u.w;
+      }
     } else {
-      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.x) + row * q.ldx + k);
-      v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
-      v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-      v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
-      v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.x) + row * q.ldx + k0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 w = p[i];
+        v[8 * i] = bf16_lo(w.x);
+        v[8 * i + 1] = bf16_hi(w.x);
+        v[8 * i + 2] = bf16_lo(w.y);
+        v[8 * i + 3] = bf16_hi(w.y);
+        v[8 * i + 4] = bf16_lo(w.z);
+        v[8 * i + 5] = bf16_hi(w.z);
+        v[8 * i + 6] = bf16_lo(w.w);
+        v[8 * i + 7] = bf16_hi(w.w);
+      }
     }
     if constexpr (SCALE) {
-      const float* m = q.mult;
-      if constexpr (GROUPED) m += (int64_t)expert_of_row(q.offsets, q.E, row) * q.K;
-      const float4* mp = reinterpret_cast<const float4*>(m + k);
-      const float4 m0 = mp[0], m1 = mp[1];
-      v[0] *= m0.x; v[1] *= m0.y; v[2] *= m0.z; v[3] *= m0.w;
-      v[4] *= m1.x; v[5] *= m1.y; v[6] *= m1.z; v[7] *= m1.w;
+      const float4* mp;
+      if constexpr (GROUPED)
+        mp = reinterpret_cast<const float4*>(q.mult + (int64_t)expert_of_row(q.offsets, q.E, row) * q.K + k0);
+      else
+        mp = reinterpret_cast<const float4*>(msh + c * 32);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 u = mp[i];
+        v[4 * i] *= u.x;
+        v[4 * i + 1] *= u.y;
+        v[4 * i + 2] *= u.z;
+        v[4 * i + 3] *= u.w;
+      }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
   }
 
   if constexpr (B > 0) {
-    // spans 1, 2, 4 inside the lane
+    // spans 1 .. 16 inside the lane
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
+    for (int h = 1; h < 32; h <<= 1) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 32; ++i) {
         if (i & h) continue;
         const float u = v[i], w = v[i + h];
         v[i] = u + w;
         v[i + h] = u - w;
       }
     }
-    // spans 8 .. B/2 across lanes d = span/8 apart: the lower lane keeps
-    // u + w, the upper lane u - w. fma with +-1 rounds once, exactly as the
-    // plain add or subtract would.
+    // spans 32 .. B/2 across the lanes of chunks d apart: the lower chunk
+    // keeps u + w, the upper one u - w. fma with +-1 rounds once, exactly as
+    // the plain add or subtract would.
 #pragma unroll
-    for (int d = 1; d < B / 8; d <<= 1) {
-      const float sgn = (lane & d) ? -1.0f : 1.0f;
+    for (int d = 1; d < B / 32; d <<= 1) {
+      const float sgn = (c & d) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = __shfl_xor(v[i], d);
+      for (int i = 0; i < 32; ++i) {
+        const float p = xor_lane(v[i], d);
         v[i] = __builtin_fmaf(sgn, v[i], p);
       }
     }
   }
 
-  // group maximum of |t| over the 4 lanes of the group
-  float amax = fabsf(v[0]);
+  float amax = 0.0f;
 #pragma unroll
-  for (int i = 1; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
 
   // E8M0: biased exponent of amax minus E2M1's largest exponent (2),
   // clamped at 0 (2^-127); covers amax == 0 and subnormal amax.
@@ -114,20 +147,25 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
   const int sc = ebits > 2 ? ebits - 2 : 0;
   const float scale = sc ? __uint_as_float((uint32_t)sc << 23) : __uint_as_float(0x00400000u);
 
-  uint32_t packed = 0;
-  packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[0], v[1], scale, 0);
-  packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[2], v[3], scale, 1);
-  packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[4], v[5], scale, 2);
-  packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[6], v[7], scale, 3);
+  uint32_t packed[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * d], v[8 * d + 1], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * d + 2], v[8 * d + 3], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * d + 4], v[8 * d + 5], scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * d + 6], v[8 * d + 7], scale, 3);
+    packed[d] = w;
+  }
+  const uint4 out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
 
   if constexpr (TILED) {
     // every lane of the padded grid writes (zeros outside M x K)
-    // a lane's 8 elements are 4 code bytes inside one 16-byte chunk
-    *reinterpret_cast<uint32_t*>(q.codes + tiled_code_offset(row, k, q.kpad)) = packed;
-    if ((k & 31) == 0) q.scales[tiled_scale_offset(row, k, q.kpad)] = (uint8_t)sc;
+    *reinterpret_cast<uint4*>(q.codes + tiled_code_offset(row, k0, q.kpad)) = out;
+    q.scales[tiled_scale_offset(row, k0, q.kpad)] = (uint8_t)sc;
   } else if (valid) {
-    *reinterpret_cast<uint32_t*>(q.codes + row * (q.K >> 1) + (k >> 1)) = packed;
-    if ((k & 31) == 0) q.scales[row * (q.K >> 5) + (k >> 5)] = (uint8_t)sc;
+    *reinterpret_cast<uint4*>(q.codes + row * (q.K >> 1) + (k0 >> 1)) = out;
+    q.scales[row * (q.K >> 5) + (k0 >> 5)] = (uint8_t)sc;
   }
 }
 
@@ -189,8 +227,7 @@ template <bool F32_IN, int B, bool SCALE, bool GROUPED, bool TILED>
 hipError_t launch_one(const QuantArgs& q, hipStream_t stream) {
   // tiled: cover the padded rows and K; row-major: just M x K
   const int64_t rows = TILED ? pad_rows(q.M) : q.M;
-  const int64_t kk = TILED ? q.kpad : q.K;
-  const int64_t gx = (rows + kTileRows - 1) / kTileRows, gy = (kk + kTileK - 1) / kTileK;
+  const int64_t gx = (rows + kGroupRows - 1) / kGroupRows, gy = q.kpad / kBlockK;
   if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL((quant_rows_kernel<F32_IN, B, SCALE, GROUPED, TILED>), dim3((unsigned)gx, (unsigned)gy),
                      dim3(kThreads), 0, stream, q);
