@@ -4,15 +4,20 @@ Default workload (the headline): the prefill 8B-shaped layer set, M = 2048
 tokens through (K, N) = (4096, 4096), (4096, 14336), (14336, 4096), Hadamard
 block 32. One step = macaq_linear on each of the three layers (activation
 scale + block-Hadamard + MXFP4 quantize + scaled-FP4 GEMM), bf16 in and out.
-Weights are prepared beforehand (offline). Inputs are resident in HBM; the
-timed steps rotate through several copies of activations and weights so that
-no step finds its operands in the 256 MB last-level cache.
+Weights are prepared beforehand (offline). Other workloads (--workload):
+decode-32b (M = 1, 8, 32, 64 through 5120x25600 and 25600x5120), moe-128e
+(grouped gate/up and down projections of 4096 tokens routed top-8 over 128
+experts), prefill-large (M = 8192 through 8192x28672 and 28672x8192, Hadamard
+block from --block) and tiny.
 
-Steps are captured into HIP graphs (one per operand copy) and replayed, so
-the timed region has no host launch gaps. Prints one JSON line with the
-metric, the plain-MXFP4 overhead, the GEMM kernel's roofline (HIP events on
-the launch stream around graph replays of that kernel alone, per layer) and
-the CPU oracle's throughput on a bounded sample of the same work.
+Inputs are resident in HBM; the timed steps rotate through several copies of
+activations and weights so that no step finds its operands in the 256 MB
+last-level cache. Steps are captured into HIP graphs (one per operand copy)
+and replayed, so the timed region has no host launch gaps. Prints one JSON
+line with the metric, the overhead of the fused transform over plain MXFP4
+(same kernels with no scale and no Hadamard), the dominant kernel's roofline
+(HIP events on the launch stream around graph replays of that kernel alone)
+and the CPU oracle's throughput on a bounded sample of the same work.
 """
 from __future__ import annotations
 
@@ -32,6 +37,7 @@ PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ROTATE = 4                  # operand copies cycled through by the timed steps
 ORACLE_THREADS_CAP = 16     # the GPU machine's CPU share for one GPU
+WORKLOADS = {"tiny": 1, "prefill-8b": 2, "decode-32b": 3, "moe-128e": 4, "prefill-large": 5}
 
 
 def parse():
@@ -39,13 +45,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="prefill-8b",
-                   choices=["prefill-8b", "decode-32b", "moe-128e", "prefill-large", "tiny"])
+    p.add_argument("--workload", default="prefill-8b", choices=sorted(WORKLOADS))
     p.add_argument("--block", type=int, default=None, help="Hadamard block (default: the workload's first)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--profile-steps", type=int, default=0,
-                   help="if > 0: only run this many steps of the fused path (for rocprofv3) and exit")
+                   help="if > 0: only run this many eager steps of the fused path (for rocprofv3) and exit")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="if > 0: only copy a MIB-MiB device buffer 3 times (the known-size reference for the "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -79,43 +84,100 @@ def source_digest(paths):
     return h.hexdigest()[:16]
 
 
-def build_layers(torch, binding, inputs, cfg, shapes, M, b, dev):
-    """Per (K, N): rotating copies of x and of the prepared weights (fused and plain)."""
-    layers = []
-    for si, (K, N) in enumerate(shapes):
-        case = inputs.linear_case(cfg, si, M=M, b=b)
-        x = case.x.to(dev)
+def packed_clone(binding, p):
+    return binding.Packed(p.codes.clone(), p.scales.clone(), p.rows, p.K)
+
+
+class Entry:
+    """One layer call of a step: the fused and plain calls on operand copy c,
+    and (dense layers) the quantize and GEMM kernels alone."""
+
+    def __init__(self, name, flops, nbytes, gemm_bytes):
+        self.name, self.flops, self.bytes, self.gemm_bytes = name, flops, nbytes, gemm_bytes
+        self.fused = self.plain = None
+        self.quant = self.gemm = self.quant_plain = self.gemm_plain = None
+        self.oracle_case = None  # (inputs case, rows) for the CPU baseline
+
+
+def dense_entries(torch, binding, inputs, wl, b, dev):
+    spec = inputs.CONFIGS[wl]
+    Ms = [spec["M"]] if "M" in spec else list(spec["Ms"])
+    entries = []
+    for si, (K, N) in enumerate(spec["shapes"]):
+        case = inputs.linear_case(wl, si, M=max(Ms), b=b)
         w = case.w.to(dev)
         s = binding.calibrate(case.xcal.to(dev))
         a, r = binding.make_multipliers(s, b)
-        w_fused = binding.prepare_weights(w, r, b)
-        w_plain = binding.prepare_weights(w, None, 0)
+        wf = [binding.prepare_weights(w, r, b)]
+        wp = [binding.prepare_weights(w, None, 0)]
         del w
+        wf += [packed_clone(binding, wf[0]) for _ in range(ROTATE - 1)]
+        wp += [packed_clone(binding, wp[0]) for _ in range(ROTATE - 1)]
+        xs_full = case.x.to(dev)
+        for M in Ms:
+            xs = [xs_full[:M].clone() for _ in range(ROTATE)]
+            wbytes = N * K * 17 / 32
+            e = Entry("M=%d K=%d N=%d" % (M, K, N), 2.0 * M * N * K, 2 * M * K + wbytes + 2 * M * N,
+                      M * K * 17 / 32 + wbytes + 2 * M * N)
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            work = torch.empty(max(binding.linear_workspace_size(M, K, N), 1), dtype=torch.uint8, device=dev)
+            gwork = torch.empty(max(binding.gemm_workspace_size(M, K, N), 1), dtype=torch.uint8, device=dev)
+            qa = binding.Packed(torch.empty(binding.packed_codes_bytes(M, K), dtype=torch.uint8, device=dev),
+                                torch.empty(binding.packed_scales_bytes(M, K), dtype=torch.uint8, device=dev), M, K)
+            qp = binding.Packed(torch.empty_like(qa.codes), torch.empty_like(qa.scales), M, K)
+            binding.quant_act(xs[0], a, b, layout="gemm", codes=qa.codes, scales=qa.scales)
+            binding.quant_act(xs[0], None, 0, layout="gemm", codes=qp.codes, scales=qp.scales)
+            e.fused = lambda c, xs=xs, a=a, wf=wf, y=y, work=work: binding.linear(xs[c], a, b, wf[c], out=y,
+                                                                                   workspace=work)
+            e.plain = lambda c, xs=xs, wp=wp, y=y, work=work: binding.linear(xs[c], None, 0, wp[c], out=y,
+                                                                              workspace=work)
+            e.quant = lambda c, xs=xs, a=a, qa=qa: binding.quant_act(xs[c], a, b, layout="gemm", codes=qa.codes,
+                                                                     scales=qa.scales)
+            e.quant_plain = lambda c, xs=xs, qp=qp: binding.quant_act(xs[c], None, 0, layout="gemm",
+                                                                      codes=qp.codes, scales=qp.scales)
+            e.gemm = lambda c, qa=qa, wf=wf, y=y, gwork=gwork: binding.linear_plain_gemm(qa, wf[c], out=y,
+                                                                                        workspace=gwork)
+            e.gemm_plain = lambda c, qp=qp, wp=wp, y=y, gwork=gwork: binding.linear_plain_gemm(qp, wp[c], out=y,
+                                                                                              workspace=gwork)
+            e.oracle_case = (case, M)
+            entries.append(e)
+        del xs_full
+    return entries, Ms
 
-        def clone(p):
-            return binding.Packed(p.codes.clone(), p.scales.clone(), p.rows, p.K)
 
-        copies = [dict(x=x.clone(), w=clone(w_fused), wp=clone(w_plain)) for _ in range(ROTATE)]
-        del x, w_fused, w_plain
-        ws_bytes = binding.linear_workspace_size(M, K, N)
-        qa = binding.Packed(torch.empty(binding.packed_codes_bytes(M, K), dtype=torch.uint8, device=dev),
-                            torch.empty(binding.packed_scales_bytes(M, K), dtype=torch.uint8, device=dev), M, K)
-        layers.append(dict(K=K, N=N, M=M, a=a, b=b, case=case, copies=copies,
-                           y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
-                           work=torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev),
-                           gwork=torch.empty(max(binding.gemm_workspace_size(M, K, N), 1), dtype=torch.uint8,
-                                             device=dev),
-                           qa=qa))
-    return layers
-
-
-def enqueue_step(binding, layers, copy, plain=False):
-    for L in layers:
-        c = L["copies"][copy]
-        if plain:
-            binding.linear(c["x"], None, 0, c["wp"], out=L["y"], workspace=L["work"])
-        else:
-            binding.linear(c["x"], L["a"], L["b"], c["w"], out=L["y"], workspace=L["work"])
+def moe_entries(torch, binding, inputs, b, dev):
+    entries = []
+    for proj in ("gate_up", "down"):
+        case = inputs.moe_case(proj)
+        E, K, N, T = case.E, case.K, case.N, case.T
+        offsets = torch.from_numpy(case.offsets.astype("int32")).to(dev)
+        a = torch.empty(E, K, dtype=torch.float32, device=dev)
+        wf = binding.empty_grouped_weights(E, N, K, dev)
+        wp = binding.empty_grouped_weights(E, N, K, dev)
+        for ex in range(E):
+            s = binding.calibrate(case.xcal[ex].to(dev))
+            ae, re_ = binding.make_multipliers(s, b)
+            a[ex].copy_(ae)
+            w = case.w[ex].to(dev)
+            binding.prepare_weights(w, re_, b, out=binding.expert(wf, ex))
+            binding.prepare_weights(w, None, 0, out=binding.expert(wp, ex))
+        wfs = [wf] + [packed_clone(binding, wf) for _ in range(ROTATE - 1)]
+        wps = [wp] + [packed_clone(binding, wp) for _ in range(ROTATE - 1)]
+        xs = [case.x.to(dev) for _ in range(ROTATE)]
+        y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+        work = torch.empty(max(binding.linear_grouped_workspace_size(T, E, K, N), 1), dtype=torch.uint8,
+                           device=dev)
+        wbytes = E * N * K * 17 / 32
+        e = Entry("%s T=%d E=%d K=%d N=%d" % (proj, T, E, K, N), 2.0 * T * N * K, 2 * T * K + wbytes + 2 * T * N,
+                  T * K * 17 / 32 + wbytes + 2 * T * N)
+        e.fused = lambda c, xs=xs, a=a, wfs=wfs, y=y, work=work, off=offsets: binding.linear_grouped(
+            xs[c], off, a, b, wfs[c], out=y, workspace=work)
+        e.plain = lambda c, xs=xs, wps=wps, y=y, work=work, off=offsets: binding.linear_grouped(
+            xs[c], off, None, 0, wps[c], out=y, workspace=work)
+        e.oracle_case = (case, None)
+        entries.append(e)
+        del case
+    return entries
 
 
 def capture(torch, fn):
@@ -133,91 +195,84 @@ def capture(torch, fn):
     return g
 
 
-def timed_graphs(torch, graphs, steps, warmup):
-    """Replay graphs[i % len] for warmup untimed and `steps` timed steps."""
-    for i in range(warmup):
-        graphs[i % len(graphs)].replay()
+def timed_steps(torch, step, steps, warmup):
+    """`warmup` untimed steps, then exactly `steps` timed steps, each step(c)
+    on operand copy c = i % ROTATE. The steps are captured in one HIP graph
+    per phase, so the timed replay has no host gaps between steps; HIP events
+    on the launch stream bracket it. Returns (ms per step, wall seconds)."""
+    gw = capture(torch, lambda: [step(i % ROTATE) for i in range(warmup)]) if warmup > 0 else None
+    gt = capture(torch, lambda: [step((warmup + i) % ROTATE) for i in range(steps)])
+    if gw is not None:
+        gw.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with Timer(torch) as t:
-        for i in range(steps):
-            graphs[(warmup + i) % len(graphs)].replay()
+        gt.replay()
     torch.cuda.synchronize()
     return t.ms() / steps, time.perf_counter() - t0
 
 
-def kernel_breakdown(torch, binding, layers, reps):
-    """Per layer: the two kernels of macaq_linear (quantize, GEMM) each alone,
-    `reps` launches captured in one graph, timed with HIP events on the launch
-    stream around the replay; returns average ms per launch."""
-    q_ms, g_ms = [], []
-    for L in layers:
-        def quant():
-            for i in range(reps):
-                c = L["copies"][i % ROTATE]
-                binding.quant_act(c["x"], L["a"], L["b"], layout="gemm", codes=L["qa"].codes, scales=L["qa"].scales)
-
-        def gemm():
-            for i in range(reps):
-                c = L["copies"][i % ROTATE]
-                binding.linear_plain_gemm(L["qa"], c["w"], out=L["y"], workspace=L["gwork"])
-
-        for fn, acc in ((quant, q_ms), (gemm, g_ms)):
-            g = capture(torch, fn)
-            g.replay()
-            torch.cuda.synchronize()
-            with Timer(torch) as t:
-                g.replay()
-            torch.cuda.synchronize()
-            acc.append(t.ms() / reps)
-    return q_ms, g_ms
-
-
-def cpu_baseline(layers, target_s):
-    """The oracle (C, fp64 GEMM over codes, as it stands) on a bounded row sample."""
+def cpu_baseline(entries, target_s, moe):
+    """The oracle (C, fp64 GEMM over codes, as it stands) on a bounded sample
+    of the step's rows: rows of every dense layer, or the first experts."""
     import numpy as np
 
     import oracle
     from mxfp4_w4a4_post_amd import inputs as inp
 
     threads = min(oracle.default_threads(), ORACLE_THREADS_CAP)
+    if moe:
+        flops, dt, experts = 0.0, 0.0, 0
+        while dt < target_s and experts < entries[0].oracle_case[0].E:
+            for e in entries:
+                case = e.oracle_case[0]
+                lo, hi = int(case.offsets[experts]), int(case.offsets[experts + 1])
+                if hi <= lo:
+                    continue
+                s = oracle.calibrate(inp.bf16_bits(case.xcal[experts]))
+                a, r = oracle.multipliers(s, case.b)
+                wc, ws = oracle.prepare_weights(inp.bf16_bits(case.w[experts]), r, case.b)
+                xb = np.ascontiguousarray(inp.bf16_bits(case.x[lo:hi]))
+                t0 = time.perf_counter()
+                oracle.linear(xb, a, case.b, wc, ws, threads=threads)
+                dt += time.perf_counter() - t0
+                flops += 2.0 * (hi - lo) * case.N * case.K
+            experts += 1
+        return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
+                    sample="experts 0..%d of both projections (quantize + fp64 GEMM over codes, weights prepared "
+                           "outside the timing), %.1f s" % (experts - 1, dt))
     prepared = []
-    for L in layers:
-        case = L["case"]
+    for e in entries:
+        case, M = e.oracle_case
         s = oracle.calibrate(inp.bf16_bits(case.xcal))
         a, r = oracle.multipliers(s, case.b)
         wc, ws = oracle.prepare_weights(inp.bf16_bits(case.w), r, case.b)
-        prepared.append((inp.bf16_bits(case.x), a, case.b, wc, ws, L["K"], L["N"]))
-    rows = 4
+        prepared.append((inp.bf16_bits(case.x[:M]), a, case.b, wc, ws, case.K, case.N, M))
+    frac = 1.0 / 64
     while True:
         t0 = time.perf_counter()
-        flops = 0
-        for xb, a, b, wc, ws, K, N in prepared:
+        flops, rows_done, rows_all = 0.0, 0, 0
+        for xb, a, b, wc, ws, K, N, M in prepared:
+            rows = max(1, min(M, int(round(M * frac))))
             oracle.linear(np.ascontiguousarray(xb[:rows]), a, b, wc, ws, threads=threads)
-            flops += 2 * rows * K * N
+            flops += 2.0 * rows * K * N
+            rows_done += rows
+            rows_all += M
         dt = time.perf_counter() - t0
-        if dt >= target_s * 0.5 or rows >= layers[0]["M"]:
+        if dt >= target_s * 0.5 or frac >= 1.0:
             break
-        rows = min(layers[0]["M"], max(rows * 2, int(rows * target_s / max(dt, 1e-3))))
+        frac = min(1.0, frac * max(2.0, target_s / max(dt, 1e-3)))
     return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
-                sample="%d of %d token rows through all %d layers (quantize + fp64 GEMM over codes), %.1f s"
-                       % (rows, layers[0]["M"], len(layers), dt))
+                sample="%d of %d token rows over the step's %d layer calls (quantize + fp64 GEMM over codes, "
+                       "weights prepared outside the timing), %.1f s" % (rows_done, rows_all, len(prepared), dt))
 
 
-def copy_mb(layers):
-    total = 0
-    for L in layers:
-        c = L["copies"][0]
-        total += c["x"].numel() * 2 + c["w"].codes.numel() + c["w"].scales.numel()
-    return total / 1e6
-
-
-def load_traffic(kernel_digest):
+def load_traffic(workload, kernel_digest):
     """HBM bytes (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known
     size) per GEMM launch, the mean over the step's layers, from the committed
     rocprofv3 counter summary; None unless it was taken on the current kernel
     source."""
-    path = os.path.join(ROOT, "profiles", "gemm_prefill_8b_pmc.json")
+    path = os.path.join(ROOT, "profiles", "gemm_%s_pmc.json" % workload.replace("-", "_"))
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -230,8 +285,8 @@ def load_traffic(kernel_digest):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md for how the layer "
-              "would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: this build has no multi-GPU path (the design notes describe how the "
+              "layer would shard); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -248,33 +303,43 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copied_bytes": n, "copies": 3}), flush=True)
         return
-    wl = {"tiny": 1, "prefill-8b": 2, "decode-32b": 3, "moe-128e": 4, "prefill-large": 5}[args.workload]
-    if wl in (3, 4):
-        print("workload %s: not wired into bench.py yet" % args.workload, file=sys.stderr)
-        sys.exit(2)
+    wl = WORKLOADS[args.workload]
     spec = inputs.CONFIGS[wl]
     b = args.block if args.block is not None else spec["blocks"][0]
-    M = spec["M"]
-    shapes = spec["shapes"]
-    layers = build_layers(torch, binding, inputs, wl, shapes, M, b, dev)
+    moe = wl == 4
+    if moe:
+        entries = moe_entries(torch, binding, inputs, b, dev)
+        workload = ("%s: %d tokens routed top-%d over %d experts (Zipf(%.1f) popularity), grouped gate/up %d->%d "
+                    "and down %d->%d, Hadamard block %d, bf16 in/out"
+                    % (spec["name"], spec["tokens"], spec["top_k"], spec["experts"], spec["zipf"], spec["hidden"],
+                       2 * spec["ffn"], spec["ffn"], spec["hidden"], b))
+        tokens = spec["tokens"]
+        cfg_extra = {"tokens": tokens, "experts": spec["experts"], "top_k": spec["top_k"], "hadamard_block": b}
+    else:
+        entries, Ms = dense_entries(torch, binding, inputs, wl, b, dev)
+        workload = ("%s: M=%s tokens, (K,N) in %s, Hadamard block %d, bf16 in/out"
+                    % (spec["name"], Ms[0] if len(Ms) == 1 else Ms, spec["shapes"], b))
+        tokens = sum(Ms)
+        cfg_extra = {"tokens": Ms[0] if len(Ms) == 1 else Ms, "layers": [list(s) for s in spec["shapes"]],
+                     "hadamard_block": b}
     torch.cuda.synchronize()
+
+    def step(c, plain=False):
+        for e in entries:
+            (e.plain if plain else e.fused)(c)
 
     if args.profile_steps > 0:
         for i in range(args.profile_steps):
-            enqueue_step(binding, layers, i % ROTATE)
+            step(i % ROTATE)
         torch.cuda.synchronize()
         print(json.dumps({"profiled_steps": args.profile_steps, "workload": spec["name"]}), flush=True)
         return
 
-    flops = sum(2 * M * K * N for K, N in shapes)
-    fused = [capture(torch, lambda c=c: enqueue_step(binding, layers, c)) for c in range(ROTATE)]
-    plain = [capture(torch, lambda c=c: enqueue_step(binding, layers, c, plain=True)) for c in range(ROTATE)]
-    ms, wall = timed_graphs(torch, fused, args.steps, args.warmup)
-    ms_plain, _ = timed_graphs(torch, plain, args.steps, args.warmup)
-    q_ms, g_ms = kernel_breakdown(torch, binding, layers, 20)
+    flops = sum(e.flops for e in entries)
+    nbytes = sum(e.bytes for e in entries)
+    ms, wall = timed_steps(torch, step, args.steps, args.warmup)
+    ms_plain, _ = timed_steps(torch, lambda c: step(c, True), args.steps, args.warmup)
     tflops = flops / (ms * 1e-3) / 1e12
-    gemm_ms = sum(g_ms)
-    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     digest = source_digest([os.path.join(ROOT, "mxfp4_w4a4_post_amd", "csrc", "gemm.hip")])
     out = {
         "metric": METRIC,
@@ -288,25 +353,54 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp4 (MXFP4 E2M1/E8M0 operands, fp32 accumulate, fp32 transform, bf16 in/out)",
-        "data": "synthetic (seeded Student-t(3) activations with 1% outlier channels x30, N(0,0.02^2) weights)",
-        "config": {"workload": "%s: M=%d tokens, (K,N) in %s, Hadamard block %d, bf16 in/out"
-                               % (spec["name"], M, shapes, b),
-                   "tokens": M, "layers": [list(s) for s in shapes], "hadamard_block": b},
+        "data": "synthetic (seeded activations with outlier channels, N(0,sigma^2) weights; recipe in inputs.py)",
+        "config": dict({"workload": workload}, **cfg_extra),
         "pct_mxfp4_peak": round(100 * tflops / PEAK_FP4_TFLOPS, 2),
-        "tokens_per_s": round(M / (ms * 1e-3), 1),
+        "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+        "hbm_gbs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
         "plain_mxfp4_ms_per_step": round(ms_plain, 5),
         "transform_overhead_pct": round(100 * (ms / ms_plain - 1), 2),
         "wall_s_timed": round(wall, 4),
-        "timing": "HIP graphs of one step per operand copy (%d copies, %.0f MB each, cycled past the 256 MB "
-                  "last-level cache), HIP events on the launch stream" % (ROTATE, copy_mb(layers)),
-        "kernels_ms": {"quant": [round(v, 5) for v in q_ms], "gemm": [round(v, 5) for v in g_ms]},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP4_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
-                     "traffic": load_traffic(digest), "kernel": "gemm_kernel (scaled-FP4 MFMA)",
-                     "kernel_source_digest": digest},
+        "timing": "the timed steps in one HIP graph (operand copies cycled, %d copies), HIP events on the launch "
+                  "stream" % ROTATE,
     }
+    if not moe:
+        # each kernel of the step alone: the same timed steps with only that
+        # kernel of every layer call, on the same operand copies
+        def kernel_ms(attr):
+            return timed_steps(torch, lambda c: [getattr(e, attr)(c) for e in entries], args.steps,
+                               args.warmup)[0]
+
+        q, g, qp, gp = (kernel_ms(k) for k in ("quant", "gemm", "quant_plain", "gemm_plain"))
+        out["kernels_ms_per_step"] = {"calls": len(entries), "quant": round(q, 5), "gemm": round(g, 5),
+                                      "quant_plain": round(qp, 5), "gemm_plain": round(gp, 5)}
+        out["overhead_split_ms"] = {"quantize": round(q - qp, 5), "gemm_on_transformed_codes": round(g - gp, 5)}
+        gemm_ms = g
+        if wl == 3:  # decode: the GEMM streams the weights
+            gb = sum(e.gemm_bytes for e in entries) / (gemm_ms * 1e-3) / 1e9
+            out["roofline"] = {"bound": "hbm", "achieved": round(gb, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(gb / PEAK_HBM_GBS, 4), "traffic": load_traffic(spec["name"], digest),
+                               "kernel": "gemm_kernel (weights streamed per wave)",
+                               "avg_launch_us": round(1e3 * gemm_ms / len(entries), 3),
+                               "kernel_source_digest": digest}
+        else:
+            tf = flops / (gemm_ms * 1e-3) / 1e12
+            out["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP4_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(tf / PEAK_FP4_TFLOPS, 4),
+                               "traffic": load_traffic(spec["name"], digest),
+                               "kernel": "gemm_kernel (scaled-FP4 MFMA)",
+                               "avg_launch_us": round(1e3 * gemm_ms / len(entries), 3),
+                               "kernel_source_digest": digest}
+    else:
+        calls = [timed_steps(torch, e.fused, 10, 2)[0] for e in entries]
+        gb = nbytes / (sum(calls) * 1e-3) / 1e9
+        out["calls_ms"] = {"calls": [e.name for e in entries], "fused": [round(v, 5) for v in calls]}
+        out["roofline"] = {"bound": "hbm", "achieved": round(gb, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(gb / PEAK_HBM_GBS, 4), "traffic": None,
+                           "kernel": "macaq_linear_grouped (quantize + tile map + grouped GEMM per call)",
+                           "kernel_source_digest": digest}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(entries, args.cpu_seconds, moe)
     print(json.dumps(out), flush=True)
 
 
