@@ -29,8 +29,9 @@ namespace macaq {
 namespace {
 
 constexpr int NH = kBlockK / 64;  // MFMAs along K per step (4)
-constexpr int kEpiPitch = 64 * 2 + 16;  // epilogue staging: one row of 64 bf16, padded (16-byte aligned)
-constexpr int kEpiRegion = 32 * kEpiPitch;  // one wave's 32 staged rows
+// epilogue staging: one wave's 32 rows of WN bf16, each padded by 16 bytes
+constexpr int epi_pitch(int wn) { return wn * 2 + 16; }
+constexpr int epi_region(int wn) { return 32 * epi_pitch(wn); }
 constexpr int NT = 256;           // 4 waves
 constexpr int kNumCu = 256;
 
@@ -44,9 +45,14 @@ constexpr int lcm2(int a, int b) {
   return a / x * b;
 }
 
-template <int BM_, int BN_, int PW_, int PA_>
+// OVERLAP: issue the next tile's loads before the current tile's epilogue
+// (hides their latency; keeps both tiles' registers live at once).
+// OCC: resident workgroups per CU (waves per SIMD) the register budget is
+// sized for; the persistent grid is OCC workgroups per CU.
+template <int BM_, int BN_, int PW_, int PA_, bool OVERLAP_ = true, int OCC_ = 1>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, PW = PW_, PA = PA_;
+  static constexpr int BM = BM_, BN = BN_, PW = PW_, PA = PA_, OCC = OCC_;
+  static constexpr bool OVERLAP = OVERLAP_;
   static constexpr int FM = BM / kGroupRows;  // activation fragments (32 rows each)
   static constexpr int WN = BN / 4;           // weight rows per wave
   static constexpr int FN = WN / kGroupRows;  // weight fragments per wave
@@ -59,7 +65,7 @@ struct TileCfg {
   static constexpr int STAGE = A_CODES + A_SCALES + LDS_TRASH;
   static constexpr int NBUF = 3;  // LDS buffers: compute s, read s+1, write s+2
   // the epilogue reuses the LDS: one staging region per wave
-  static constexpr int LDS_BYTES = (NBUF * STAGE > 4 * kEpiRegion) ? NBUF * STAGE : 4 * kEpiRegion;
+  static constexpr int LDS_BYTES = (NBUF * STAGE > 4 * epi_region(WN)) ? NBUF * STAGE : 4 * epi_region(WN);
   // main-loop unroll: register slots static
   static constexpr int U = lcm2(PW, PA);
   static constexpr int N_MFMA = FM * FN;  // per half step
@@ -211,15 +217,17 @@ __device__ __forceinline__ void store_sel(const Acc<C>& acc, void* p, int64_t ld
   }
 }
 
-// bf16 output staged through a wave-private LDS region (kEpiRows rows of
-// kEpiPitch bytes): per 32-row fragment the wave writes its 32 x 64 tile in
-// the MFMA layout and reads it back by rows, so each store instruction writes
-// 8 whole 128-byte row segments instead of 16-byte pieces of 32 rows.
-
+// bf16 output staged through a wave-private LDS region: per 32-row fragment
+// the wave writes its 32 x WN tile in the MFMA layout and reads it back by
+// rows, so each store instruction writes whole row segments of 2*WN bytes
+// instead of 16-byte pieces of 32 rows.
 template <class C>
 __device__ __forceinline__ void store_bf16_staged(const Acc<C>& acc, uint16_t* y, int64_t ld, int64_t m_lim,
                                                   int64_t n_lim, uint8_t* region, int lane) {
-  static_assert(C::WN == 64, "one 128-byte row segment per wave");
+  constexpr int PITCH = epi_pitch(C::WN);
+  constexpr int LPR = C::WN / 8;       // lanes per row (16 bytes each)
+  constexpr int RPP = 64 / LPR;        // rows per pass
+  static_assert(C::WN == 32 || C::WN == 64, "row segment of one wave");
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
@@ -231,17 +239,18 @@ __device__ __forceinline__ void store_bf16_staged(const Acc<C>& acc, uint16_t* y
         uint2 w;
         w.x = f32_to_bf16_rne(a[4 * q]) | (f32_to_bf16_rne(a[4 * q + 1]) << 16);
         w.y = f32_to_bf16_rne(a[4 * q + 2]) | (f32_to_bf16_rne(a[4 * q + 3]) << 16);
-        lds_at<uint2>(region, (lane & 31) * kEpiPitch + n * 2) = w;
+        lds_at<uint2>(region, (lane & 31) * PITCH + n * 2) = w;
       }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = p * 8 + (lane >> 3), c = (lane & 7) * 8;
-      const uint4 v = lds_at<uint4>(region, r * kEpiPitch + c * 2);
+    for (int p = 0; p < 32 / RPP; ++p) {
+      const int r = p * RPP + lane / LPR, c = (lane % LPR) * 8;
+      const uint4 v = lds_at<uint4>(region, r * PITCH + c * 2);
       const int m = i * 32 + r;
       if (m < m_lim) {
         uint16_t* dst = y + m * ld + c;
         if (c + 8 <= n_lim) {
-          *reinterpret_cast<uint4*>(dst) = v;
+          // streaming store: the output is not read again by this kernel
+          __builtin_nontemporal_store(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, reinterpret_cast<v4i*>(dst));
         } else {
           const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -268,7 +277,7 @@ __device__ __forceinline__ void store_out(const Acc<C>& acc, const GemmArgs& g, 
     store_sel<C, 2>(acc, p, g.N, m_lim, n_lim, g.vec_partial, lane);
   } else if constexpr (MODE == kOutBf16Staged) {
     store_bf16_staged<C>(acc, static_cast<uint16_t*>(g.y) + m0 * g.ldy + n0, g.ldy, m_lim, n_lim,
-                         smem + wave * kEpiRegion, lane);
+                         smem + wave * epi_region(C::WN), lane);
   } else if constexpr (MODE == kOutBf16) {
     store_sel<C, 1>(acc, static_cast<uint16_t*>(g.y) + m0 * g.ldy + n0, g.ldy, m_lim, n_lim, g.vec_y, lane);
   } else {
@@ -605,12 +614,16 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& g, int64_t total, uin
     TileRef nxt;
     int64_t tn = t + gridDim.x;
     while (tn < total && !tile_at<C, GROUPED>(g, xcd_remap(tn, total), nxt)) tn += gridDim.x;
-    if (tn < total) {
+    if (C::OVERLAP && tn < total) {
       p.set_tile(g, nxt.tc, g.M, nxt.bc, nxt.bs);
       p.prologue_loads();
     }
     store_out<C, MODE>(p.acc, g, cur.tc, wave, lane, smem);
     if (tn >= total) break;
+    if (!C::OVERLAP) {
+      p.set_tile(g, nxt.tc, g.M, nxt.bc, nxt.bs);
+      p.prologue_loads();
+    }
     __syncthreads();  // every wave is done with its epilogue staging in LDS
     cur = nxt;
     t = tn;
@@ -618,7 +631,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& g, int64_t total, uin
 }
 
 template <class C, int MODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC))) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
   const int64_t tiles = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
   gemm_tiles<C, false, MODE>(g, tiles * g.splits, smem);
@@ -627,7 +640,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // Grouped: the tile map (built by build_tile_map_kernel) lists, per m-tile,
 // the expert and the first row; unused entries are skipped.
 template <class C, int MODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_grouped_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC))) void gemm_grouped_kernel(
+    GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
   gemm_tiles<C, true, MODE>(g, g.max_mtiles * ((g.N + C::BN - 1) / C::BN), smem);
 }
@@ -667,9 +681,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   else static_cast<float*>(y)[m * ldy + n] = s;
 }
 
-using CfgM = TileCfg<128, 256, 2, 2>;  // prefill
-using CfgS64 = TileCfg<64, 256, 4, 2>; // decode, M <= 64
-using CfgS32 = TileCfg<32, 256, 4, 2>; // decode, M <= 32
+#ifndef CFGM
+#define CFGM 128, 256, 2, 2
+#endif
+using CfgM = TileCfg<CFGM>;  // prefill
+#ifndef CFGS64
+#define CFGS64 64, 128, 4, 2, true, 2
+#endif
+#ifndef CFGS32
+#define CFGS32 32, 128, 4, 2, true, 2
+#endif
+using CfgS64 = TileCfg<CFGS64>;  // decode, M <= 64
+using CfgS32 = TileCfg<CFGS32>;  // decode, M <= 32
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
@@ -677,7 +700,8 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
   const int64_t nt = (g.N + C::BN - 1) / C::BN;
   const int64_t total = mt * nt * g.splits;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const int64_t grid = total < kNumCu ? total : kNumCu;  // one resident workgroup per CU
+  const int64_t resident = (int64_t)kNumCu * C::OCC;
+  const int64_t grid = total < resident ? total : resident;
   const dim3 gd((unsigned)grid), bd(NT);
   if (g.splits > 1) hipLaunchKernelGGL((gemm_kernel<C, kOutPartial>), gd, bd, 0, stream, g);
   else if (g.y_bf16 && g.vec16_y) hipLaunchKernelGGL((gemm_kernel<C, kOutBf16Staged>), gd, bd, 0, stream, g);
@@ -713,28 +737,39 @@ void set_vec_flags(GemmArgs& g) {
 
 }  // namespace
 
-#ifndef MACAQ_DECODE_UNITS
-#define MACAQ_DECODE_UNITS 256
-#endif
-constexpr int64_t kDecodeUnits = MACAQ_DECODE_UNITS;
+// Bytes a CU would stream in the time a work unit spends starting its
+// pipeline (first loads in flight, nothing consumed yet).
+constexpr double kUnitStartBytes = 64.0 * 1024.0;
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   GemmPlan p{};
-  if (M <= 32) { p.cfg = 3; p.bm = 32; }
-  else if (M <= 64) { p.cfg = 2; p.bm = 64; }
-  else { p.cfg = 1; p.bm = 128; }
-  p.bn = 256;
+  int64_t resident;
+  if (M <= 32) { p.cfg = 3; p.bm = CfgS32::BM; p.bn = CfgS32::BN; resident = (int64_t)kNumCu * CfgS32::OCC; }
+  else if (M <= 64) { p.cfg = 2; p.bm = CfgS64::BM; p.bn = CfgS64::BN; resident = (int64_t)kNumCu * CfgS64::OCC; }
+  else { p.cfg = 1; p.bm = CfgM::BM; p.bn = CfgM::BN; resident = (int64_t)kNumCu * CfgM::OCC; }
   const int64_t nt = (N + p.bn - 1) / p.bn;
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * nt;
   const int64_t KT = pad_k(K) / kBlockK;
   int64_t splits = 1;
-  // Skinny (decode) shapes stream the weights: split K so that about
-  // kDecodeUnits work units of at least 4 k-blocks keep every CU streaming
-  // (the persistent workgroups take about two units each).
-  if (M <= 64 && tiles < kDecodeUnits) {
-    splits = (kDecodeUnits + tiles / 2) / tiles;
-    if (splits > KT / 4) splits = KT / 4;
-    if (splits < 1) splits = 1;
+  // Skinny (decode) shapes stream the weights. Split K (units of at least 4
+  // k-blocks) to keep every CU streaming: the units spread evenly over the
+  // CUs, so the time goes as the weight bytes of the busiest CU (units per
+  // CU, rounded up, times the longest unit plus a pipeline start of about
+  // kUnitStartBytes each), plus the fp32 partial sums written and read back.
+  if (M <= 64 && tiles < resident) {
+    const double row_block_bytes = (double)p.bn * kBlockK * 17.0 / 32.0;  // one tile's weights per k-block
+    double best = 0.0;
+    for (int64_t s = 1; s <= KT / 4 || s == 1; ++s) {
+      const int64_t units = tiles * s;
+      const int64_t per_cu = (units + kNumCu - 1) / kNumCu;
+      const double unit_bytes = row_block_bytes * (double)((KT + s - 1) / s);
+      const double partial = s > 1 ? 8.0 * (double)M * (double)N * (double)s : 0.0;
+      const double cost = (double)kNumCu * (double)per_cu * (unit_bytes + kUnitStartBytes) + partial;
+      if (s == 1 || cost < best) {
+        best = cost;
+        splits = s;
+      }
+    }
   }
   p.splits = (int)splits;
   p.partial_bytes = splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;

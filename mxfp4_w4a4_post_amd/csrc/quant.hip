@@ -56,12 +56,25 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
   const bool valid = row < q.M && k0 < q.K;
 
   // the block's 256 multipliers are shared by its 32 rows: stage them in LDS
-  // once (MoE rows may belong to different experts, so those read their own)
+  // once. MoE rows take their expert's multipliers; a block whose rows span
+  // two experts (rows are expert-major) has each lane read its own.
   __shared__ __attribute__((aligned(16))) float msh[kBlockK];
-  if constexpr (SCALE && !GROUPED) {
-    const int64_t kk = (int64_t)blockIdx.y * kBlockK + tid;
-    msh[tid] = kk < q.K ? q.mult[kk] : 0.0f;
-    __syncthreads();
+  bool staged = false;
+  if constexpr (SCALE) {
+    const float* mrow = q.mult;
+    staged = true;
+    if constexpr (GROUPED) {
+      const int64_t r0 = (int64_t)blockIdx.x * kGroupRows;
+      const int64_t r1 = (r0 + kGroupRows - 1 < q.M ? r0 + kGroupRows - 1 : q.M - 1);
+      const int e0 = expert_of_row(q.offsets, q.E, r0 < q.M ? r0 : q.M - 1);
+      staged = e0 == expert_of_row(q.offsets, q.E, r1);
+      mrow += (int64_t)e0 * q.K;
+    }
+    if (staged) {
+      const int64_t kk = (int64_t)blockIdx.y * kBlockK + tid;
+      msh[tid] = kk < q.K ? mrow[kk] : 0.0f;
+      __syncthreads();
+    }
   }
 
   float v[32];
@@ -93,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
     }
     if constexpr (SCALE) {
       const float4* mp;
-      if constexpr (GROUPED)
+      if (GROUPED && !staged)
         mp = reinterpret_cast<const float4*>(q.mult + (int64_t)expert_of_row(q.offsets, q.E, row) * q.K + k0);
       else
         mp = reinterpret_cast<const float4*>(msh + c * 32);
