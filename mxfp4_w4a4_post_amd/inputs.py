@@ -157,12 +157,13 @@ class MoECase:
     counts: np.ndarray = field(default=None)
 
 
-def moe_routing(tokens: int, experts: int, top_k: int, zipf: float, seed_cfg: int = 4):
+def moe_topk(tokens: int, experts: int, top_k: int, zipf: float, seed_cfg: int = 4):
     """Top-k expert choice per token with Zipf(`zipf`) expert popularity.
 
     Logits are ln p(pi(e)) + Gumbel(0, 1) with p(r) proportional to r^-zipf
     and pi a seeded permutation of the experts; each token takes its k
-    largest logits. Returns (expert-major row -> token index, offsets[E+1]).
+    largest logits. Returns (ids int32 [T, k], routing weights fp32 [T, k]:
+    the softmax of the token's k chosen logits).
     """
     rng = _rng(seed_cfg, 0, 4)
     ranks = np.arange(1, experts + 1, dtype=np.float64)
@@ -173,6 +174,16 @@ def moe_routing(tokens: int, experts: int, top_k: int, zipf: float, seed_cfg: in
     g = rng.gumbel(size=(tokens, experts))
     logits = logp[None, :] + g
     topk = np.argsort(-logits, axis=1, kind="stable")[:, :top_k]
+    chosen = np.take_along_axis(logits, topk, axis=1)
+    wexp = np.exp(chosen - chosen.max(axis=1, keepdims=True))
+    weights = (wexp / wexp.sum(axis=1, keepdims=True)).astype(np.float32)
+    return topk.astype(np.int32), weights
+
+
+def moe_routing(tokens: int, experts: int, top_k: int, zipf: float, seed_cfg: int = 4):
+    """The grouped layer's row order for the routing of `moe_topk`: rows sorted
+    by expert, then token. Returns (row -> token index, offsets[E+1])."""
+    topk, _ = moe_topk(tokens, experts, top_k, zipf, seed_cfg)
     tok = np.repeat(np.arange(tokens), top_k)
     exp_ = topk.reshape(-1)
     order = np.lexsort((tok, exp_))  # by expert, then token
@@ -211,3 +222,58 @@ def moe_case(proj: str = "gate_up", tokens: int | None = None, experts: int | No
         wt = torch.empty(E, 0, K, dtype=torch.bfloat16)
     counts = np.diff(offsets)
     return MoECase(int(offsets[-1]), E, K, N, spec["blocks"][0], x, offsets, tok_of_row, xcal, wt, counts)
+
+
+@dataclass
+class MoEBlockCase:
+    """The MoE block: T bf16 tokens [T, H], top-k ids and routing weights
+    [T, k], per-expert calibration rows for the gate/up input [E, 64, H] and
+    for the down input [E, 64, F], and bf16 weights gate, up [E, F, H] and
+    down [E, H, F]."""
+    T: int
+    E: int
+    k: int
+    H: int
+    F: int
+    b: int
+    x: torch.Tensor
+    ids: np.ndarray
+    w: np.ndarray
+    xcal_gu: torch.Tensor
+    xcal_dn: torch.Tensor
+    w_gate: torch.Tensor
+    w_up: torch.Tensor
+    w_dn: torch.Tensor
+
+
+def moe_block_case(tokens: int | None = None, experts: int | None = None, top_k: int | None = None,
+                   hidden: int | None = None, ffn: int | None = None, b: int | None = None,
+                   with_weights: bool = True) -> MoEBlockCase:
+    """The MoE workload as a whole block (defaults: 4096 tokens, 128 experts,
+    top-8, hidden 2048, expert FFN 768, b = 32). Token activations follow the
+    MoE recipe at K = hidden; the down projection's calibration rows are
+    drawn with the same recipe at K = ffn (a stand-in for the gated
+    activations of calibration text). Smaller sizes keep the distributions."""
+    spec = MOE
+    T = spec["tokens"] if tokens is None else tokens
+    E = spec["experts"] if experts is None else experts
+    k = min(spec["top_k"] if top_k is None else top_k, E)
+    H = spec["hidden"] if hidden is None else hidden
+    F = spec["ffn"] if ffn is None else ffn
+    b = spec["blocks"][0] if b is None else b
+    ids, w = moe_topk(T, E, k, spec["zipf"])
+    chans_h = outlier_channels(4, 0, H)
+    chans_f = outlier_channels(4, 1, F)
+    x = to_bf16(_draw_acts(_rng(4, 0, 2), 4, T, H, chans_h))
+    xcal_gu = to_bf16(_draw_acts(_rng(4, 0, 1), 4, E * CALIB_ROWS, H, chans_h).reshape(E, CALIB_ROWS, H))
+    xcal_dn = to_bf16(_draw_acts(_rng(4, 1, 1), 4, E * CALIB_ROWS, F, chans_f).reshape(E, CALIB_ROWS, F))
+    if with_weights:
+        rng = _rng(4, 2, 3)
+        wg = rng.standard_normal((E, F, H), dtype=np.float32) * np.float32(0.02)
+        wu = rng.standard_normal((E, F, H), dtype=np.float32) * np.float32(0.02)
+        wd = rng.standard_normal((E, H, F), dtype=np.float32) * np.float32(0.02)
+        w_gate, w_up, w_dn = to_bf16(wg), to_bf16(wu), to_bf16(wd)
+    else:
+        w_gate = w_up = torch.empty(E, 0, H, dtype=torch.bfloat16)
+        w_dn = torch.empty(E, 0, F, dtype=torch.bfloat16)
+    return MoEBlockCase(T, E, k, H, F, b, x, ids, w, xcal_gu, xcal_dn, w_gate, w_up, w_dn)

@@ -14,10 +14,17 @@ arithmetic lives there, with its sources:
   layer's weights, MXFP4 W4A4, round-to-nearest weights.
 * OCP Microscaling Formats v1.0 -- E2M1 elements, one E8M0 scale per 32.
 
+* The MoE block (routing, gathered gate/up, SiLU * up, the down projection's
+  own transform and MXFP4, down, weighted combine): "MACaQ - Huawei
+  open-sources a 4-bit quantizer ..." (What it is) covers MoE models;
+  "Huawei's MACaQ-R beats Unsloth's ..." ("Changed tensors") names the
+  experts' gate, up and down projections. The gated FFN form is a reading.
+
 Parity status per function (what pins it, see ``tests/test_oracle_pins.py``):
 calibrate, multipliers, transform_rows, quant_rows, dequant_rows, gemm_codes,
-linear and linear_grouped are all pinned by closed forms, hand-worked values
-and brute force; none is "parity unpinned".
+linear, linear_grouped, moe_route, silu_mul, moe_combine and moe_block are
+all pinned by closed forms, hand-worked values, independent restatements and
+brute force; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -67,8 +74,14 @@ def _load():
     lib.oracle_linear.argtypes = [vp, _i64, _i64, _i64, _f32p, _int, _u8p, _u8p, _i64, _f64p, _int]
     lib.oracle_linear_grouped.argtypes = [vp, _i32p, _int, _i64, _i64, _f32p, _int, _u8p, _u8p, _i64,
                                           _f64p, _int]
+    lib.oracle_moe_route.argtypes = [_i32p, _i64, _int, _int, _i32p, _i32p, _i32p]
+    lib.oracle_silu_mul.argtypes = [_f64p, _i64, _i64, _f32p]
+    lib.oracle_moe_combine.argtypes = [_f32p, _i64, _i32p, _f32p, _i64, _int, _f64p]
+    lib.oracle_moe_block.argtypes = [vp, _i64, _i64, _i32p, _f32p, _int, _int, _f32p, _u8p, _u8p, _f32p, _u8p,
+                                     _u8p, _i64, _int, _u8p, _u8p, _u8p, _f64p, _int]
     for f in (lib.oracle_calibrate, lib.oracle_multipliers, lib.oracle_transform_rows, lib.oracle_quant_rows,
-              lib.oracle_dequant_rows, lib.oracle_gemm_codes, lib.oracle_linear, lib.oracle_linear_grouped):
+              lib.oracle_dequant_rows, lib.oracle_gemm_codes, lib.oracle_linear, lib.oracle_linear_grouped,
+              lib.oracle_moe_route, lib.oracle_silu_mul, lib.oracle_moe_combine, lib.oracle_moe_block):
         f.restype = _int
     _lib = lib
     return lib
@@ -213,3 +226,76 @@ def linear_grouped(x: np.ndarray, offsets: np.ndarray, a, b: int, w_codes, w_sca
                                      _ptr(ws, _u8p), N, _ptr(y, _f64p), threads or default_threads()),
            "linear_grouped")
     return y
+
+
+def moe_route(ids: np.ndarray, E: int):
+    """(offsets [E+1], row_token [T*k], pos [T*k]) of the stable sort of the
+    (token, slot) entries by expert; ids [T, k] int32."""
+    lib = _load()
+    ids = np.ascontiguousarray(ids, np.int32)
+    T, k = ids.shape
+    off = np.empty(E + 1, np.int32)
+    row_token = np.full(T * k, -1, np.int32)
+    pos = np.empty(T * k, np.int32)
+    _check(lib.oracle_moe_route(_ptr(ids, _i32p), T, k, E, _ptr(off, _i32p), _ptr(row_token, _i32p),
+                                _ptr(pos, _i32p)), "moe_route")
+    return off, row_token, pos
+
+
+def silu_mul(gu: np.ndarray) -> np.ndarray:
+    """h [R, F] fp32 = SiLU(gate) * up from stacked gate/up outputs [R, 2F]
+    (blocks of 32 gate columns, then the matching 32 up columns)."""
+    lib = _load()
+    gu = np.ascontiguousarray(gu, np.float64)
+    R, F2 = gu.shape
+    h = np.empty((R, F2 // 2), np.float32)
+    _check(lib.oracle_silu_mul(_ptr(gu, _f64p), R, F2 // 2, _ptr(h, _f32p)), "silu_mul")
+    return h
+
+
+def moe_combine(rows: np.ndarray, pos: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y [T, H] fp64 = sum_j w[t, j] * rows[pos[t, j]] (pos < 0 skipped)."""
+    lib = _load()
+    rows = np.ascontiguousarray(rows, np.float32)
+    pos = np.ascontiguousarray(pos, np.int32)
+    w = np.ascontiguousarray(w, np.float32)
+    T, k = w.shape
+    H = rows.shape[1]
+    y = np.empty((T, H), np.float64)
+    _check(lib.oracle_moe_combine(_ptr(rows, _f32p), H, _ptr(pos, _i32p), _ptr(w, _f32p), T, k, _ptr(y, _f64p)),
+           "moe_combine")
+    return y
+
+
+def moe_block(x: np.ndarray, ids: np.ndarray, w: np.ndarray, E: int, a_gu, wgu_codes, wgu_scales, a_dn,
+              wdn_codes, wdn_scales, b: int, want: np.ndarray | None = None, threads: int | None = None):
+    """(y [T, H] fp64, dn_codes [T*k, F/2], dn_scales [T*k, F/32]) of the MoE
+    block for bf16 tokens x [T, H] (uint16 bits), top-k ids and weights
+    [T, k]; stacked gate/up weights [E, 2F, H/2] + [E, 2F, H/32], down
+    weights [E, H, F/2] + [E, H, F/32]. `want` (bool [T]) restricts the work
+    to some tokens; the other rows of y and of the down inputs stay zero."""
+    lib = _load()
+    x = np.ascontiguousarray(x, np.uint16)
+    T, H = x.shape
+    ids = np.ascontiguousarray(ids, np.int32)
+    w = np.ascontiguousarray(w, np.float32)
+    k = ids.shape[1]
+    gc = np.ascontiguousarray(wgu_codes, np.uint8)
+    gs = np.ascontiguousarray(wgu_scales, np.uint8)
+    dc = np.ascontiguousarray(wdn_codes, np.uint8)
+    ds = np.ascontiguousarray(wdn_scales, np.uint8)
+    F = 2 * dc.shape[2]
+    agu_keep, agp = _opt_f32(a_gu)
+    adn_keep, adp = _opt_f32(a_dn)
+    if want is None:
+        wp = _u8p()
+    else:
+        want = np.ascontiguousarray(want, np.uint8)
+        wp = _ptr(want, _u8p)
+    y = np.zeros((T, H), np.float64)
+    hc = np.zeros((T * k, F // 2), np.uint8)
+    hs = np.zeros((T * k, F // 32), np.uint8)
+    _check(lib.oracle_moe_block(x.ctypes.data, T, H, _ptr(ids, _i32p), _ptr(w, _f32p), k, E, agp, _ptr(gc, _u8p),
+                                _ptr(gs, _u8p), adp, _ptr(dc, _u8p), _ptr(ds, _u8p), F, b, wp, _ptr(hc, _u8p),
+                                _ptr(hs, _u8p), _ptr(y, _f64p), threads or default_threads()), "moe_block")
+    return y, hc, hs

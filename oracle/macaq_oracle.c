@@ -339,3 +339,181 @@ int oracle_linear_grouped(const uint16_t* x, const int32_t* off, int E, int64_t 
   }
   return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* MoE block around the grouped layer                                   */
+/* ------------------------------------------------------------------ */
+/*
+ * Sources: "MACaQ ..." (paper card, Abstract) treats every linear layer on
+ * its own; "MACaQ - Huawei open-sources a 4-bit quantizer ..." (What it is)
+ * lists MoE models among those it covers; "Huawei's MACaQ-R beats Unsloth's
+ * ..." (the "Changed tensors" item) names the routed experts' three
+ * projections, gate, up and down. The pages do not spell out the expert
+ * FFN; it is taken as the usual gated one, y = down(SiLU(gate x) * up x),
+ * with the token's top-k expert outputs summed with its routing weights.
+ * Readings (choices, not page text):
+ *   - routing order: the rows of the grouped layers are the (token, slot)
+ *     entries sorted by expert, ties by entry index i = t * k + j (stable);
+ *     an id outside [0, E) takes no row;
+ *   - gate and up projections of one expert are stacked as one weight
+ *     matrix [2F, H] whose rows alternate in blocks of 32: rows 64c .. 64c+31
+ *     are gate channels 32c .. 32c+31, rows 64c+32 .. 64c+63 up channels
+ *     32c .. 32c+31;
+ *   - h = SiLU(g) * u with SiLU(g) = g / (1 + exp(-g)), evaluated here in
+ *     fp64 on the fp64 GEMM outputs and rounded once to fp32; h then goes
+ *     through the down projection's own transform and MXFP4 exactly as an
+ *     activation row does (its multiplier a_dn[e], block b);
+ *   - each expert's down-projection output row is rounded to bf16 (it is a
+ *     layer output), and the combine sums w[t, j] * row over j = 0 .. k-1
+ *     in that order (fp64 here).
+ */
+
+/* Stable counting sort of the entries by expert. offsets [E+1]; row_token
+   [T*k] gets the token of each row (rows past offsets[E] are left alone);
+   pos [T*k] gets the row of each entry, or -1 for an id outside [0, E). */
+int oracle_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
+                     int32_t* pos) {
+  if (!ids || !offsets || !row_token || !pos || T < 0 || k < 1 || E < 1) return ORACLE_EINVAL;
+  const int64_t n = T * k;
+  int64_t row = 0;
+  for (int64_t i = 0; i < n; ++i) pos[i] = -1;
+  for (int e = 0; e < E; ++e) {
+    offsets[e] = (int32_t)row;
+    for (int64_t i = 0; i < n; ++i) {
+      if (ids[i] != e) continue;
+      row_token[row] = (int32_t)(i / k);
+      pos[i] = (int32_t)row;
+      ++row;
+    }
+  }
+  offsets[E] = (int32_t)row;
+  return ORACLE_OK;
+}
+
+static double silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* h[r, c] = RN32(SiLU(g) * u) from gate/up outputs stacked as above:
+   gu [R, 2F] (fp64), h [R, F] (fp32). F % 32 == 0. */
+int oracle_silu_mul(const double* gu, int64_t R, int64_t F, float* h) {
+  if (!gu || !h || R < 0 || F < 32 || F % 32 != 0) return ORACLE_EINVAL;
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t c = 0; c < F; ++c) {
+      const int64_t gcol = 64 * (c / 32) + c % 32;
+      const double g = gu[r * 2 * F + gcol], u = gu[r * 2 * F + gcol + 32];
+      h[r * F + c] = (float)(silu(g) * u);
+    }
+  return ORACLE_OK;
+}
+
+/* bf16 rounding (to nearest, ties to even) of a finite fp64 value, through
+   fp32 first as a device would round its fp32 result; returned as a float. */
+static float round_bf16_of(double v) {
+  float f = (float)v;
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  const uint32_t lsb = (u >> 16) & 1u;
+  u = (u + 0x7FFFu + lsb) & 0xFFFF0000u;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* y[t, :] = sum_j w[t, j] * rows[pos[t*k + j], :] (j ascending, fp64),
+   entries with pos < 0 skipped. rows [R, H] fp32 values. */
+int oracle_moe_combine(const float* rows, int64_t H, const int32_t* pos, const float* w, int64_t T, int k,
+                       double* y) {
+  if (!rows || !pos || !w || !y || H < 1 || T < 0 || k < 1) return ORACLE_EINVAL;
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t c = 0; c < H; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) {
+        const int32_t r = pos[t * k + j];
+        if (r < 0) continue;
+        acc += (double)w[t * k + j] * (double)rows[(int64_t)r * H + c];
+      }
+      y[t * H + c] = acc;
+    }
+  return ORACLE_OK;
+}
+
+/* The block for the tokens with want[t] != 0 (want == NULL: all tokens):
+   route, gather each row's token, gate/up through expert e's a_gu[e] and
+   stacked weights, SiLU * up, the down projection's transform and MXFP4
+   with a_dn[e], the down GEMM, bf16 rows, combine. Rows of tokens not
+   wanted are skipped (their y rows are left alone).
+   Optional outputs (NULL to skip): dn_codes [T*k, F/2], dn_scales
+   [T*k, F/32] (row-major, rows in routing order; rows of unwanted tokens
+   left alone). x [T, H] bf16 bits; wgu [E, 2F, H/2] + [E, 2F, H/32];
+   wdn [E, H, F/2] + [E, H, F/32]; y [T, H] fp64. */
+int oracle_moe_block(const uint16_t* x, int64_t T, int64_t H, const int32_t* ids, const float* w, int k, int E,
+                     const float* a_gu, const uint8_t* wgu_codes, const uint8_t* wgu_scales, const float* a_dn,
+                     const uint8_t* wdn_codes, const uint8_t* wdn_scales, int64_t F, int b, const uint8_t* want,
+                     uint8_t* dn_codes, uint8_t* dn_scales, double* y, int threads) {
+  if (!x || !ids || !w || !wgu_codes || !wgu_scales || !wdn_codes || !wdn_scales || !y || T < 1 || k < 1 ||
+      E < 1 || H < 32 || H % 32 != 0 || F < 32 || F % 32 != 0 || !valid_block(b))
+    return ORACLE_EINVAL;
+  if (b > 0 && (H % b != 0 || F % b != 0)) return ORACLE_EINVAL;
+  const int64_t n = T * k;
+  int32_t* off = (int32_t*)malloc((size_t)(E + 1) * sizeof(int32_t));
+  int32_t* row_token = (int32_t*)malloc((size_t)n * sizeof(int32_t));
+  int32_t* pos = (int32_t*)malloc((size_t)n * sizeof(int32_t));
+  float* rows_out = (float*)calloc((size_t)n * H, sizeof(float));
+  int rc = (off && row_token && pos && rows_out) ? ORACLE_OK : ORACLE_EINVAL;
+  if (rc == ORACLE_OK) rc = oracle_moe_route(ids, T, k, E, off, row_token, pos);
+  for (int e = 0; rc == ORACLE_OK && e < E; ++e) {
+    /* this expert's wanted rows */
+    int64_t cnt = 0;
+    for (int64_t r = off[e]; r < off[e + 1]; ++r)
+      if (!want || want[row_token[r]]) ++cnt;
+    if (cnt == 0) continue;
+    int64_t* idx = (int64_t*)malloc((size_t)cnt * sizeof(int64_t));
+    uint16_t* xe = (uint16_t*)malloc((size_t)cnt * H * sizeof(uint16_t));
+    double* gu = (double*)malloc((size_t)cnt * 2 * F * sizeof(double));
+    float* h = (float*)malloc((size_t)cnt * F * sizeof(float));
+    uint8_t* hc = (uint8_t*)malloc((size_t)cnt * F / 2);
+    uint8_t* hs = (uint8_t*)malloc((size_t)cnt * F / 32);
+    double* ye = (double*)malloc((size_t)cnt * H * sizeof(double));
+    if (!idx || !xe || !gu || !h || !hc || !hs || !ye) rc = ORACLE_EINVAL;
+    if (rc == ORACLE_OK) {
+      int64_t j = 0;
+      for (int64_t r = off[e]; r < off[e + 1]; ++r)
+        if (!want || want[row_token[r]]) idx[j++] = r;
+      for (int64_t i = 0; i < cnt; ++i) memcpy(xe + i * H, x + (int64_t)row_token[idx[i]] * H, (size_t)H * 2);
+      rc = oracle_linear(xe, cnt, H, H, a_gu ? a_gu + (int64_t)e * H : NULL, b,
+                         wgu_codes + (int64_t)e * 2 * F * (H / 2), wgu_scales + (int64_t)e * 2 * F * (H / 32),
+                         2 * F, gu, threads);
+    }
+    if (rc == ORACLE_OK) rc = oracle_silu_mul(gu, cnt, F, h);
+    if (rc == ORACLE_OK)
+      rc = oracle_quant_rows(h, 1, cnt, F, F, a_dn ? a_dn + (int64_t)e * F : NULL, b, hc, hs);
+    if (rc == ORACLE_OK)
+      rc = oracle_gemm_codes(hc, hs, cnt, wdn_codes + (int64_t)e * H * (F / 2),
+                             wdn_scales + (int64_t)e * H * (F / 32), H, F, ye, threads);
+    if (rc == ORACLE_OK) {
+      for (int64_t i = 0; i < cnt; ++i) {
+        const int64_t r = idx[i];
+        for (int64_t c = 0; c < H; ++c) rows_out[r * H + c] = round_bf16_of(ye[i * H + c]);
+        if (dn_codes) memcpy(dn_codes + r * (F / 2), hc + i * (F / 2), (size_t)F / 2);
+        if (dn_scales) memcpy(dn_scales + r * (F / 32), hs + i * (F / 32), (size_t)F / 32);
+      }
+    }
+    free(idx);
+    free(xe);
+    free(gu);
+    free(h);
+    free(hc);
+    free(hs);
+    free(ye);
+  }
+  if (rc == ORACLE_OK) {
+    for (int64_t t = 0; t < T; ++t) {
+      if (want && !want[t]) continue;
+      rc = oracle_moe_combine(rows_out, H, pos + t * k, w + t * k, 1, k, y + t * H);
+      if (rc != ORACLE_OK) break;
+    }
+  }
+  free(off);
+  free(row_token);
+  free(pos);
+  free(rows_out);
+  return rc;
+}
