@@ -190,6 +190,90 @@ macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t
                                   int64_t N, void* Y, macaq_dtype y_dtype, void* workspace,
                                   size_t workspace_bytes, macaq_stream_t stream);
 
+/*
+ * ---- MoE block around macaq_linear_grouped --------------------------------
+ *
+ * "MACaQ - Huawei open-sources a 4-bit quantizer ..." (What it is) lists MoE
+ * models among those the method covers, and "Huawei's MACaQ-R beats
+ * Unsloth's ..." ("Changed tensors") names each routed expert's gate, up and
+ * down projections; every one of them is a MACaQ layer with its own D and
+ * absorbed weights. The block computes, for T tokens with top-k experts
+ * ids[t, j] and routing weights w[t, j]:
+ *
+ *     y[t] = sum_j w[t, j] * bf16( Down_e( Q_dn( SiLU(Gate_e x_t) * Up_e x_t ) ) ),  e = ids[t, j]
+ *
+ * where Gate_e / Up_e / Down_e are MACaQ layers (Q_dn = the down layer's
+ * transform and MXFP4 with a_dn[e]). Readings where the pages are silent:
+ *   - the expert FFN is the gated one, SiLU(g) = g / (1 + exp(-g)), h in fp32;
+ *   - rows: the (t, j) entries sorted by expert, ties by i = t*k + j; an id
+ *     outside [0, E) takes no row and adds nothing to y;
+ *   - gate and up are one stacked weight [2F, H] per expert whose rows
+ *     alternate blocks of 32: rows 64c .. 64c+31 are gate channels 32c ..
+ *     32c+31, rows 64c+32 .. 64c+63 the matching up channels (prepare W_gate
+ *     and W_up with the same r, then interleave, or interleave the bf16 rows
+ *     and prepare once: row preparation is per row);
+ *   - each expert output row is rounded to bf16, and the combine sums over
+ *     j = 0 .. k-1 in fp32.
+ * Limits: 1 <= E <= 4096, 1 <= k, H and F multiples of 32 (and of b), T*k
+ * rows fit every packed operand under 2 GiB.
+ */
+
+/* Bytes of workspace that each MoE call below needs (the same figure serves
+   macaq_moe_gate_up, macaq_moe_down_combine and macaq_moe_block). */
+size_t macaq_moe_workspace_size(int64_t T, int32_t k, int32_t E, int64_t H, int64_t F);
+
+/*
+ * Routing: the stable sort of the T*k entries of ids by expert.
+ * ids: device int32 [T, k], 16-byte aligned; offsets: device int32 [E+1]
+ * (rows of expert e are [offsets[e], offsets[e+1])); row_token: device int32
+ * [T*k], the token of each row (rows past offsets[E] get token 0); pos:
+ * device int32 [T*k], the row of entry i = t*k + j, or -1.
+ */
+macaq_status macaq_moe_route(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* offsets,
+                             int32_t* row_token, int32_t* pos, macaq_stream_t stream);
+
+/*
+ * Gate/up of every routed row and the down projection's quantized input:
+ * row r gathers token row_token[r] of X, goes through expert e's a_gu[e] and
+ * stacked weights, and h = SiLU(gate) * up goes through a_dn[e] and the
+ * block-Hadamard of size b into MXFP4.
+ * X: device bf16 [T, ldx]; row_token, offsets: from macaq_moe_route (R = T*k
+ * rows); a_gu: device fp32 [E, H] or NULL (with b = 0); wgu_codes/scales: E
+ * prepared stacked weights [2F, H] one after another (MACAQ_GEMM_LAYOUT,
+ * expert e at e * macaq_packed_codes_bytes(2F, H)); a_dn: device fp32 [E, F]
+ * or NULL (with b = 0); dn_codes/dn_scales: device outputs, MACAQ_GEMM_LAYOUT
+ * of R rows x F (macaq_packed_*_bytes(R, F)); rows past offsets[E] are left
+ * alone. workspace: macaq_moe_workspace_size bytes, 256-byte aligned.
+ */
+macaq_status macaq_moe_gate_up(const void* X, int64_t T, int64_t H, int64_t ldx, int32_t k, const int32_t* row_token,
+                               const int32_t* offsets, int32_t E, const float* a_gu, int32_t b,
+                               const uint8_t* wgu_codes, const uint8_t* wgu_scales, int64_t F, const float* a_dn,
+                               uint8_t* dn_codes, uint8_t* dn_scales, void* workspace, size_t workspace_bytes,
+                               macaq_stream_t stream);
+
+/*
+ * Down projection of every routed row (bf16 rows in the workspace) and the
+ * weighted combine: y[t] = sum_j w[t, j] * row(pos[t*k + j]).
+ * dn_codes/dn_scales, offsets, pos: as above (R = T*k rows); wdn_codes/scales:
+ * E prepared down weights [H, F] one after another; w: device fp32 [T, k];
+ * Y: device [T, ldy] of y_dtype.
+ */
+macaq_status macaq_moe_down_combine(const uint8_t* dn_codes, const uint8_t* dn_scales, const int32_t* offsets,
+                                    const int32_t* pos, const float* w, int64_t T, int32_t k, int32_t E,
+                                    const uint8_t* wdn_codes, const uint8_t* wdn_scales, int64_t H, int64_t F,
+                                    void* Y, macaq_dtype y_dtype, int64_t ldy, void* workspace,
+                                    size_t workspace_bytes, macaq_stream_t stream);
+
+/*
+ * The whole block: macaq_moe_route, macaq_moe_gate_up and
+ * macaq_moe_down_combine in one call, their intermediates in the workspace.
+ */
+macaq_status macaq_moe_block(const void* X, int64_t T, int64_t H, int64_t ldx, const int32_t* ids, const float* w,
+                             int32_t k, int32_t E, const float* a_gu, const uint8_t* wgu_codes,
+                             const uint8_t* wgu_scales, const float* a_dn, const uint8_t* wdn_codes,
+                             const uint8_t* wdn_scales, int64_t F, int32_t b, void* Y, macaq_dtype y_dtype,
+                             int64_t ldy, void* workspace, size_t workspace_bytes, macaq_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

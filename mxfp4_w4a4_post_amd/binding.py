@@ -45,12 +45,20 @@ _SIGNATURES = {
     "macaq_linear_grouped_workspace_size": (_sz, [_i64, _i32, _i64, _i64]),
     "macaq_linear_grouped": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _i64, _vp,
                                             ctypes.c_int, _vp, _sz, _vp]),
+    "macaq_moe_workspace_size": (_sz, [_i64, _i32, _i32, _i64, _i64]),
+    "macaq_moe_route": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "macaq_moe_gate_up": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i64,
+                                         _vp, _vp, _vp, _vp, _sz, _vp]),
+    "macaq_moe_down_combine": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _i64, _i64, _vp,
+                                              ctypes.c_int, _i64, _vp, _sz, _vp]),
+    "macaq_moe_block": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _i64, _i32, _vp, ctypes.c_int, _i64, _vp, _sz, _vp]),
 }
 
 
 class Packed(NamedTuple):
-    """An MXFP4 operand in the GEMM layout: `rows` x `K` elements (padded to 64
-    rows and a multiple of 128 in K inside the buffers). codes / scales are
+    """An MXFP4 operand in the GEMM layout: `rows` x `K` elements (padded to 32
+    rows and a multiple of 256 in K inside the buffers). codes / scales are
     uint8 tensors of packed_codes_bytes / packed_scales_bytes bytes (with a
     leading expert dimension for grouped weights)."""
     codes: torch.Tensor
@@ -284,3 +292,139 @@ def prepare_layer(w: torch.Tensor, xcal: torch.Tensor | None, b: int) -> Layer:
     s = calibrate(xcal)
     a, r = make_multipliers(s, b)
     return Layer(a, r, b, prepare_weights(w, r, b), s)
+
+
+# ---- MoE block around the grouped layer -----------------------------------
+
+def stack_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor:
+    """[.., F, H] gate and up weights -> [.., 2F, H] with alternating blocks of
+    32 rows (gate channels 32c .. 32c+31, then the matching up channels), the
+    layout the MoE gate/up GEMM's epilogue expects."""
+    assert w_gate.shape == w_up.shape and w_gate.shape[-2] % 32 == 0
+    F, H = w_gate.shape[-2:]
+    lead = w_gate.shape[:-2]
+    g = w_gate.reshape(*lead, F // 32, 1, 32, H)
+    u = w_up.reshape(*lead, F // 32, 1, 32, H)
+    return torch.cat([g, u], dim=-3).reshape(*lead, 2 * F, H).contiguous()
+
+
+def moe_workspace_size(T: int, k: int, E: int, H: int, F: int) -> int:
+    return int(load_library().macaq_moe_workspace_size(T, k, E, H, F))
+
+
+def moe_route(ids: torch.Tensor, E: int):
+    """(offsets [E+1], row_token [T*k], pos [T*k]) of the stable sort of the
+    top-k entries ids [T, k] (int32) by expert."""
+    _need_cuda(ids)
+    assert ids.dtype == torch.int32 and ids.dim() == 2 and ids.is_contiguous()
+    T, k = ids.shape
+    dev = ids.device
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    pos = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    _check(load_library().macaq_moe_route(_ptr(ids), T, k, E, _ptr(offsets), _ptr(row_token), _ptr(pos),
+                                          _stream(ids)), "macaq_moe_route")
+    return offsets, row_token[:T * k], pos[:T * k]
+
+
+def moe_gate_up(x: torch.Tensor, k: int, row_token: torch.Tensor, offsets: torch.Tensor, a_gu, b: int, wgu: Packed,
+                a_dn, out: Packed | None = None, workspace: torch.Tensor | None = None) -> Packed:
+    """The down projection's MXFP4 input (GEMM layout, T*k rows x F) of every
+    routed row: gathered gate/up through a_gu[e] and the stacked weights, then
+    SiLU(gate) * up through a_dn[e] and the block-Hadamard."""
+    _need_cuda(x, row_token, offsets, a_gu, a_dn, wgu.codes, wgu.scales)
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    T, H = x.shape
+    E = offsets.numel() - 1
+    F = wgu.rows // 2
+    R = T * k
+    if out is None:
+        out = Packed(torch.empty(packed_codes_bytes(R, F), dtype=torch.uint8, device=x.device),
+                     torch.empty(packed_scales_bytes(R, F), dtype=torch.uint8, device=x.device), R, F)
+    ws = _workspace(moe_workspace_size(T, k, E, H, F), x.device, workspace)
+    _check(load_library().macaq_moe_gate_up(_ptr(x), T, H, x.stride(0), k, _ptr(row_token), _ptr(offsets), E,
+                                            _ptr(a_gu), b, _ptr(wgu.codes), _ptr(wgu.scales), F, _ptr(a_dn),
+                                            _ptr(out.codes), _ptr(out.scales), _ptr(ws), ws.numel(), _stream(x)),
+           "macaq_moe_gate_up")
+    return out
+
+
+def moe_down_combine(dn: Packed, offsets: torch.Tensor, pos: torch.Tensor, w: torch.Tensor, wdn: Packed,
+                     out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y [T, H] = sum_j w[t, j] * bf16(down_e(row pos[t*k + j])) for routing
+    weights w [T, k] (fp32)."""
+    _need_cuda(dn.codes, offsets, pos, w, wdn.codes)
+    assert w.dtype == torch.float32 and w.is_contiguous()
+    T, k = w.shape
+    E = offsets.numel() - 1
+    H, F = wdn.rows, wdn.K
+    y = out if out is not None else torch.empty(T, H, dtype=out_dtype, device=w.device)
+    ws = _workspace(moe_workspace_size(T, k, E, H, F), w.device, workspace)
+    _check(load_library().macaq_moe_down_combine(_ptr(dn.codes), _ptr(dn.scales), _ptr(offsets), _ptr(pos), _ptr(w),
+                                                 T, k, E, _ptr(wdn.codes), _ptr(wdn.scales), H, F, _ptr(y),
+                                                 _dtype_code(y.dtype), y.stride(0), _ptr(ws), ws.numel(),
+                                                 _stream(w)), "macaq_moe_down_combine")
+    return y
+
+
+def moe_block(x: torch.Tensor, ids: torch.Tensor, w: torch.Tensor, a_gu, wgu: Packed, a_dn, wdn: Packed, b: int,
+              out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The whole MoE block for bf16 tokens x [T, H], top-k ids [T, k] (int32)
+    and routing weights w [T, k] (fp32)."""
+    _need_cuda(x, ids, w, a_gu, a_dn, wgu.codes, wdn.codes)
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    assert ids.dtype == torch.int32 and ids.is_contiguous() and w.dtype == torch.float32 and w.is_contiguous()
+    T, H = x.shape
+    k = ids.shape[1]
+    E = wgu.codes.shape[0]
+    F = wgu.rows // 2
+    y = out if out is not None else torch.empty(T, H, dtype=out_dtype, device=x.device)
+    ws = _workspace(moe_workspace_size(T, k, E, H, F), x.device, workspace)
+    _check(load_library().macaq_moe_block(_ptr(x), T, H, x.stride(0), _ptr(ids), _ptr(w), k, E, _ptr(a_gu),
+                                          _ptr(wgu.codes), _ptr(wgu.scales), _ptr(a_dn), _ptr(wdn.codes),
+                                          _ptr(wdn.scales), F, b, _ptr(y), _dtype_code(y.dtype), y.stride(0),
+                                          _ptr(ws), ws.numel(), _stream(x)), "macaq_moe_block")
+    return y
+
+
+class MoELayer:
+    """A prepared MoE block: per-expert multipliers a_gu [E, H], a_dn [E, F] and
+    the stacked gate/up and down weights of every expert."""
+
+    def __init__(self, a_gu, wgu: Packed, a_dn, wdn: Packed, b: int):
+        self.a_gu, self.wgu, self.a_dn, self.wdn, self.b = a_gu, wgu, a_dn, wdn, b
+
+    def __call__(self, x, ids, w, out_dtype=torch.bfloat16, out=None, workspace=None):
+        return moe_block(x, ids, w, self.a_gu, self.wgu, self.a_dn, self.wdn, self.b, out_dtype, out, workspace)
+
+
+def prepare_moe(w_gate: torch.Tensor, w_up: torch.Tensor, w_dn: torch.Tensor, xcal_gu: torch.Tensor | None,
+                xcal_dn: torch.Tensor | None, b: int) -> MoELayer:
+    """Per expert e: calibrate the gate/up input on xcal_gu[e] and the down
+    input on xcal_dn[e], fold c_b into the multipliers, and prepare the
+    stacked gate/up [2F, H] and down [H, F] weights. With no calibration rows
+    and b == 0 the block is plain MXFP4."""
+    E, F, H = w_gate.shape
+    dev = w_gate.device
+    wgu_rows = stack_gate_up(w_gate, w_up)
+    wgu = empty_grouped_weights(E, 2 * F, H, dev)
+    wdn = empty_grouped_weights(E, H, F, dev)
+    plain = xcal_gu is None
+    if plain and b != 0:
+        raise ValueError("a Hadamard block without calibration rows is not a MACaQ layer")
+    a_gu = None if plain else torch.empty(E, H, dtype=torch.float32, device=dev)
+    a_dn = None if plain else torch.empty(E, F, dtype=torch.float32, device=dev)
+    for e in range(E):
+        if plain:
+            prepare_weights(wgu_rows[e], None, 0, out=expert(wgu, e))
+            prepare_weights(w_dn[e], None, 0, out=expert(wdn, e))
+            continue
+        a, r = make_multipliers(calibrate(xcal_gu[e]), b)
+        a_gu[e] = a
+        prepare_weights(wgu_rows[e], r, b, out=expert(wgu, e))
+        a, r = make_multipliers(calibrate(xcal_dn[e]), b)
+        a_dn[e] = a
+        prepare_weights(w_dn[e], r, b, out=expert(wdn, e))
+    return MoELayer(a_gu, wgu, a_dn, wdn, b)

@@ -100,6 +100,127 @@ macaq_status check_out(const void* Y, macaq_dtype dt, int64_t N, int64_t ldy, co
   return MACAQ_OK;
 }
 
+// Workspace of the MoE calls, R = T*k rows: routing arrays, the tile map of
+// the grouped GEMMs, the gathered gate/up input, the down input and the bf16
+// expert rows.
+struct MoeWs {
+  size_t offsets, row_token, pos, map, agu_codes, agu_scales, dn_codes, dn_scales, rows, total;
+  int64_t max_mtiles;
+};
+
+MoeWs moe_ws(int64_t T, int32_t k, int32_t E, int64_t H, int64_t F) {
+  const int64_t R = T * k;
+  const GemmPlan p = plan_gemm_grouped(R, E, 2 * F, H);
+  MoeWs w;
+  w.max_mtiles = (R + p.bm - 1) / p.bm + E;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t here = at;
+    at += round_up(bytes, kWsAlign);
+    return here;
+  };
+  w.offsets = take((size_t)(E + 1) * 4);
+  w.row_token = take((size_t)R * 4);
+  w.pos = take((size_t)R * 4);
+  w.map = take((size_t)w.max_mtiles * 2 * 4);
+  w.agu_codes = take((size_t)tiled_codes_bytes(R, H));
+  w.agu_scales = take((size_t)tiled_scales_bytes(R, H));
+  w.dn_codes = take((size_t)tiled_codes_bytes(R, F));
+  w.dn_scales = take((size_t)tiled_scales_bytes(R, F));
+  w.rows = take((size_t)R * H * 2);
+  w.total = at;
+  return w;
+}
+
+macaq_status check_moe_shape(int64_t T, int32_t k, int32_t E, int64_t H, int64_t F, int32_t b, const char* who) {
+  if (T < 0) return fail(MACAQ_EINVAL, "%s: T = %lld < 0", who, (long long)T);
+  if (k < 1) return fail(MACAQ_EINVAL, "%s: k = %d < 1", who, k);
+  if (E < 1 || E > kMaxExperts) return fail(MACAQ_EINVAL, "%s: E = %d not in [1, %d]", who, E, kMaxExperts);
+  if (H < 32 || H % 32 != 0) return fail(MACAQ_EINVAL, "%s: H = %lld is not a positive multiple of 32", who, (long long)H);
+  if (F < 32 || F % 32 != 0) return fail(MACAQ_EINVAL, "%s: F = %lld is not a positive multiple of 32", who, (long long)F);
+  if (!valid_block(b)) return fail(MACAQ_EINVAL, "%s: Hadamard block %d not in {0, 32, 64, 128}", who, b);
+  if (b > 0 && (H % b != 0 || F % b != 0)) return fail(MACAQ_EINVAL, "%s: H and F must be multiples of b = %d", who, b);
+  const int64_t R = T * (int64_t)k;
+  if (R > 0x7FFFFFFF) return fail(MACAQ_EINVAL, "%s: T*k = %lld rows exceed int32", who, (long long)R);
+  if (!operand_fits(R, H) || !operand_fits(R, F) || !operand_fits(2 * F, H) || !operand_fits(H, F))
+    return fail(MACAQ_EINVAL, "%s: packed operand over 2 GiB", who);
+  return MACAQ_OK;
+}
+
+hipError_t moe_gate_up_launch(const void* X, int64_t T, int64_t H, int64_t ldx, int32_t k, const int32_t* row_token,
+                              const int32_t* offsets, int32_t E, const float* a_gu, int32_t b,
+                              const uint8_t* wgu_codes, const uint8_t* wgu_scales, int64_t F, const float* a_dn,
+                              uint8_t* dn_codes, uint8_t* dn_scales, uint8_t* ws, const MoeWs& w, bool build_map,
+                              hipStream_t s) {
+  const int64_t R = T * k;
+  QuantArgs q{};
+  q.x = X;
+  q.M = R;
+  q.K = H;
+  q.ldx = ldx;
+  q.mult = a_gu;
+  q.offsets = a_gu ? offsets : nullptr;
+  q.E = E;
+  q.codes = ws + w.agu_codes;
+  q.scales = ws + w.agu_scales;
+  q.tiled = true;
+  q.kpad = pad_k(H);
+  q.gather = row_token;
+  q.src_rows = T;
+  hipError_t e = launch_quant_rows(q, b, false, s);
+  if (e != hipSuccess) return e;
+  GemmArgs g{};
+  g.a_codes = q.codes;
+  g.a_scales = q.scales;
+  g.b_codes = wgu_codes;
+  g.b_scales = wgu_scales;
+  g.M = R;
+  g.N = 2 * F;
+  g.K = H;
+  g.splits = 1;
+  g.offsets = offsets;
+  g.tile_map = reinterpret_cast<int32_t*>(ws + w.map);
+  g.E = E;
+  g.max_mtiles = w.max_mtiles;
+  g.map_ready = !build_map;
+  g.swiglu = true;
+  g.q_codes = dn_codes;
+  g.q_scales = dn_scales;
+  g.q_mult = a_dn;
+  g.q_F = F;
+  g.q_b = b;
+  return launch_gemm_grouped(g, plan_gemm_grouped(R, E, 2 * F, H), s);
+}
+
+hipError_t moe_down_combine_launch(const uint8_t* dn_codes, const uint8_t* dn_scales, const int32_t* offsets,
+                                   const int32_t* pos, const float* w_route, int64_t T, int32_t k, int32_t E,
+                                   const uint8_t* wdn_codes, const uint8_t* wdn_scales, int64_t H, int64_t F,
+                                   void* Y, macaq_dtype y_dtype, int64_t ldy, uint8_t* ws, const MoeWs& w,
+                                   bool build_map, hipStream_t s) {
+  const int64_t R = T * k;
+  uint16_t* rows = reinterpret_cast<uint16_t*>(ws + w.rows);
+  GemmArgs g{};
+  g.a_codes = dn_codes;
+  g.a_scales = dn_scales;
+  g.b_codes = wdn_codes;
+  g.b_scales = wdn_scales;
+  g.M = R;
+  g.N = H;
+  g.K = F;
+  g.y = rows;
+  g.ldy = H;
+  g.y_bf16 = true;
+  g.splits = 1;
+  g.offsets = offsets;
+  g.tile_map = reinterpret_cast<int32_t*>(ws + w.map);
+  g.E = E;
+  g.max_mtiles = w.max_mtiles;
+  g.map_ready = !build_map;
+  hipError_t e = launch_gemm_grouped(g, plan_gemm_grouped(R, E, H, F), s);
+  if (e != hipSuccess) return e;
+  return launch_moe_combine(rows, H, pos, w_route, T, k, Y, y_dtype == MACAQ_BF16, ldy, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -372,6 +493,121 @@ macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t
   g.max_mtiles = max_mtiles;
   e = launch_gemm_grouped(g, p, s);
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_linear_grouped GEMM launch");
+}
+
+size_t macaq_moe_workspace_size(int64_t T, int32_t k, int32_t E, int64_t H, int64_t F) {
+  if (T <= 0 || k < 1 || E < 1 || H < 32 || F < 32) return 0;
+  return moe_ws(T, k, E, H, F).total;
+}
+
+macaq_status macaq_moe_route(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* offsets,
+                             int32_t* row_token, int32_t* pos, macaq_stream_t stream) {
+  const char* who = "macaq_moe_route";
+  if (T < 0 || k < 1) return fail(MACAQ_EINVAL, "%s: T = %lld, k = %d", who, (long long)T, k);
+  if (E < 1 || E > kMaxExperts) return fail(MACAQ_EINVAL, "%s: E = %d not in [1, %d]", who, E, kMaxExperts);
+  if (T * (int64_t)k > 0x7FFFFFFF) return fail(MACAQ_EINVAL, "%s: T*k exceeds int32", who);
+  if (!ids || !offsets || !row_token || !pos) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (!aligned(ids, 4) || !aligned(offsets, 4) || !aligned(row_token, 4) || !aligned(pos, 4))
+    return fail(MACAQ_EALIGN, "%s: int32 arrays must be 4-byte aligned", who);
+  macaq_status st = check_device();
+  if (st != MACAQ_OK) return st;
+  hipError_t e = launch_moe_route(ids, T, k, E, offsets, row_token, pos, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_route launch");
+}
+
+macaq_status macaq_moe_gate_up(const void* X, int64_t T, int64_t H, int64_t ldx, int32_t k, const int32_t* row_token,
+                               const int32_t* offsets, int32_t E, const float* a_gu, int32_t b,
+                               const uint8_t* wgu_codes, const uint8_t* wgu_scales, int64_t F, const float* a_dn,
+                               uint8_t* dn_codes, uint8_t* dn_scales, void* workspace, size_t workspace_bytes,
+                               macaq_stream_t stream) {
+  const char* who = "macaq_moe_gate_up";
+  macaq_status st = check_moe_shape(T, k, E, H, F, b, who);
+  if (st != MACAQ_OK) return st;
+  if (ldx < H) return fail(MACAQ_EINVAL, "%s: ldx = %lld < H", who, (long long)ldx);
+  if (!X || !row_token || !offsets || !wgu_codes || !wgu_scales || !dn_codes || !dn_scales)
+    return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if ((!a_gu || !a_dn) && b != 0) return fail(MACAQ_EINVAL, "%s: a_gu and a_dn are required when b > 0", who);
+  if (!aligned(X, 16) || ldx % 8 != 0 || (a_gu && !aligned(a_gu, 16)) || (a_dn && !aligned(a_dn, 4)) ||
+      !aligned(wgu_codes, 16) || !aligned(wgu_scales, 16) || !aligned(dn_codes, 16) || !aligned(dn_scales, 4) ||
+      !aligned(row_token, 4) || !aligned(offsets, 4))
+    return fail(MACAQ_EALIGN, "%s: X, a_gu, weights and dn_codes 16-byte aligned, ldx a multiple of 8", who);
+  if (T == 0) return MACAQ_OK;
+  const MoeWs w = moe_ws(T, k, E, H, F);
+  if (!workspace || workspace_bytes < w.total || !aligned(workspace, kWsAlign))
+    return fail(MACAQ_EWORKSPACE, "%s: need %zu workspace bytes, 256-byte aligned", who, w.total);
+  st = check_device();
+  if (st != MACAQ_OK) return st;
+  hipError_t e = moe_gate_up_launch(X, T, H, ldx, k, row_token, offsets, E, a_gu, b, wgu_codes, wgu_scales, F, a_dn,
+                                    dn_codes, dn_scales, static_cast<uint8_t*>(workspace), w, true,
+                                    reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_gate_up launch");
+}
+
+macaq_status macaq_moe_down_combine(const uint8_t* dn_codes, const uint8_t* dn_scales, const int32_t* offsets,
+                                    const int32_t* pos, const float* w_route, int64_t T, int32_t k, int32_t E,
+                                    const uint8_t* wdn_codes, const uint8_t* wdn_scales, int64_t H, int64_t F,
+                                    void* Y, macaq_dtype y_dtype, int64_t ldy, void* workspace,
+                                    size_t workspace_bytes, macaq_stream_t stream) {
+  const char* who = "macaq_moe_down_combine";
+  macaq_status st = check_moe_shape(T, k, E, H, F, 0, who);
+  if (st != MACAQ_OK) return st;
+  if (!dn_codes || !dn_scales || !offsets || !pos || !w_route || !wdn_codes || !wdn_scales)
+    return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  st = check_out(Y, y_dtype, H, ldy, who);
+  if (st != MACAQ_OK) return st;
+  if (!aligned(dn_codes, 16) || !aligned(dn_scales, 16) || !aligned(wdn_codes, 16) || !aligned(wdn_scales, 16) ||
+      !aligned(offsets, 4) || !aligned(pos, 4) || !aligned(w_route, 4))
+    return fail(MACAQ_EALIGN, "%s: packed operands 16-byte aligned, int32/fp32 arrays 4-byte aligned", who);
+  if (T == 0) return MACAQ_OK;
+  const MoeWs w = moe_ws(T, k, E, H, F);
+  if (!workspace || workspace_bytes < w.total || !aligned(workspace, kWsAlign))
+    return fail(MACAQ_EWORKSPACE, "%s: need %zu workspace bytes, 256-byte aligned", who, w.total);
+  st = check_device();
+  if (st != MACAQ_OK) return st;
+  hipError_t e = moe_down_combine_launch(dn_codes, dn_scales, offsets, pos, w_route, T, k, E, wdn_codes, wdn_scales,
+                                         H, F, Y, y_dtype, ldy, static_cast<uint8_t*>(workspace), w, true,
+                                         reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_down_combine launch");
+}
+
+macaq_status macaq_moe_block(const void* X, int64_t T, int64_t H, int64_t ldx, const int32_t* ids, const float* w_route,
+                             int32_t k, int32_t E, const float* a_gu, const uint8_t* wgu_codes,
+                             const uint8_t* wgu_scales, const float* a_dn, const uint8_t* wdn_codes,
+                             const uint8_t* wdn_scales, int64_t F, int32_t b, void* Y, macaq_dtype y_dtype,
+                             int64_t ldy, void* workspace, size_t workspace_bytes, macaq_stream_t stream) {
+  const char* who = "macaq_moe_block";
+  macaq_status st = check_moe_shape(T, k, E, H, F, b, who);
+  if (st != MACAQ_OK) return st;
+  if (ldx < H) return fail(MACAQ_EINVAL, "%s: ldx = %lld < H", who, (long long)ldx);
+  if (!X || !ids || !w_route || !wgu_codes || !wgu_scales || !wdn_codes || !wdn_scales)
+    return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if ((!a_gu || !a_dn) && b != 0) return fail(MACAQ_EINVAL, "%s: a_gu and a_dn are required when b > 0", who);
+  st = check_out(Y, y_dtype, H, ldy, who);
+  if (st != MACAQ_OK) return st;
+  if (!aligned(X, 16) || ldx % 8 != 0 || (a_gu && !aligned(a_gu, 16)) || (a_dn && !aligned(a_dn, 4)) ||
+      !aligned(wgu_codes, 16) || !aligned(wgu_scales, 16) || !aligned(wdn_codes, 16) || !aligned(wdn_scales, 16) ||
+      !aligned(ids, 4) || !aligned(w_route, 4))
+    return fail(MACAQ_EALIGN, "%s: X, a_gu and weights 16-byte aligned, ldx a multiple of 8", who);
+  if (T == 0) return MACAQ_OK;
+  const MoeWs w = moe_ws(T, k, E, H, F);
+  if (!workspace || workspace_bytes < w.total || !aligned(workspace, kWsAlign))
+    return fail(MACAQ_EWORKSPACE, "%s: need %zu workspace bytes, 256-byte aligned", who, w.total);
+  st = check_device();
+  if (st != MACAQ_OK) return st;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + w.offsets);
+  int32_t* row_token = reinterpret_cast<int32_t*>(ws + w.row_token);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + w.pos);
+  hipError_t e = launch_moe_route(ids, T, k, E, offsets, row_token, pos, s);
+  if (e != hipSuccess) return hip_fail(e, "macaq_moe_block routing launch");
+  e = moe_gate_up_launch(X, T, H, ldx, k, row_token, offsets, E, a_gu, b, wgu_codes, wgu_scales, F, a_dn,
+                         ws + w.dn_codes, ws + w.dn_scales, ws, w, true, s);
+  if (e != hipSuccess) return hip_fail(e, "macaq_moe_block gate/up launch");
+  // both grouped GEMMs use the same tile size, so the map built above serves the down GEMM
+  e = moe_down_combine_launch(ws + w.dn_codes, ws + w.dn_scales, offsets, pos, w_route, T, k, E, wdn_codes,
+                              wdn_scales, H, F, Y, y_dtype, ldy, ws, w, false, s);
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_block down/combine launch");
 }
 
 }  // extern "C"

@@ -65,6 +65,8 @@ struct QuantArgs {
   uint8_t* scales;       // [M, K/32] row-major, or the GEMM layout
   bool tiled;            // write the GEMM layout (with its zero padding)
   int64_t kpad;          // pad_k(K)
+  const int32_t* gather;  // optional: row r reads x row gather[r] (clamped to [0, src_rows))
+  int64_t src_rows;
 };
 
 hipError_t launch_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx, float* s, hipStream_t stream);
@@ -88,6 +90,16 @@ struct GemmArgs {
   int32_t* tile_map;        // workspace: per m-tile (expert, first row)
   int E;
   int64_t max_mtiles;
+  bool map_ready;           // grouped: tile_map already holds the map of these offsets
+  // grouped SwiGLU epilogue (MoE gate/up): instead of Y, write the down
+  // projection's MXFP4 input h = SiLU(gate) * up through its multiplier and
+  // block-Hadamard; B's rows alternate blocks of 32 gate and 32 up rows
+  bool swiglu;
+  uint8_t* q_codes;         // GEMM layout [M, q_F]
+  uint8_t* q_scales;
+  const float* q_mult;      // [E, q_F] or nullptr
+  int64_t q_F;              // channels (N = 2 q_F)
+  int q_b;                  // Hadamard block of the down input
   // set by the launcher: outputs may be stored as 4-element vectors
   bool vec_y, vec_partial, vec16_y;
 };
@@ -103,5 +115,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 GemmPlan plan_gemm_grouped(int64_t T, int E, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmArgs& g, const GemmPlan& p, hipStream_t stream);
 hipError_t launch_gemm_grouped(const GemmArgs& g, const GemmPlan& p, hipStream_t stream);
+
+// MoE block: routing (one workgroup per expert, LDS histogram of at most
+// kMaxExperts experts) and the weighted combine of bf16 expert rows.
+constexpr int kMaxExperts = 4096;
+hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
+                            int32_t* pos, hipStream_t stream);
+hipError_t launch_moe_combine(const uint16_t* rows, int64_t H, const int32_t* pos, const float* w, int64_t T, int k,
+                              void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
 
 }  // namespace macaq

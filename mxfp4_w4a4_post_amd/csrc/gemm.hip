@@ -23,7 +23,7 @@
 // each wave reads its MFMA fragments back one half-step ahead of their use.
 // LDS holds only the activations, with the layout's fragment order, so every
 // LDS access of a wave is 64 consecutive 16-byte (or 4-byte) words.
-#include "common.hpp"
+#include "mx_lane.hpp"
 
 namespace macaq {
 namespace {
@@ -262,13 +262,110 @@ __device__ __forceinline__ void store_bf16_staged(const Acc<C>& acc, uint16_t* y
   }
 }
 
+// MoE gate/up epilogue: the tile's B rows alternate 32 gate and 32 up rows,
+// so wave w holds, per 32-row group of A, gate and up of channels
+// c0 + 32w .. c0 + 32w + 31 (c0 = n0 / 2) in matching registers. It writes
+// h = SiLU(gate) * up (fp32) to LDS as [BM rows][BN/2 channels], then quads
+// of lanes take the 4 channel groups of a row: multiply by the down
+// projection's multipliers, block-Hadamard, MXFP4, and store the codes and
+// scale in the GEMM layout of the down input. "MACaQ - Huawei open-sources a
+// 4-bit quantizer ..." (What it is) covers MoE models; the gated form of the
+// expert FFN is a reading.
+constexpr int swiglu_pitch(int bn) { return (bn / 2) * 4 + 16; }
+template <class C>
+constexpr int swiglu_lds() {
+  return C::BM * swiglu_pitch(C::BN) + (C::BN / 2) * 4;
+}
+
+template <class C, int B>
+__device__ __forceinline__ void store_swiglu_quant(const Acc<C>& acc, const GemmArgs& g, const TileCoord& tc,
+                                                   int expert, int wave, int lane, uint8_t* smem) {
+  static_assert(C::FN == 2, "a wave holds 32 gate and 32 up rows");
+  constexpr int CH = C::BN / 2;  // channels of the tile
+  constexpr int GR = CH / 32;    // channel groups per row
+  constexpr int PITCH = swiglu_pitch(C::BN);
+  static_assert(GR == 4 && (C::BM * GR) % NT == 0, "a quad of lanes per row");
+  float* mult = reinterpret_cast<float*>(smem + C::BM * PITCH);
+  const int tid = threadIdx.x;
+  const int64_t c0 = tc.n0 / 2;
+  if (tid < CH) {
+    const int64_t ch = c0 + tid;
+    mult[tid] = (g.q_mult && ch < g.q_F) ? g.q_mult[(int64_t)expert * g.q_F + ch] : 1.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float gt = acc.v[i][0][4 * q + e], up = acc.v[i][1][4 * q + e];
+        h[e] = gt / (1.0f + expf(-gt)) * up;
+      }
+      const int row = i * 32 + (lane & 31), ch = wave * 32 + 8 * q + 4 * (lane >> 5);
+      lds_at<float4>(smem, row * PITCH + ch * 4) = make_float4(h[0], h[1], h[2], h[3]);
+    }
+  __syncthreads();
+  const int64_t kpad = pad_k(g.q_F);
+#pragma unroll
+  for (int rd = 0; rd < C::BM * GR / NT; ++rd) {
+    const int item = rd * NT + tid;
+    const int row = item / GR, grp = item % GR;
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 hv = lds_at<float4>(smem, row * PITCH + (grp * 32 + 4 * j) * 4);
+      const float4 mv = *reinterpret_cast<const float4*>(mult + grp * 32 + 4 * j);
+      v[4 * j] = hv.x * mv.x;
+      v[4 * j + 1] = hv.y * mv.y;
+      v[4 * j + 2] = hv.z * mv.z;
+      v[4 * j + 3] = hv.w * mv.w;
+    }
+    fwht_lane<B>(v, grp);
+    uint4 codes;
+    const int sc = mx_encode(v, codes);
+    const int64_t m = tc.m0 + row, ch = c0 + grp * 32;
+    if (m < tc.m_end && ch < g.q_F) {
+      *reinterpret_cast<uint4*>(g.q_codes + tiled_code_offset(m, ch, kpad)) = codes;
+      g.q_scales[tiled_scale_offset(m, ch, kpad)] = (uint8_t)sc;
+    }
+  }
+  // the last tile along N also writes the zero padding of K up to kpad
+  if (tc.n0 + C::BN >= g.N) {
+    const int g0 = (int)(g.q_F / 32), g1 = (int)(kpad / 32);
+    for (int item = tid; item < C::BM * (g1 - g0); item += NT) {
+      const int row = item / (g1 - g0), grp = g0 + item % (g1 - g0);
+      const int64_t m = tc.m0 + row;
+      if (m < tc.m_end) {
+        *reinterpret_cast<uint4*>(g.q_codes + tiled_code_offset(m, (int64_t)grp * 32, kpad)) = make_uint4(0, 0, 0, 0);
+        g.q_scales[tiled_scale_offset(m, (int64_t)grp * 32, kpad)] = 0;
+      }
+    }
+  }
+}
+
 // Output modes, chosen on the host per launch: fp32 to Y, bf16 to Y (plain
-// stores), bf16 to Y staged through LDS (aligned rows), fp32 split-K partials.
-enum OutMode { kOutF32 = 0, kOutBf16 = 1, kOutBf16Staged = 2, kOutPartial = 3 };
+// stores), bf16 to Y staged through LDS (aligned rows), fp32 split-K partials,
+// and the MoE gate/up epilogue with a Hadamard block of 0, 32, 64 or 128.
+enum OutMode {
+  kOutF32 = 0,
+  kOutBf16 = 1,
+  kOutBf16Staged = 2,
+  kOutPartial = 3,
+  kOutSwiGlu0 = 4,
+  kOutSwiGlu32 = 5,
+  kOutSwiGlu64 = 6,
+  kOutSwiGlu128 = 7
+};
 
 template <class C, int MODE>
-__device__ __forceinline__ void store_out(const Acc<C>& acc, const GemmArgs& g, const TileCoord& tc, int wave,
-                                          int lane, uint8_t* smem) {
+__device__ __forceinline__ void store_out(const Acc<C>& acc, const GemmArgs& g, const TileCoord& tc, int expert,
+                                          int wave, int lane, uint8_t* smem) {
+  if constexpr (MODE >= kOutSwiGlu0) {
+    constexpr int B = MODE == kOutSwiGlu0 ? 0 : (32 << (MODE - kOutSwiGlu32));
+    store_swiglu_quant<C, B>(acc, g, tc, expert, wave, lane, smem);
+    return;
+  }
   const int64_t m0 = tc.m0, n0 = tc.n0 + wave * C::WN;
   const int64_t m_lim = tc.m_end - m0, n_lim = g.N - n0;
   if (n_lim <= 0) return;
@@ -540,6 +637,7 @@ struct TileRef {
   TileCoord tc;
   const uint8_t* bc;
   const uint8_t* bs;
+  int expert;
 };
 
 template <class C, bool GROUPED>
@@ -558,6 +656,7 @@ __device__ __forceinline__ bool tile_at(const GemmArgs& g, int64_t t, TileRef& r
     r.tc.split = 0;
     r.tc.kt_begin = 0;
     r.tc.kt_end = KT;
+    r.expert = expert;
     r.bc = g.b_codes + (int64_t)expert * tiled_codes_bytes(g.N, g.K);
     r.bs = g.b_scales + (int64_t)expert * tiled_scales_bytes(g.N, g.K);
   } else {
@@ -581,6 +680,7 @@ __device__ __forceinline__ bool tile_at(const GemmArgs& g, int64_t t, TileRef& r
     r.tc.kt_end = KT * (split + 1) / g.splits;
     r.bc = g.b_codes;
     r.bs = g.b_scales;
+    r.expert = 0;
   }
   return true;
 }
@@ -618,7 +718,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& g, int64_t total, uin
       p.set_tile(g, nxt.tc, g.M, nxt.bc, nxt.bs);
       p.prologue_loads();
     }
-    store_out<C, MODE>(p.acc, g, cur.tc, wave, lane, smem);
+    store_out<C, MODE>(p.acc, g, cur.tc, cur.expert, wave, lane, smem);
     if (tn >= total) break;
     if (!C::OVERLAP) {
       p.set_tile(g, nxt.tc, g.M, nxt.bc, nxt.bs);
@@ -640,9 +740,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::O
 // Grouped: the tile map (built by build_tile_map_kernel) lists, per m-tile,
 // the expert and the first row; unused entries are skipped.
 template <class C, int MODE>
+constexpr int grouped_lds() {
+  return (MODE >= kOutSwiGlu0 && swiglu_lds<C>() > C::LDS_BYTES) ? swiglu_lds<C>() : C::LDS_BYTES;
+}
+
+template <class C, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC))) void gemm_grouped_kernel(
     GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[grouped_lds<C, MODE>()];
   gemm_tiles<C, true, MODE>(g, g.max_mtiles * ((g.N + C::BN - 1) / C::BN), smem);
 }
 
@@ -712,16 +817,25 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
 
 template <class C>
 hipError_t launch_grouped_cfg(const GemmArgs& g, hipStream_t stream) {
-  hipLaunchKernelGGL(build_tile_map_kernel, dim3(1), dim3(256), 0, stream, g.offsets, g.E, C::BM, g.max_mtiles,
-                     g.tile_map);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!g.map_ready) {
+    hipLaunchKernelGGL(build_tile_map_kernel, dim3(1), dim3(256), 0, stream, g.offsets, g.E, C::BM, g.max_mtiles,
+                       g.tile_map);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t nt = (g.N + C::BN - 1) / C::BN;
   const int64_t total = g.max_mtiles * nt;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int64_t grid = total < kNumCu ? total : kNumCu;
   const dim3 gd((unsigned)grid), bd(NT);
-  if (g.y_bf16 && g.vec16_y) hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutBf16Staged>), gd, bd, 0, stream, g);
+  if (g.swiglu) {
+    switch (g.q_b) {
+      case 0: hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutSwiGlu0>), gd, bd, 0, stream, g); break;
+      case 32: hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutSwiGlu32>), gd, bd, 0, stream, g); break;
+      case 64: hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutSwiGlu64>), gd, bd, 0, stream, g); break;
+      default: hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutSwiGlu128>), gd, bd, 0, stream, g); break;
+    }
+  } else if (g.y_bf16 && g.vec16_y) hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutBf16Staged>), gd, bd, 0, stream, g);
   else if (g.y_bf16) hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutBf16>), gd, bd, 0, stream, g);
   else hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutF32>), gd, bd, 0, stream, g);
   return hipGetLastError();

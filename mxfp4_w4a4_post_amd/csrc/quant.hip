@@ -9,7 +9,7 @@
 // The encode and nibble packing use the hardware scaled FP4 convert, which
 // rounds to nearest-even, saturates at 6 and keeps the sign (it only reads
 // the exponent of its fp32 scale operand).
-#include "common.hpp"
+#include "mx_lane.hpp"
 
 namespace macaq {
 namespace {
@@ -18,13 +18,6 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// The value of lane ^ d (d = 1 or 2, inside a quad of lanes) through a DPP
-// quad permutation: [1,0,3,2] for d = 1, [2,3,0,1] for d = 2.
-__device__ __forceinline__ float xor_lane(float x, int d) {
-  return __int_as_float(d == 1 ? __builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)
-                               : __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
-}
 
 // Largest e in [0, E) with off[e] <= row (the expert that owns `row`).
 __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ off, int E, int64_t row) {
@@ -79,8 +72,13 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
 
   float v[32];
   if (valid) {
+    int64_t src = row;
+    if (q.gather) {  // MoE rows read their token's activations
+      src = q.gather[row];
+      src = src < 0 ? 0 : (src >= q.src_rows ? q.src_rows - 1 : src);
+    }
     if constexpr (F32_IN) {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q.x) + row * q.ldx + k0);
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q.x) + src * q.ldx + k0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float4 u = p[i];
@@ -90,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
         v[4 * i + 3] = u.w;
       }
     } else {
-      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.x) + row * q.ldx + k0);
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.x) + src * q.ldx + k0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint4 w = p[i];
@@ -124,53 +122,9 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
     for (int i = 0; i < 32; ++i) v[i] = 0.0f;
   }
 
-  if constexpr (B > 0) {
-    // spans 1 .. 16 inside the lane
-#pragma unroll
-    for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i & h) continue;
-        const float u = v[i], w = v[i + h];
-        v[i] = u + w;
-        v[i + h] = u - w;
-      }
-    }
-    // spans 32 .. B/2 across the lanes of chunks d apart: the lower chunk
-    // keeps u + w, the upper one u - w. fma with +-1 rounds once, exactly as
-    // the plain add or subtract would.
-#pragma unroll
-    for (int d = 1; d < B / 32; d <<= 1) {
-      const float sgn = (c & d) ? -1.0f : 1.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float p = xor_lane(v[i], d);
-        v[i] = __builtin_fmaf(sgn, v[i], p);
-      }
-    }
-  }
-
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-
-  // E8M0: biased exponent of amax minus E2M1's largest exponent (2),
-  // clamped at 0 (2^-127); covers amax == 0 and subnormal amax.
-  const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xFF);
-  const int sc = ebits > 2 ? ebits - 2 : 0;
-  const float scale = sc ? __uint_as_float((uint32_t)sc << 23) : __uint_as_float(0x00400000u);
-
-  uint32_t packed[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    uint32_t w = 0;
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * d], v[8 * d + 1], scale, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * d + 2], v[8 * d + 3], scale, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * d + 4], v[8 * d + 5], scale, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * d + 6], v[8 * d + 7], scale, 3);
-    packed[d] = w;
-  }
-  const uint4 out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  fwht_lane<B>(v, c);
+  uint4 out;
+  const int sc = mx_encode(v, out);
 
   if constexpr (TILED) {
     // every lane of the padded grid writes (zeros outside M x K)

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding._SIGNATURES), "binding signatures out of sync with the header"
@@ -141,3 +141,53 @@ def test_binding_has_no_cpu_fallback():
     import torch
     with pytest.raises(ValueError):
         binding.quant_act(torch.zeros(4, 64, dtype=torch.bfloat16), None, 0)
+
+
+def test_moe_calls_reject(lib):
+    """Host checks of the MoE block calls (nothing is dereferenced)."""
+    ws = 1 << 30
+    # route: bad E, k, T*k overflow, NULL, misaligned
+    assert lib.macaq_moe_route(FAKE, 16, 2, 0, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.macaq_moe_route(FAKE, 16, 2, 5000, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.macaq_moe_route(FAKE, 16, 0, 8, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.macaq_moe_route(FAKE, 1 << 30, 8, 8, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.macaq_moe_route(None, 16, 2, 8, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.macaq_moe_route(FAKE + 2, 16, 2, 8, FAKE, FAKE, FAKE, None) == EALIGN
+
+    def gate_up(X=FAKE, T=16, H=256, ldx=256, k=2, E=8, a_gu=FAKE, b=32, F=128, a_dn=FAKE, dn=FAKE, wsb=ws,
+                wsp=FAKE):
+        return lib.macaq_moe_gate_up(X, T, H, ldx, k, FAKE, FAKE, E, a_gu, b, FAKE, FAKE, F, a_dn, dn, FAKE, wsp,
+                                     wsb, None)
+
+    assert gate_up(H=48) == EINVAL          # H % 32
+    assert gate_up(F=96, b=64) == EINVAL    # F % b
+    assert gate_up(b=16) == EINVAL
+    assert gate_up(ldx=128) == EINVAL
+    assert gate_up(a_gu=None) == EINVAL     # b > 0 needs multipliers
+    assert gate_up(X=FAKE + 8) == EALIGN
+    assert gate_up(dn=FAKE + 4) == EALIGN
+    assert gate_up(wsb=16) == EWORKSPACE
+    assert gate_up(wsp=FAKE + 16) == EWORKSPACE
+    assert gate_up(T=0) == OK               # nothing to do
+
+    def down(T=16, k=2, E=8, H=256, F=128, Y=FAKE, dt=0, ldy=256, wsb=ws):
+        return lib.macaq_moe_down_combine(FAKE, FAKE, FAKE, FAKE, FAKE, T, k, E, FAKE, FAKE, H, F, Y, dt, ldy, FAKE,
+                                          wsb, None)
+
+    assert down(ldy=128) == EINVAL
+    assert down(dt=3) == EINVAL
+    assert down(Y=None) == EINVAL
+    assert down(E=0) == EINVAL
+    assert down(wsb=0) == EWORKSPACE
+
+    def block(T=16, H=256, ldx=256, k=2, E=8, b=32, F=128, wsb=ws, a_dn=FAKE):
+        return lib.macaq_moe_block(FAKE, T, H, ldx, FAKE, FAKE, k, E, FAKE, FAKE, FAKE, a_dn, FAKE, FAKE, F, b, FAKE,
+                                   0, H, FAKE, wsb, None)
+
+    assert block(a_dn=None) == EINVAL
+    assert block(F=40) == EINVAL
+    assert block(wsb=1024) == EWORKSPACE
+    assert block(T=0) == OK
+    need = lib.macaq_moe_workspace_size(16, 2, 8, 256, 128)
+    assert need > 0 and block(wsb=need - 1) == EWORKSPACE
+    assert lib.macaq_moe_workspace_size(0, 2, 8, 256, 128) == 0

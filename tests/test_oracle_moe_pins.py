@@ -10,9 +10,9 @@ numpy, and against the dense layer when there is one expert and k = 1.
 """
 import numpy as np
 import pytest
-import torch
-
 from mxfp4_w4a4_post_amd import inputs
+
+from moe_util import bf16_round as _bf16_round, oracle_prepare as _prepare_case
 
 
 def _np_route(ids, E):
@@ -116,38 +116,6 @@ def test_combine_selects_and_weights(orc):
             if pos[t, j] >= 0:
                 expect[t] += np.float64(w[t, j]) * rows[pos[t, j]].astype(np.float64)
     assert np.allclose(y, expect, rtol=1e-15, atol=0)
-
-
-def _prepare_case(orc, c):
-    """Oracle-side preparation of a MoE block case (per expert: calibrate,
-    multipliers, prepared stacked gate/up and down weights)."""
-    bits = inputs.bf16_bits
-    E, F, H, b = c.E, c.F, c.H, c.b
-    a_gu = np.empty((E, H), np.float32)
-    a_dn = np.empty((E, F), np.float32)
-    gc = np.empty((E, 2 * F, H // 2), np.uint8)
-    gs = np.empty((E, 2 * F, H // 32), np.uint8)
-    dc = np.empty((E, H, F // 2), np.uint8)
-    ds = np.empty((E, H, F // 32), np.uint8)
-    for e in range(E):
-        a, r = orc.multipliers(orc.calibrate(bits(c.xcal_gu[e])), b)
-        a_gu[e] = a
-        wgu = _stack_rows(bits(c.w_gate[e]), bits(c.w_up[e]))
-        gc[e], gs[e] = orc.prepare_weights(wgu, r, b)
-        a, r = orc.multipliers(orc.calibrate(bits(c.xcal_dn[e])), b)
-        a_dn[e] = a
-        dc[e], ds[e] = orc.prepare_weights(bits(c.w_dn[e]), r, b)
-    return a_gu, gc, gs, a_dn, dc, ds
-
-
-def _stack_rows(wg, wu):
-    """[F, H] gate and up weight rows -> [2F, H], alternating blocks of 32 rows."""
-    F, H = wg.shape
-    return np.stack([wg.reshape(F // 32, 32, H), wu.reshape(F // 32, 32, H)], axis=1).reshape(2 * F, H)
-
-
-def _bf16_round(v):
-    return torch.from_numpy(np.asarray(v, np.float64)).float().bfloat16().float().numpy().astype(np.float64)
 
 
 def test_moe_block_matches_restatement(orc):
