@@ -7,8 +7,10 @@ scale + block-Hadamard + MXFP4 quantize + scaled-FP4 GEMM), bf16 in and out.
 Weights are prepared beforehand (offline). Other workloads (--workload):
 decode-32b (M = 1, 8, 32, 64 through 5120x25600 and 25600x5120), moe-128e
 (grouped gate/up and down projections of 4096 tokens routed top-8 over 128
-experts), prefill-large (M = 8192 through 8192x28672 and 28672x8192, Hadamard
-block from --block) and tiny.
+experts), moe-block (the same 4096 tokens through the whole MoE block:
+routing, gathered gate/up with the SwiGLU epilogue that quantizes the down
+input, down, weighted top-8 combine), prefill-large (M = 8192 through
+8192x28672 and 28672x8192, Hadamard block from --block) and tiny.
 
 Inputs are resident in HBM; the timed steps rotate through several copies of
 activations and weights so that no step finds its operands in the 256 MB
@@ -37,7 +39,8 @@ PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ROTATE = 4                  # operand copies cycled through by the timed steps
 ORACLE_THREADS_CAP = 16     # the GPU machine's CPU share for one GPU
-WORKLOADS = {"tiny": 1, "prefill-8b": 2, "decode-32b": 3, "moe-128e": 4, "prefill-large": 5}
+WORKLOADS = {"tiny": 1, "prefill-8b": 2, "decode-32b": 3, "moe-128e": 4, "prefill-large": 5, "moe-block": 6}
+MOE_BLOCK = 6  # the MoE workload as a whole block: routing, gathered gate/up + SwiGLU, down, combine
 
 
 def parse():
@@ -180,6 +183,48 @@ def moe_entries(torch, binding, inputs, b, dev):
     return entries
 
 
+def moe_block_entries(torch, binding, inputs, b, dev):
+    """One entry: the MoE block on the MoE workload's tokens, with the fused
+    (MACaQ) and plain MXFP4 prepared experts; the parts of the block alone for
+    the per-kernel split."""
+    case = inputs.moe_block_case(b=b)
+    T, E, k, H, F = case.T, case.E, case.k, case.H, case.F
+    wg, wu, wd = case.w_gate.to(dev), case.w_up.to(dev), case.w_dn.to(dev)
+    lf = binding.prepare_moe(wg, wu, wd, case.xcal_gu.to(dev), case.xcal_dn.to(dev), b)
+    lp = binding.prepare_moe(wg, wu, wd, None, None, 0)
+    del wg, wu, wd
+
+    def copies(lay):
+        out = [lay]
+        for _ in range(ROTATE - 1):
+            out.append(binding.MoELayer(lay.a_gu, packed_clone(binding, lay.wgu), lay.a_dn,
+                                        packed_clone(binding, lay.wdn), lay.b))
+        return out
+
+    lfs, lps = copies(lf), copies(lp)
+    xs = [case.x.to(dev) for _ in range(ROTATE)]
+    ids = torch.from_numpy(case.ids).to(dev)
+    w = torch.from_numpy(case.w).to(dev)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    work = torch.empty(binding.moe_workspace_size(T, k, E, H, F), dtype=torch.uint8, device=dev)
+    R = T * k
+    wbytes = E * (2 * F * H + H * F) * 17 / 32
+    flops = 2.0 * R * (2 * F) * H + 2.0 * R * H * F
+    e = Entry("moe block T=%d k=%d E=%d H=%d F=%d" % (T, k, E, H, F), flops, 2 * T * H + wbytes + 2 * T * H, None)
+    e.fused = lambda c: lfs[c](xs[c], ids, w, out=y, workspace=work)
+    e.plain = lambda c: lps[c](xs[c], ids, w, out=y, workspace=work)
+    off, tok, pos = binding.moe_route(ids, E)
+    dn = binding.moe_gate_up(xs[0], k, tok, off, lf.a_gu, b, lf.wgu, lf.a_dn, workspace=work)
+    e.route = lambda c: binding.moe_route(ids, E)
+    e.gate_up = lambda c: binding.moe_gate_up(xs[c], k, tok, off, lfs[c].a_gu, b, lfs[c].wgu, lfs[c].a_dn, out=dn,
+                                              workspace=work)
+    e.down_combine = lambda c: binding.moe_down_combine(dn, off, pos, w, lfs[c].wdn, out=y, workspace=work)
+    e.parts_bytes = {"gate_up": 2 * R * H + E * 2 * F * H * 17 / 32 + R * F * 17 / 32,
+                     "down_combine": R * F * 17 / 32 + E * H * F * 17 / 32 + 2 * R * H * 2 + 2 * T * H}
+    e.oracle_case = (case, None)
+    return [e]
+
+
 def capture(torch, fn):
     """A HIP graph of the kernels that fn enqueues on the current stream."""
     s = torch.cuda.Stream()
@@ -221,6 +266,42 @@ def cpu_baseline(entries, target_s, moe):
     from mxfp4_w4a4_post_amd import inputs as inp
 
     threads = min(oracle.default_threads(), ORACLE_THREADS_CAP)
+    if moe == "block":
+        case = entries[0].oracle_case[0]
+        bits = inp.bf16_bits
+        x = bits(case.x)
+        n, dt, flops = 4, 0.0, 0.0
+        while True:
+            want = np.zeros(case.T, bool)
+            want[:n] = True
+            used = np.unique(case.ids[:n])
+            a_gu = np.ones((case.E, case.H), np.float32)
+            a_dn = np.ones((case.E, case.F), np.float32)
+            gc = np.zeros((case.E, 2 * case.F, case.H // 2), np.uint8)
+            gs = np.zeros((case.E, 2 * case.F, case.H // 32), np.uint8)
+            dc = np.zeros((case.E, case.H, case.F // 2), np.uint8)
+            ds = np.zeros((case.E, case.H, case.F // 32), np.uint8)
+            for ex in used:
+                a, r = oracle.multipliers(oracle.calibrate(bits(case.xcal_gu[ex])), case.b)
+                a_gu[ex] = a
+                wgu = np.stack([bits(case.w_gate[ex]).reshape(case.F // 32, 32, case.H),
+                                bits(case.w_up[ex]).reshape(case.F // 32, 32, case.H)], axis=1)
+                gc[ex], gs[ex] = oracle.prepare_weights(wgu.reshape(2 * case.F, case.H), r, case.b)
+                a, r = oracle.multipliers(oracle.calibrate(bits(case.xcal_dn[ex])), case.b)
+                a_dn[ex] = a
+                dc[ex], ds[ex] = oracle.prepare_weights(bits(case.w_dn[ex]), r, case.b)
+            t0 = time.perf_counter()
+            oracle.moe_block(x, case.ids, case.w, case.E, a_gu, gc, gs, a_dn, dc, ds, case.b, want=want,
+                             threads=threads)
+            dt = time.perf_counter() - t0
+            flops = 2.0 * n * case.k * (2 * case.F * case.H + case.H * case.F)
+            if dt >= target_s * 0.5 or n >= case.T:
+                break
+            n = min(case.T, n * max(2, int(target_s / max(dt, 1e-3))))
+        return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
+                    sample="the whole block (routing, gathered gate/up, SiLU x up, down input quantize, down, "
+                           "combine) for the first %d of %d tokens, weights of their experts prepared outside "
+                           "the timing, %.1f s" % (n, case.T, dt))
     if moe:
         flops, dt, experts = 0.0, 0.0, 0
         while dt < target_s and experts < entries[0].oracle_case[0].E:
@@ -304,10 +385,19 @@ def main():
         print(json.dumps({"copied_bytes": n, "copies": 3}), flush=True)
         return
     wl = WORKLOADS[args.workload]
-    spec = inputs.CONFIGS[wl]
+    spec = inputs.CONFIGS[4 if wl == MOE_BLOCK else wl]
     b = args.block if args.block is not None else spec["blocks"][0]
     moe = wl == 4
-    if moe:
+    if wl == MOE_BLOCK:
+        entries = moe_block_entries(torch, binding, inputs, b, dev)
+        workload = ("moe-block: %d tokens routed top-%d over %d experts (Zipf(%.1f) popularity), hidden %d, expert "
+                    "FFN %d (gate/up stacked, SwiGLU epilogue quantizing the down input), down, weighted combine, "
+                    "Hadamard block %d, bf16 in/out" % (spec["tokens"], spec["top_k"], spec["experts"], spec["zipf"],
+                                                        spec["hidden"], spec["ffn"], b))
+        tokens = spec["tokens"]
+        cfg_extra = {"tokens": tokens, "experts": spec["experts"], "top_k": spec["top_k"], "hidden": spec["hidden"],
+                     "ffn": spec["ffn"], "hadamard_block": b}
+    elif moe:
         entries = moe_entries(torch, binding, inputs, b, dev)
         workload = ("%s: %d tokens routed top-%d over %d experts (Zipf(%.1f) popularity), grouped gate/up %d->%d "
                     "and down %d->%d, Hadamard block %d, bf16 in/out"
@@ -364,7 +454,20 @@ def main():
         "timing": "the timed steps in one HIP graph (operand copies cycled, %d copies), HIP events on the launch "
                   "stream" % ROTATE,
     }
-    if not moe:
+    if wl == MOE_BLOCK:
+        e = entries[0]
+        parts = {k: timed_steps(torch, getattr(e, k), args.steps, args.warmup)[0]
+                 for k in ("route", "gate_up", "down_combine")}
+        out["calls_ms_per_step"] = {k: round(v, 5) for k, v in parts.items()}
+        gb_step = nbytes / (ms * 1e-3) / 1e9
+        gu_gb = e.parts_bytes["gate_up"] / (parts["gate_up"] * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(gb_step, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(gb_step / PEAK_HBM_GBS, 4), "traffic": None,
+                           "kernel": "macaq_moe_block (algorithmic bytes: tokens read once, both expert weight "
+                                     "sets, y written once)",
+                           "gate_up_call_gbs": round(gu_gb, 1),
+                           "kernel_source_digest": digest}
+    elif not moe:
         # each kernel of the step alone: the same timed steps with only that
         # kernel of every layer call, on the same operand copies
         def kernel_ms(attr):
@@ -400,7 +503,7 @@ def main():
                            "kernel": "macaq_linear_grouped (quantize + tile map + grouped GEMM per call)",
                            "kernel_source_digest": digest}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(entries, args.cpu_seconds, moe)
+        out["cpu_baseline"] = cpu_baseline(entries, args.cpu_seconds, "block" if wl == MOE_BLOCK else moe)
     print(json.dumps(out), flush=True)
 
 

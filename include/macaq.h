@@ -267,6 +267,8 @@ macaq_status macaq_moe_down_combine(const uint8_t* dn_codes, const uint8_t* dn_s
 /*
  * The whole block: macaq_moe_route, macaq_moe_gate_up and
  * macaq_moe_down_combine in one call, their intermediates in the workspace.
+ * ids: device int32 [T, k], 16-byte aligned; w: device fp32 [T, k]; other
+ * arguments as in those calls.
  */
 macaq_status macaq_moe_block(const void* X, int64_t T, int64_t H, int64_t ldx, const int32_t* ids, const float* w,
                              int32_t k, int32_t E, const float* a_gu, const uint8_t* wgu_codes,

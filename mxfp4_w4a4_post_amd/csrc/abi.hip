@@ -110,9 +110,10 @@ struct MoeWs {
 
 MoeWs moe_ws(int64_t T, int32_t k, int32_t E, int64_t H, int64_t F) {
   const int64_t R = T * k;
-  const GemmPlan p = plan_gemm_grouped(R, E, 2 * F, H);
+  const GemmPlan pg = plan_gemm_grouped(R, E, 2 * F, H, true), pd = plan_gemm_grouped(R, E, H, F);
+  const int64_t bm = pg.bm < pd.bm ? pg.bm : pd.bm;
   MoeWs w;
-  w.max_mtiles = (R + p.bm - 1) / p.bm + E;
+  w.max_mtiles = (R + bm - 1) / bm + E;
   size_t at = 0;
   auto take = [&](size_t bytes) {
     const size_t here = at;
@@ -122,7 +123,7 @@ MoeWs moe_ws(int64_t T, int32_t k, int32_t E, int64_t H, int64_t F) {
   w.offsets = take((size_t)(E + 1) * 4);
   w.row_token = take((size_t)R * 4);
   w.pos = take((size_t)R * 4);
-  w.map = take((size_t)w.max_mtiles * 2 * 4);
+  w.map = take(((size_t)w.max_mtiles * 2 + 1) * 4);
   w.agu_codes = take((size_t)tiled_codes_bytes(R, H));
   w.agu_scales = take((size_t)tiled_scales_bytes(R, H));
   w.dn_codes = take((size_t)tiled_codes_bytes(R, F));
@@ -189,7 +190,7 @@ hipError_t moe_gate_up_launch(const void* X, int64_t T, int64_t H, int64_t ldx, 
   g.q_mult = a_dn;
   g.q_F = F;
   g.q_b = b;
-  return launch_gemm_grouped(g, plan_gemm_grouped(R, E, 2 * F, H), s);
+  return launch_gemm_grouped(g, plan_gemm_grouped(R, E, 2 * F, H, true), s);
 }
 
 hipError_t moe_down_combine_launch(const uint8_t* dn_codes, const uint8_t* dn_scales, const int32_t* offsets,
@@ -430,7 +431,7 @@ size_t macaq_linear_grouped_workspace_size(int64_t T, int32_t E, int64_t K, int6
   if (T <= 0 || E < 1 || K <= 0 || N <= 0) return 0;
   const GemmPlan p = plan_gemm_grouped(T, E, N, K);
   const int64_t max_mtiles = (T + p.bm - 1) / p.bm + E;
-  return linear_ws(T, K, (size_t)max_mtiles * 2 * sizeof(int32_t)).total;
+  return linear_ws(T, K, ((size_t)max_mtiles * 2 + 1) * sizeof(int32_t)).total;
 }
 
 macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t E, int64_t T, int64_t K,
@@ -458,7 +459,7 @@ macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t
   if (st != MACAQ_OK) return st;
   const GemmPlan p = plan_gemm_grouped(T, E, N, K);
   const int64_t max_mtiles = (T + p.bm - 1) / p.bm + E;
-  const LinearWs w = linear_ws(T, K, (size_t)max_mtiles * 2 * sizeof(int32_t));
+  const LinearWs w = linear_ws(T, K, ((size_t)max_mtiles * 2 + 1) * sizeof(int32_t));
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   QuantArgs q{};
@@ -507,8 +508,8 @@ macaq_status macaq_moe_route(const int32_t* ids, int64_t T, int32_t k, int32_t E
   if (E < 1 || E > kMaxExperts) return fail(MACAQ_EINVAL, "%s: E = %d not in [1, %d]", who, E, kMaxExperts);
   if (T * (int64_t)k > 0x7FFFFFFF) return fail(MACAQ_EINVAL, "%s: T*k exceeds int32", who);
   if (!ids || !offsets || !row_token || !pos) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
-  if (!aligned(ids, 4) || !aligned(offsets, 4) || !aligned(row_token, 4) || !aligned(pos, 4))
-    return fail(MACAQ_EALIGN, "%s: int32 arrays must be 4-byte aligned", who);
+  if (!aligned(ids, 16) || !aligned(offsets, 4) || !aligned(row_token, 4) || !aligned(pos, 4))
+    return fail(MACAQ_EALIGN, "%s: ids must be 16-byte aligned, the other int32 arrays 4-byte aligned", who);
   macaq_status st = check_device();
   if (st != MACAQ_OK) return st;
   hipError_t e = launch_moe_route(ids, T, k, E, offsets, row_token, pos, reinterpret_cast<hipStream_t>(stream));
@@ -586,8 +587,8 @@ macaq_status macaq_moe_block(const void* X, int64_t T, int64_t H, int64_t ldx, c
   if (st != MACAQ_OK) return st;
   if (!aligned(X, 16) || ldx % 8 != 0 || (a_gu && !aligned(a_gu, 16)) || (a_dn && !aligned(a_dn, 4)) ||
       !aligned(wgu_codes, 16) || !aligned(wgu_scales, 16) || !aligned(wdn_codes, 16) || !aligned(wdn_scales, 16) ||
-      !aligned(ids, 4) || !aligned(w_route, 4))
-    return fail(MACAQ_EALIGN, "%s: X, a_gu and weights 16-byte aligned, ldx a multiple of 8", who);
+      !aligned(ids, 16) || !aligned(w_route, 4))
+    return fail(MACAQ_EALIGN, "%s: X, a_gu, weights and ids 16-byte aligned, ldx a multiple of 8", who);
   if (T == 0) return MACAQ_OK;
   const MoeWs w = moe_ws(T, k, E, H, F);
   if (!workspace || workspace_bytes < w.total || !aligned(workspace, kWsAlign))
@@ -604,9 +605,10 @@ macaq_status macaq_moe_block(const void* X, int64_t T, int64_t H, int64_t ldx, c
   e = moe_gate_up_launch(X, T, H, ldx, k, row_token, offsets, E, a_gu, b, wgu_codes, wgu_scales, F, a_dn,
                          ws + w.dn_codes, ws + w.dn_scales, ws, w, true, s);
   if (e != hipSuccess) return hip_fail(e, "macaq_moe_block gate/up launch");
-  // both grouped GEMMs use the same tile size, so the map built above serves the down GEMM
+  // the map built for the gate/up GEMM serves the down GEMM when both use the same tile rows
+  const bool same_bm = plan_gemm_grouped(T * k, E, 2 * F, H, true).bm == plan_gemm_grouped(T * k, E, H, F).bm;
   e = moe_down_combine_launch(ws + w.dn_codes, ws + w.dn_scales, offsets, pos, w_route, T, k, E, wdn_codes,
-                              wdn_scales, H, F, Y, y_dtype, ldy, ws, w, false, s);
+                              wdn_scales, H, F, Y, y_dtype, ldy, ws, w, !same_bm, s);
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_block down/combine launch");
 }
 

@@ -87,7 +87,7 @@ struct GemmArgs {
   int splits;
   // grouped
   const int32_t* offsets;   // [E+1] or nullptr
-  int32_t* tile_map;        // workspace: per m-tile (expert, first row)
+  int32_t* tile_map;        // workspace: per m-tile (expert, first row), then the used count
   int E;
   int64_t max_mtiles;
   bool map_ready;           // grouped: tile_map already holds the map of these offsets
@@ -112,12 +112,33 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
-GemmPlan plan_gemm_grouped(int64_t T, int E, int64_t N, int64_t K);
+// swiglu: the MoE gate/up GEMM with the SwiGLU epilogue (its own tile shape)
+GemmPlan plan_gemm_grouped(int64_t T, int E, int64_t N, int64_t K, bool swiglu = false);
 hipError_t launch_gemm(const GemmArgs& g, const GemmPlan& p, hipStream_t stream);
 hipError_t launch_gemm_grouped(const GemmArgs& g, const GemmPlan& p, hipStream_t stream);
 
-// MoE block: routing (one workgroup per expert, LDS histogram of at most
-// kMaxExperts experts) and the weighted combine of bf16 expert rows.
+// Exclusive prefix sum of v over a workgroup of NTH threads (Hillis-Steele
+// in the LDS array sh[NTH]); *total receives the sum of every thread's v.
+// Every thread of the workgroup must call it.
+template <int NTH>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int d = 1; d < NTH; d <<= 1) {
+    const int t = tid >= d ? sh[tid - d] : 0;
+    __syncthreads();
+    sh[tid] += t;
+    __syncthreads();
+  }
+  const int incl = sh[tid];
+  *total = sh[NTH - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+// MoE block: routing (one workgroup per expert, at most kMaxExperts) and the
+// weighted combine of bf16 expert rows.
 constexpr int kMaxExperts = 4096;
 hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
                             int32_t* pos, hipStream_t stream);

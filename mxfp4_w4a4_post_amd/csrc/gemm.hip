@@ -300,7 +300,9 @@ __device__ __forceinline__ void store_swiglu_quant(const Acc<C>& acc, const Gemm
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float gt = acc.v[i][0][4 * q + e], up = acc.v[i][1][4 * q + e];
-        h[e] = gt / (1.0f + expf(-gt)) * up;
+        // SiLU(g) = g / (1 + e^-g) through the hardware exp2 and reciprocal
+        // (about 1 ulp each); e^-g overflowing to inf gives -0, as it should
+        h[e] = gt * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gt * -1.44269504f)) * up;
       }
       const int row = i * 32 + (lane & 31), ch = wave * 32 + 8 * q + 4 * (lane >> 5);
       lds_at<float4>(smem, row * PITCH + ch * 4) = make_float4(h[0], h[1], h[2], h[3]);
@@ -686,12 +688,12 @@ __device__ __forceinline__ bool tile_at(const GemmArgs& g, int64_t t, TileRef& r
 }
 
 // Workgroup ids are dispatched round-robin over the 8 XCDs (id i runs on XCD
-// i % 8). Renumber so that each XCD works through a contiguous run of tiles,
-// which the grouped order above makes share A and B panels in that XCD's L2.
+// i % 8). Renumber so that each XCD works through a contiguous run of tiles
+// (the first total % 8 XCDs one tile more), which the grouped order above
+// makes share A and B panels in that XCD's L2.
 __device__ __forceinline__ int64_t xcd_remap(int64_t id, int64_t total) {
-  if (total % kNumXcd != 0) return id;
-  const int64_t per = total / kNumXcd;
-  return (id % kNumXcd) * per + id / kNumXcd;
+  const int64_t x = id % kNumXcd, q = total / kNumXcd, r = total % kNumXcd;
+  return x * q + (x < r ? x : r) + id / kNumXcd;
 }
 
 // Persistent workgroups: workgroup b takes tiles b, b + G, b + 2G, ... (G
@@ -748,31 +750,42 @@ template <class C, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC))) void gemm_grouped_kernel(
     GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[grouped_lds<C, MODE>()];
-  gemm_tiles<C, true, MODE>(g, g.max_mtiles * ((g.N + C::BN - 1) / C::BN), smem);
+  // the used m-tiles lead the map; the entry after the map holds their count
+  const int64_t used = g.tile_map[2 * g.max_mtiles];
+  gemm_tiles<C, true, MODE>(g, used * ((g.N + C::BN - 1) / C::BN), smem);
 }
 
-// One thread walks the experts: m-tile j of expert e gets entry (tiles of
-// experts before e) + j; the remaining entries get expert -1.
-__global__ void build_tile_map_kernel(const int32_t* __restrict__ off, int E, int bm, int64_t max_mtiles,
-                                      int32_t* __restrict__ map) {
-  __shared__ int64_t used[1];
-  if (threadIdx.x == 0) {
-    int64_t acc = 0;
-    for (int e = 0; e < E; ++e) {
-      const int64_t rows = (int64_t)off[e + 1] - off[e];
-      const int64_t tiles = rows > 0 ? (rows + bm - 1) / bm : 0;
-      for (int64_t j = 0; j < tiles && acc < max_mtiles; ++j, ++acc) {
-        map[2 * acc] = e;
-        map[2 * acc + 1] = (int32_t)(off[e] + j * bm);
-      }
-    }
-    used[0] = acc;
+// Thread t takes experts [t * ce, (t + 1) * ce): it counts their m-tiles, a
+// workgroup scan gives its first entry, and m-tile j of expert e gets entry
+// (tiles of experts before e) + j; the remaining entries get expert -1, and
+// map[2 * max_mtiles] the number of used entries.
+__global__ __launch_bounds__(256) void build_tile_map_kernel(const int32_t* __restrict__ off, int E, int bm,
+                                                             int64_t max_mtiles, int32_t* __restrict__ map) {
+  __shared__ int sh[256];
+  const int tid = threadIdx.x;
+  const int ce = (E + 255) / 256;
+  const int e0 = tid * ce < E ? tid * ce : E, e1 = e0 + ce < E ? e0 + ce : E;
+  int cnt = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int64_t rows = (int64_t)off[e + 1] - off[e];
+    cnt += rows > 0 ? (int)((rows + bm - 1) / bm) : 0;
   }
-  __syncthreads();
-  for (int64_t i = used[0] + threadIdx.x; i < max_mtiles; i += blockDim.x) {
+  int used = 0;
+  int64_t acc = block_exclusive_scan<256>(cnt, sh, &used);
+  for (int e = e0; e < e1; ++e) {
+    const int64_t rows = (int64_t)off[e + 1] - off[e];
+    const int64_t tiles = rows > 0 ? (rows + bm - 1) / bm : 0;
+    for (int64_t j = 0; j < tiles && acc < max_mtiles; ++j, ++acc) {
+      map[2 * acc] = e;
+      map[2 * acc + 1] = (int32_t)(off[e] + j * bm);
+    }
+  }
+  const int64_t n_used = used < max_mtiles ? used : max_mtiles;
+  for (int64_t i = n_used + tid; i < max_mtiles; i += 256) {
     map[2 * i] = -1;
     map[2 * i + 1] = 0;
   }
+  if (tid == 0) map[2 * max_mtiles] = (int32_t)n_used;
 }
 
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t M,
@@ -798,6 +811,14 @@ using CfgM = TileCfg<CFGM>;  // prefill
 #endif
 using CfgS64 = TileCfg<CFGS64>;  // decode, M <= 64
 using CfgS32 = TileCfg<CFGS32>;  // decode, M <= 32
+#ifndef CFGG
+#define CFGG 128, 256, 2, 2
+#endif
+using CfgG = TileCfg<CFGG>;  // grouped (MoE experts), bf16 / fp32 output
+#ifndef CFGGS
+#define CFGGS 64, 256, 2, 2, true, 2
+#endif
+using CfgGS = TileCfg<CFGGS>;  // grouped with the SwiGLU epilogue (MoE gate/up)
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
@@ -815,7 +836,7 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <class C>
+template <class C, bool SWIGLU>
 hipError_t launch_grouped_cfg(const GemmArgs& g, hipStream_t stream) {
   if (!g.map_ready) {
     hipLaunchKernelGGL(build_tile_map_kernel, dim3(1), dim3(256), 0, stream, g.offsets, g.E, C::BM, g.max_mtiles,
@@ -826,18 +847,21 @@ hipError_t launch_grouped_cfg(const GemmArgs& g, hipStream_t stream) {
   const int64_t nt = (g.N + C::BN - 1) / C::BN;
   const int64_t total = g.max_mtiles * nt;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const int64_t grid = total < kNumCu ? total : kNumCu;
+  const int64_t resident = (int64_t)kNumCu * C::OCC;
+  const int64_t grid = total < resident ? total : resident;
   const dim3 gd((unsigned)grid), bd(NT);
-  if (g.swiglu) {
+  if constexpr (SWIGLU) {
     switch (g.q_b) {
       case 0: hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutSwiGlu0>), gd, bd, 0, stream, g); break;
       case 32: hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutSwiGlu32>), gd, bd, 0, stream, g); break;
       case 64: hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutSwiGlu64>), gd, bd, 0, stream, g); break;
       default: hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutSwiGlu128>), gd, bd, 0, stream, g); break;
     }
-  } else if (g.y_bf16 && g.vec16_y) hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutBf16Staged>), gd, bd, 0, stream, g);
-  else if (g.y_bf16) hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutBf16>), gd, bd, 0, stream, g);
-  else hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutF32>), gd, bd, 0, stream, g);
+  } else {
+    if (g.y_bf16 && g.vec16_y) hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutBf16Staged>), gd, bd, 0, stream, g);
+    else if (g.y_bf16) hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutBf16>), gd, bd, 0, stream, g);
+    else hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutF32>), gd, bd, 0, stream, g);
+  }
   return hipGetLastError();
 }
 
@@ -890,15 +914,15 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
-GemmPlan plan_gemm_grouped(int64_t T, int E, int64_t N, int64_t K) {
+GemmPlan plan_gemm_grouped(int64_t T, int E, int64_t N, int64_t K, bool swiglu) {
   (void)T;
   (void)E;
   (void)N;
   (void)K;
   GemmPlan p{};
-  p.cfg = 1;
-  p.bm = 128;
-  p.bn = 256;
+  p.cfg = swiglu ? 2 : 1;
+  p.bm = swiglu ? CfgGS::BM : CfgG::BM;
+  p.bn = swiglu ? CfgGS::BN : CfgG::BN;
   p.splits = 1;
   p.partial_bytes = 0;
   return p;
@@ -925,7 +949,12 @@ hipError_t launch_gemm_grouped(const GemmArgs& g_in, const GemmPlan& p, hipStrea
   (void)p;
   GemmArgs g = g_in;
   set_vec_flags(g);
-  return launch_grouped_cfg<CfgM>(g, stream);
+  if (p.cfg == 2) {
+    if (!g.swiglu) return hipErrorInvalidValue;
+    return launch_grouped_cfg<CfgGS, true>(g, stream);
+  }
+  if (g.swiglu) return hipErrorInvalidValue;
+  return launch_grouped_cfg<CfgG, false>(g, stream);
 }
 
 }  // namespace macaq
