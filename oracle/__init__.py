@@ -20,11 +20,18 @@ arithmetic lives there, with its sources:
   "Huawei's MACaQ-R beats Unsloth's ..." ("Changed tensors") names the
   experts' gate, up and down projections. The gated FFN form is a reading.
 
-Parity status per function (what pins it, see ``tests/test_oracle_pins.py``):
+* Flip-Refinement (Hessian of the transformed calibration rows, greedy
+  single-code moves with the block scales kept): "MACaQ ..." (paper card,
+  Abstract); "Huawei's MACaQ-R beats Unsloth's ..." (Why that's still
+  interesting; What we found when we compared the files). Objective, move
+  order and stopping rule are readings.
+
+Parity status per function (what pins it, see ``tests/test_oracle_pins.py``,
+``tests/test_oracle_moe_pins.py``, ``tests/test_oracle_refine_pins.py``):
 calibrate, multipliers, transform_rows, quant_rows, dequant_rows, gemm_codes,
-linear, linear_grouped, moe_route, silu_mul, moe_combine and moe_block are
-all pinned by closed forms, hand-worked values, independent restatements and
-brute force; none is "parity unpinned".
+linear, linear_grouped, moe_route, silu_mul, moe_combine, moe_block, hessian
+and flip_refine are all pinned by closed forms, hand-worked values,
+independent restatements and brute force; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -79,9 +86,12 @@ def _load():
     lib.oracle_moe_combine.argtypes = [_f32p, _i64, _i32p, _f32p, _i64, _int, _f64p]
     lib.oracle_moe_block.argtypes = [vp, _i64, _i64, _i32p, _f32p, _int, _int, _f32p, _u8p, _u8p, _f32p, _u8p,
                                      _u8p, _i64, _int, _u8p, _u8p, _u8p, _f64p, _int]
+    lib.oracle_hessian.argtypes = [vp, _i64, _i64, _i64, _f32p, _int, _f64p]
+    lib.oracle_flip_refine.argtypes = [vp, _int, _i64, _i64, _i64, _f32p, _int, _f64p, _int, _u8p, _u8p, _i32p]
     for f in (lib.oracle_calibrate, lib.oracle_multipliers, lib.oracle_transform_rows, lib.oracle_quant_rows,
               lib.oracle_dequant_rows, lib.oracle_gemm_codes, lib.oracle_linear, lib.oracle_linear_grouped,
-              lib.oracle_moe_route, lib.oracle_silu_mul, lib.oracle_moe_combine, lib.oracle_moe_block):
+              lib.oracle_moe_route, lib.oracle_silu_mul, lib.oracle_moe_combine, lib.oracle_moe_block,
+              lib.oracle_hessian, lib.oracle_flip_refine):
         f.restype = _int
     _lib = lib
     return lib
@@ -299,3 +309,31 @@ def moe_block(x: np.ndarray, ids: np.ndarray, w: np.ndarray, E: int, a_gu, wgu_c
                                 _ptr(gs, _u8p), adp, _ptr(dc, _u8p), _ptr(ds, _u8p), F, b, wp, _ptr(hc, _u8p),
                                 _ptr(hs, _u8p), _ptr(y, _f64p), threads or default_threads()), "moe_block")
     return y, hc, hs
+
+
+def hessian(xcal: np.ndarray, a, b: int) -> np.ndarray:
+    """H [K, K] (fp64) = X~^T X~ of bf16 calibration rows (uint16 bits)
+    through multiplier a and the block-Hadamard of size b."""
+    lib = _load()
+    x = np.ascontiguousarray(xcal, np.uint16)
+    R, K = x.shape
+    a_keep, ap = _opt_f32(a)
+    H = np.empty((K, K), np.float64)
+    _check(lib.oracle_hessian(x.ctypes.data, R, K, K, ap, b, _ptr(H, _f64p)), "hessian")
+    return H
+
+
+def flip_refine(w: np.ndarray, r, b: int, H: np.ndarray, max_flips: int, codes: np.ndarray, scales: np.ndarray):
+    """(refined codes [N, K/2], flips per row) of prepared weights (row-major
+    codes and scales, scales kept) for weight rows w (bf16 bits or fp32)."""
+    lib = _load()
+    w, dt = _elems(w)
+    N, K = w.shape
+    r_keep, rp = _opt_f32(r)
+    H = np.ascontiguousarray(H, np.float64)
+    out = np.array(codes, np.uint8, copy=True, order="C")
+    sc = np.ascontiguousarray(scales, np.uint8)
+    flips = np.zeros(N, np.int32)
+    _check(lib.oracle_flip_refine(w.ctypes.data, dt, N, K, K, rp, b, _ptr(H, _f64p), max_flips, _ptr(out, _u8p),
+                                  _ptr(sc, _u8p), _ptr(flips, _i32p)), "flip_refine")
+    return out, flips

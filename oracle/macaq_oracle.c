@@ -517,3 +517,124 @@ int oracle_moe_block(const uint16_t* x, int64_t T, int64_t H, const int32_t* ids
   free(rows_out);
   return rc;
 }
+
+/* ------------------------------------------------------------------ */
+/* Flip-Refinement of prepared weights                                  */
+/* ------------------------------------------------------------------ */
+/*
+ * Sources: "MACaQ ..." (paper card, Abstract) improves on round-to-nearest
+ * weights with Flip-Refinement, a Hessian-aware coordinate descent that
+ * greedily moves single FP4 codes to adjacent representable values; "Huawei's
+ * MACaQ-R beats Unsloth's ..." (Why that's still interesting) applies the
+ * same idea to existing codes, and (What we found when we compared the
+ * files) finds only codes changed, block scales kept. Readings (choices,
+ * not page text):
+ *   - the objective of output row n is e^T H e with e = w~ - q: w~ the row in
+ *     the transformed basis (S_b (r .* w), the fp32 values the quantizer
+ *     sees), q its dequantized codes, H = X~^T X~ over calibration rows in
+ *     the same basis (x~ = S_b (a .* x), fp32), so that e.x~ is the row's
+ *     output error on a calibration row (w~.x~ = w.x);
+ *   - a move takes one element from signed E2M1 index m (value
+ *     sign(m) LUT[|m|], m in -7..7) to m - 1 or m + 1 at the element's
+ *     fixed group scale; it changes the objective by
+ *     D = d*d*H[k][k] - 2*d*g[k] (d = the value step, g = H e);
+ *   - each step takes the move with the most negative D (ties: lowest k,
+ *     then the downward move), and the row stops when no move has D < 0 or
+ *     after max_flips moves;
+ *   - all of it in fp64 with sums in index order: g[j] = sum over k of
+ *     e[k] * H[k][j] (k ascending), H[j][k] = sum over r of x~[r][j] *
+ *     x~[r][k] (r ascending); after a move g[j] -= d * H[k][j];
+ *   - an element that is moved gets its canonical code (m = 0 is code 0);
+ *     elements never moved keep their code bits (a -0 stays 0x8).
+ */
+
+/* H [K, K] (fp64) of R bf16 calibration rows through multiplier a and the
+   block-Hadamard of size b. */
+int oracle_hessian(const uint16_t* x, int64_t R, int64_t K, int64_t ldx, const float* a, int b, double* H) {
+  if (!x || !H || R < 1 || K < 32 || ldx < K || !valid_block(b)) return ORACLE_EINVAL;
+  if (b > 0 && K % b != 0) return ORACLE_EINVAL;
+  float* t = (float*)malloc((size_t)R * K * sizeof(float));
+  if (!t) return ORACLE_EINVAL;
+  for (int64_t r = 0; r < R; ++r) transform_row(x, 0, r * ldx, a, K, b, t + r * K);
+  for (int64_t j = 0; j < K; ++j)
+    for (int64_t k = 0; k < K; ++k) {
+      double acc = 0.0;
+      for (int64_t r = 0; r < R; ++r) acc += (double)t[r * K + j] * (double)t[r * K + k];
+      H[j * K + k] = acc;
+    }
+  free(t);
+  return ORACLE_OK;
+}
+
+/* signed E2M1 index of a code: -7..7 (code 8, -0, is index 0) */
+static int code_index(unsigned c) { return (c & 8) ? -(int)(c & 7) : (int)(c & 7); }
+static unsigned index_code(int m) { return m < 0 ? (8u | (unsigned)(-m)) : (unsigned)m; }
+static double index_value(int m) { return m < 0 ? -kE2M1[-m] : kE2M1[m]; }
+
+/* Flip-Refinement of N rows of prepared weights (row-major codes [N, K/2],
+   scales [N, K/32], refined in place): W [N, ldw] (dtype 0 bf16, 1 fp32),
+   weight multiplier r, block b, H [K, K]. flips[n] (optional) receives the
+   number of moves of row n. */
+int oracle_flip_refine(const void* W, int dtype, int64_t N, int64_t K, int64_t ldw, const float* r, int b,
+                       const double* H, int max_flips, uint8_t* codes, const uint8_t* scales, int32_t* flips) {
+  if (!W || !H || !codes || !scales || N < 1 || K < 32 || K % 32 != 0 || ldw < K || !valid_block(b) || max_flips < 0)
+    return ORACLE_EINVAL;
+  if (b > 0 && K % b != 0) return ORACLE_EINVAL;
+  float* wt = (float*)malloc((size_t)K * sizeof(float));
+  double* e = (double*)malloc((size_t)K * sizeof(double));
+  double* g = (double*)malloc((size_t)K * sizeof(double));
+  int* m = (int*)malloc((size_t)K * sizeof(int));
+  int* m0 = (int*)malloc((size_t)K * sizeof(int));
+  if (!wt || !e || !g || !m || !m0) {
+    free(wt); free(e); free(g); free(m); free(m0);
+    return ORACLE_EINVAL;
+  }
+  for (int64_t n = 0; n < N; ++n) {
+    uint8_t* crow = codes + n * (K / 2);
+    const uint8_t* srow = scales + n * (K / 32);
+    transform_row(W, dtype, n * ldw, r, K, b, wt);
+    for (int64_t k = 0; k < K; ++k) {
+      const unsigned c = (k % 2 == 0) ? (crow[k / 2] & 0xF) : (crow[k / 2] >> 4);
+      m[k] = m0[k] = code_index(c);
+      e[k] = (double)wt[k] - ldexp(index_value(m[k]), (int)srow[k / 32] - 127);
+    }
+    for (int64_t j = 0; j < K; ++j) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) acc += e[k] * H[k * K + j];
+      g[j] = acc;
+    }
+    int moves = 0;
+    while (moves < max_flips) {
+      double best = 0.0;
+      int64_t bk = -1;
+      int bdir = 0;
+      for (int64_t k = 0; k < K; ++k) {
+        for (int dir = -1; dir <= 1; dir += 2) {
+          const int mn = m[k] + dir;
+          if (mn < -7 || mn > 7) continue;
+          const double d = ldexp(index_value(mn) - index_value(m[k]), (int)srow[k / 32] - 127);
+          const double D = d * d * H[k * K + k] - 2.0 * d * g[k];
+          if (D < best) {
+            best = D;
+            bk = k;
+            bdir = dir;
+          }
+        }
+      }
+      if (bk < 0) break;
+      const double d = ldexp(index_value(m[bk] + bdir) - index_value(m[bk]), (int)srow[bk / 32] - 127);
+      m[bk] += bdir;
+      for (int64_t j = 0; j < K; ++j) g[j] -= d * H[bk * K + j];
+      ++moves;
+    }
+    for (int64_t k = 0; k < K; ++k) {
+      if (m[k] == m0[k]) continue;
+      const unsigned c = index_code(m[k]);
+      uint8_t* byte = crow + k / 2;
+      *byte = (k % 2 == 0) ? (uint8_t)((*byte & 0xF0) | c) : (uint8_t)((*byte & 0x0F) | (c << 4));
+    }
+    if (flips) flips[n] = moves;
+  }
+  free(wt); free(e); free(g); free(m); free(m0);
+  return ORACLE_OK;
+}
