@@ -276,6 +276,55 @@ macaq_status macaq_moe_block(const void* X, int64_t T, int64_t H, int64_t ldx, c
                              const uint8_t* wdn_scales, int64_t F, int32_t b, void* Y, macaq_dtype y_dtype,
                              int64_t ldy, void* workspace, size_t workspace_bytes, macaq_stream_t stream);
 
+/*
+ * ---- Flip-Refinement of prepared weights (offline) -------------------------
+ *
+ * "MACaQ ..." (paper card, Abstract) improves on round-to-nearest weights
+ * with Flip-Refinement, a Hessian-aware coordinate descent that greedily moves
+ * single FP4 codes to adjacent representable values; "Huawei's MACaQ-R beats
+ * Unsloth's ..." (What we found when we compared the files) sees only codes
+ * change, the block scales kept. Readings where the pages are silent:
+ *   - row n of the layer minimises e^T H e, e = w~ - q: w~ = S_b (r .* W[n, :])
+ *     in fp32 (what macaq_prepare_weights quantizes), q its dequantized codes,
+ *     H = X~^T X~ with x~ = S_b (a .* x) of calibration rows (w~.x~ = w.x, so
+ *     e.x~ is the row's output error on a calibration row);
+ *   - a move takes one element's signed E2M1 index m (-7 .. 7) to m - 1 or
+ *     m + 1 at its group's scale, changing the objective by
+ *     d*d*H[k][k] - 2*d*g[k] with g = H e; each step takes the most negative
+ *     change (ties: lowest k, then the downward move) until none is negative
+ *     or max_flips moves are made;
+ *   - everything in fp64 with sums in index order, so the result is
+ *     reproducible bit for bit; moved elements get the canonical code of
+ *     their index, the others keep their bits.
+ */
+
+/* Bytes of workspace for macaq_hessian: R x K fp32. */
+size_t macaq_hessian_workspace_size(int64_t R, int64_t K);
+
+/*
+ * H = X~^T X~ (fp64 [K, K], row-major) of R bf16 calibration rows X [R, ldx]
+ * through the activation multiplier a (device fp32 [K], or NULL with b = 0)
+ * and the block-Hadamard of size b. H: device, K*K doubles, 16-byte aligned.
+ */
+macaq_status macaq_hessian(const void* Xcal, int64_t R, int64_t K, int64_t ldx, const float* a, int32_t b, double* H,
+                           void* workspace, size_t workspace_bytes, macaq_stream_t stream);
+
+/* Bytes of workspace for macaq_flip_refine: 2 x N x K fp64 + K fp64. */
+size_t macaq_flip_refine_workspace_size(int64_t N, int64_t K);
+
+/*
+ * Flip-Refinement of prepared weights in place: W [N, ldw] (bf16 or fp32, the
+ * rows given to macaq_prepare_weights with the same r and b), H from
+ * macaq_hessian with the matching a, w_codes / w_scales from
+ * macaq_prepare_weights (MACAQ_GEMM_LAYOUT; codes rewritten, scales read
+ * only). flips: device int32 [N] receiving each row's number of moves, or
+ * NULL. max_flips >= 0 caps the moves per row (0 leaves the codes as they
+ * are). Limits: K <= 32768, K a multiple of 32 and of b.
+ */
+macaq_status macaq_flip_refine(const void* W, macaq_dtype w_dtype, int64_t N, int64_t K, int64_t ldw, const float* r,
+                               int32_t b, const double* H, int32_t max_flips, uint8_t* w_codes, const uint8_t* w_scales,
+                               int32_t* flips, void* workspace, size_t workspace_bytes, macaq_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -53,6 +53,11 @@ _SIGNATURES = {
                                               ctypes.c_int, _i64, _vp, _sz, _vp]),
     "macaq_moe_block": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _i64, _i32, _vp, ctypes.c_int, _i64, _vp, _sz, _vp]),
+    "macaq_hessian_workspace_size": (_sz, [_i64, _i64]),
+    "macaq_hessian": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "macaq_flip_refine_workspace_size": (_sz, [_i64, _i64]),
+    "macaq_flip_refine": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _vp, _vp, _vp,
+                                         _vp, _sz, _vp]),
 }
 
 
@@ -428,3 +433,33 @@ def prepare_moe(w_gate: torch.Tensor, w_up: torch.Tensor, w_dn: torch.Tensor, xc
         a_dn[e] = a
         prepare_weights(w_dn[e], r, b, out=expert(wdn, e))
     return MoELayer(a_gu, wgu, a_dn, wdn, b)
+
+
+# ---- Flip-Refinement (offline) ---------------------------------------------
+
+def hessian(xcal: torch.Tensor, a: torch.Tensor | None, b: int) -> torch.Tensor:
+    """H = X~^T X~ (fp64 [K, K]) of bf16 calibration rows through a and the
+    block-Hadamard of size b."""
+    _need_cuda(xcal, a)
+    assert xcal.dtype == torch.bfloat16 and xcal.dim() == 2 and xcal.stride(1) == 1
+    R, K = xcal.shape
+    H = torch.empty(K, K, dtype=torch.float64, device=xcal.device)
+    ws = _workspace(int(load_library().macaq_hessian_workspace_size(R, K)), xcal.device, None)
+    _check(load_library().macaq_hessian(_ptr(xcal), R, K, xcal.stride(0), _ptr(a), b, _ptr(H), _ptr(ws), ws.numel(),
+                                        _stream(xcal)), "macaq_hessian")
+    return H
+
+
+def flip_refine(w: torch.Tensor, r: torch.Tensor | None, b: int, H: torch.Tensor, max_flips: int, packed: Packed,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Refine packed (from prepare_weights(w, r, b)) in place; returns the
+    number of moves of every row (int32 [N])."""
+    _need_cuda(w, r, H, packed.codes, packed.scales)
+    assert w.dim() == 2 and w.stride(1) == 1 and H.dtype == torch.float64 and H.is_contiguous()
+    N, K = w.shape
+    flips = torch.empty(N, dtype=torch.int32, device=w.device)
+    ws = _workspace(int(load_library().macaq_flip_refine_workspace_size(N, K)), w.device, workspace)
+    _check(load_library().macaq_flip_refine(_ptr(w), _dtype_code(w.dtype), N, K, w.stride(0), _ptr(r), b, _ptr(H),
+                                            max_flips, _ptr(packed.codes), _ptr(packed.scales), _ptr(flips),
+                                            _ptr(ws), ws.numel(), _stream(w)), "macaq_flip_refine")
+    return flips

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmacaq.so")
-SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "moe.hip"]
+SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "moe.hip", "refine.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

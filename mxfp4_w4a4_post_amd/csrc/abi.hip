@@ -79,6 +79,9 @@ LinearWs linear_ws(int64_t M, int64_t K, size_t extra_bytes) {
   return w;
 }
 
+// Flip-Refinement keeps a row's state in the registers of 1024 threads.
+constexpr int64_t kMaxRefineK = 32768;
+
 // The GEMM addresses each packed operand through a 32-bit buffer range.
 constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - (int64_t(1) << 20);
 bool operand_fits(int64_t rows, int64_t K) { return tiled_codes_bytes(rows, K) <= kMaxOperandBytes; }
@@ -610,6 +613,68 @@ macaq_status macaq_moe_block(const void* X, int64_t T, int64_t H, int64_t ldx, c
   e = moe_down_combine_launch(ws + w.dn_codes, ws + w.dn_scales, offsets, pos, w_route, T, k, E, wdn_codes,
                               wdn_scales, H, F, Y, y_dtype, ldy, ws, w, !same_bm, s);
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_block down/combine launch");
+}
+
+size_t macaq_hessian_workspace_size(int64_t R, int64_t K) {
+  if (R <= 0 || K <= 0) return 0;
+  return round_up((size_t)R * (size_t)K * sizeof(float), kWsAlign);
+}
+
+macaq_status macaq_hessian(const void* Xcal, int64_t R, int64_t K, int64_t ldx, const float* a, int32_t b, double* H,
+                           void* workspace, size_t workspace_bytes, macaq_stream_t stream) {
+  const char* who = "macaq_hessian";
+  if (R < 1) return fail(MACAQ_EINVAL, "%s: R = %lld < 1", who, (long long)R);
+  macaq_status st = check_quant_shape(R, K, ldx, b, who);
+  if (st != MACAQ_OK) return st;
+  if (K > kMaxRefineK) return fail(MACAQ_EINVAL, "%s: K = %lld > %lld", who, (long long)K, (long long)kMaxRefineK);
+  if (!Xcal || !H) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (!a && b != 0) return fail(MACAQ_EINVAL, "%s: a is required when b > 0", who);
+  if (!aligned(Xcal, 16) || ldx % 8 != 0 || (a && !aligned(a, 16)) || !aligned(H, 16))
+    return fail(MACAQ_EALIGN, "%s: Xcal, a and H must be 16-byte aligned and ldx a multiple of 8", who);
+  const size_t need = macaq_hessian_workspace_size(R, K);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign))
+    return fail(MACAQ_EWORKSPACE, "%s: need %zu workspace bytes, 256-byte aligned", who, need);
+  st = check_device();
+  if (st != MACAQ_OK) return st;
+  hipError_t e = launch_hessian(Xcal, R, K, ldx, a, b, static_cast<float*>(workspace), H,
+                                reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_hessian launch");
+}
+
+size_t macaq_flip_refine_workspace_size(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return 2 * round_up((size_t)N * (size_t)K * sizeof(double), kWsAlign) + round_up((size_t)K * sizeof(double), kWsAlign);
+}
+
+macaq_status macaq_flip_refine(const void* W, macaq_dtype w_dtype, int64_t N, int64_t K, int64_t ldw, const float* r,
+                               int32_t b, const double* H, int32_t max_flips, uint8_t* w_codes, const uint8_t* w_scales,
+                               int32_t* flips, void* workspace, size_t workspace_bytes, macaq_stream_t stream) {
+  const char* who = "macaq_flip_refine";
+  if (N < 1) return fail(MACAQ_EINVAL, "%s: N = %lld < 1", who, (long long)N);
+  macaq_status st = check_quant_shape(N, K, ldw, b, who);
+  if (st != MACAQ_OK) return st;
+  if (K > kMaxRefineK) return fail(MACAQ_EINVAL, "%s: K = %lld > %lld", who, (long long)K, (long long)kMaxRefineK);
+  if (w_dtype != MACAQ_BF16 && w_dtype != MACAQ_F32) return fail(MACAQ_EINVAL, "%s: bad weight dtype", who);
+  if (max_flips < 0) return fail(MACAQ_EINVAL, "%s: max_flips < 0", who);
+  if (!W || !H || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (!r && b != 0) return fail(MACAQ_EINVAL, "%s: r is required when b > 0", who);
+  if (!operand_fits(N, K)) return fail(MACAQ_EINVAL, "%s: packed operand over 2 GiB", who);
+  const int64_t vec = w_dtype == MACAQ_F32 ? 4 : 8;
+  if (!aligned(W, 16) || ldw % vec != 0 || (r && !aligned(r, 16)) || !aligned(H, 16) || !aligned(w_codes, 16) ||
+      !aligned(w_scales, 16) || (flips && !aligned(flips, 4)))
+    return fail(MACAQ_EALIGN, "%s: W, r, H and the packed weights 16-byte aligned, ldw a multiple of %lld", who,
+                (long long)vec);
+  const size_t need = macaq_flip_refine_workspace_size(N, K);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign))
+    return fail(MACAQ_EWORKSPACE, "%s: need %zu workspace bytes, 256-byte aligned", who, need);
+  st = check_device();
+  if (st != MACAQ_OK) return st;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t mat = round_up((size_t)N * (size_t)K * sizeof(double), kWsAlign);
+  hipError_t e = launch_flip_refine(W, w_dtype == MACAQ_F32, N, K, ldw, r, b, H, max_flips, w_codes, w_scales, flips,
+                                    reinterpret_cast<double*>(ws), reinterpret_cast<double*>(ws + mat),
+                                    reinterpret_cast<double*>(ws + 2 * mat), reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_flip_refine launch");
 }
 
 }  // extern "C"

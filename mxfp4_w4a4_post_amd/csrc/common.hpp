@@ -145,4 +145,12 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t
 hipError_t launch_moe_combine(const uint16_t* rows, int64_t H, const int32_t* pos, const float* w, int64_t T, int k,
                               void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
 
+// Flip-Refinement: the Hessian of transformed calibration rows (xt: R x K fp32
+// scratch) and the greedy code moves (E, G: N x K fp64 scratch, hdiag: K).
+hipError_t launch_hessian(const void* xcal, int64_t R, int64_t K, int64_t ldx, const float* a, int b, float* xt,
+                          double* H, hipStream_t stream);
+hipError_t launch_flip_refine(const void* W, bool w_f32, int64_t N, int64_t K, int64_t ldw, const float* r, int b,
+                              const double* H, int max_flips, uint8_t* codes, const uint8_t* scales, int32_t* flips,
+                              double* E, double* G, double* hdiag, hipStream_t stream);
+
 }  // namespace macaq

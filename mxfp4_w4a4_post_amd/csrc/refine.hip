@@ -1,0 +1,360 @@
+// Flip-Refinement of prepared MXFP4 weights (gfx950): the Hessian of the
+// transformed calibration rows, and greedy single-code moves that lower each
+// weight row's output error with the block scales kept.
+//
+// "MACaQ: Fast, Model Agnostic Calibrated Quantization for Low-Precision
+// Weights and Activations" (paper card, Abstract) improves on round-to-nearest
+// weights with a Hessian-aware coordinate descent that greedily moves single
+// FP4 codes to adjacent representable values; "Huawei's MACaQ-R beats
+// Unsloth's ..." (What we found when we compared the files) sees only codes
+// change, never the block scales. The objective, move order and stopping
+// rule are readings: row n minimises e^T H e, e = w~ - q in the transformed
+// basis (w~ = S_b (r .* w) in fp32, q its dequantized codes), H = X~^T X~ of
+// the transformed calibration rows; a step takes the adjacent move with the
+// most negative change d^2 H[k][k] - 2 d g[k] (g = H e; ties: lowest k, then
+// the downward move) until none is negative or max_flips moves are made.
+// Every sum runs in index order in fp64 with separate multiply and add, so the
+// decisions are reproducible bit for bit.
+#include "mx_lane.hpp"
+
+namespace macaq {
+namespace {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Value of E2M1 magnitude code c (0 .. 7): 0, .5, 1, 1.5, 2, 3, 4, 6 (exact).
+__device__ __forceinline__ double e2m1_mag(int c) {
+  return c < 4 ? 0.5 * c : ldexp((c & 1) ? 1.5 : 1.0, (c >> 1) - 1);
+}
+// Signed index m in -7 .. 7 of a 4-bit code (the -0 code 8 is index 0) and back.
+__device__ __forceinline__ int code_index(uint32_t c) { return (c & 8) ? -(int)(c & 7) : (int)(c & 7); }
+__device__ __forceinline__ uint32_t index_code(int m) { return m < 0 ? (8u | (uint32_t)(-m)) : (uint32_t)m; }
+__device__ __forceinline__ double index_value(int m) { return m < 0 ? -e2m1_mag(-m) : e2m1_mag(m); }
+
+// Rows through the multiplier and the block-Hadamard, one lane per 32-element
+// chunk exactly as the quantizer does it (workgroup = 32 rows x 256 elements).
+// OUT_E: write e = w~ - dequant(codes) in fp64 (codes and scales of the rows
+// in the GEMM layout); otherwise write the fp32 transformed rows.
+template <bool F32_IN, int B, bool OUT_E>
+__global__ __launch_bounds__(256) void transform_kernel(const void* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+                                                        const float* __restrict__ mult,
+                                                        const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scales, float* __restrict__ out32,
+                                                        double* __restrict__ out64) {
+  const int tid = threadIdx.x;
+  const int c = tid & 7;
+  const int64_t row = (int64_t)blockIdx.x * kGroupRows + (tid >> 3);
+  const int64_t k0 = (int64_t)blockIdx.y * kBlockK + c * 32;
+  const bool valid = row < M && k0 < K;
+  float v[32];
+  if (valid) {
+    if constexpr (F32_IN) {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + row * ldx + k0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 u = p[i];
+        v[4 * i] = u.x;
+        v[4 * i + 1] = u.y;
+        v[4 * i + 2] = u.z;
+        v[4 * i + 3] = u.w;
+      }
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + row * ldx + k0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 w = p[i];
+        const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * i + 2 * j] = bf16_lo(q[j]);
+          v[8 * i + 2 * j + 1] = bf16_hi(q[j]);
+        }
+      }
+    }
+    if (mult) {
+      const float4* mp = reinterpret_cast<const float4*>(mult + k0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 u = mp[i];
+        v[4 * i] *= u.x;
+        v[4 * i + 1] *= u.y;
+        v[4 * i + 2] *= u.z;
+        v[4 * i + 3] *= u.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  }
+  fwht_lane<B>(v, c);
+  if (!valid) return;
+  if constexpr (OUT_E) {
+    const int64_t kpad = pad_k(K);
+    const uint4 cw = *reinterpret_cast<const uint4*>(codes + tiled_code_offset(row, k0, kpad));
+    const int sc = scales[tiled_scale_offset(row, k0, kpad)];
+    const uint32_t cb[4] = {cw.x, cw.y, cw.z, cw.w};
+    double* o = out64 + row * K + k0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t nib = (cb[i >> 3] >> (4 * (i & 7))) & 0xF;
+      o[i] = (double)v[i] - ldexp(index_value(code_index(nib)), sc - 127);
+    }
+  } else {
+    float4* o = reinterpret_cast<float4*>(out32 + row * K + k0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  }
+}
+
+// C[i][j] = sum over t (ascending) of A(t, i) * B(t, j) in fp64, one 64 x 64
+// output tile per workgroup, each thread 4 x 4 outputs, t staged 16 at a time
+// through LDS. The products and the running sums round one at a time, in t
+// order, so every output equals the plain sequential sum. The two instances:
+//   Hessian: A = B = the fp32 transformed rows [R, K]:  H[j][k] = sum_r x~[r][j] x~[r][k];
+//   gradient: A = E^T (E [N, K] fp64), B = H:          G[n][j] = sum_k E[n][k] H[k][j].
+constexpr int kTile = 64, kChunk = 16;
+
+template <bool HESSIAN>
+__global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt, const double* __restrict__ e,
+                                                   const double* __restrict__ h, int64_t rows_i, int64_t cols_j,
+                                                   int64_t len_t, double* __restrict__ out) {
+  __shared__ double as[kChunk][kTile + 1];  // padded: the gradient's A is written along t
+  __shared__ double bs[kChunk][kTile];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int64_t i0 = (int64_t)blockIdx.y * kTile, j0 = (int64_t)blockIdx.x * kTile;
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  for (int64_t t0 = 0; t0 < len_t; t0 += kChunk) {
+    // stage 16 x 64 values of A and of B, 4 each per thread; loads run along
+    // the contiguous dimension (i of the rows x~, t of E, j of H)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q;
+      if constexpr (HESSIAN) {
+        const int tt = idx >> 6, col = idx & 63;
+        const int64_t t = t0 + tt;
+        as[tt][col] = (t < len_t && i0 + col < rows_i) ? (double)xt[t * rows_i + i0 + col] : 0.0;
+        bs[tt][col] = (t < len_t && j0 + col < cols_j) ? (double)xt[t * cols_j + j0 + col] : 0.0;
+      } else {
+        const int tt_a = idx & 15, col_a = idx >> 4;
+        const int64_t ta = t0 + tt_a;
+        as[tt_a][col_a] = (ta < len_t && i0 + col_a < rows_i) ? e[(i0 + col_a) * len_t + ta] : 0.0;
+        const int tt_b = idx >> 6, col_b = idx & 63;
+        const int64_t tb = t0 + tt_b;
+        bs[tt_b][col_b] = (tb < len_t && j0 + col_b < cols_j) ? h[tb * cols_j + j0 + col_b] : 0.0;
+      }
+    }
+    __syncthreads();
+    const int nt = (int)(len_t - t0 < kChunk ? len_t - t0 : kChunk);
+    for (int tt = 0; tt < nt; ++tt) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) av[a] = as[tt][ty * 4 + a];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bv[b] = bs[tt][tx * 4 + b];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = acc[a][b] + av[a] * bv[b];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int64_t i = i0 + ty * 4 + a;
+    if (i >= rows_i) continue;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t j = j0 + tx * 4 + b;
+      if (j < cols_j) out[i * cols_j + j] = acc[a][b];
+    }
+  }
+}
+
+__global__ void hdiag_kernel(const double* __restrict__ h, int64_t K, double* __restrict__ d) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k < K) d[k] = h[k * K + k];
+}
+
+// The greedy moves of one weight row per workgroup (1024 threads). Thread t
+// owns the element pairs p = t + 1024 i (elements 2p, 2p + 1, one code byte,
+// one scale) for i < P, holding g and the signed indices in registers.
+constexpr int kFlipThreads = 1024;
+
+struct Cand {
+  double D;
+  int k, dir;
+};
+__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
+  return a.D < b.D || (a.D == b.D && (a.k < b.k || (a.k == b.k && a.dir < b.dir)));
+}
+__device__ __forceinline__ Cand shfl_xor_cand(const Cand& c, int m) {
+  Cand o;
+  o.D = __shfl_xor(c.D, m);
+  o.k = __shfl_xor(c.k, m);
+  o.dir = __shfl_xor(c.dir, m);
+  return o;
+}
+
+template <int P>
+__global__ __launch_bounds__(kFlipThreads) void flip_kernel(const double* __restrict__ G, const double* __restrict__ H,
+                                                           const double* __restrict__ hdiag, int64_t N, int64_t K,
+                                                           int max_flips, uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales,
+                                                           int32_t* __restrict__ flips) {
+  __shared__ Cand slot[2][kFlipThreads / 64];
+  __shared__ double dsh[2];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t n = blockIdx.x;
+  const int64_t kpad = pad_k(K);
+  // per pair: g of both elements, and one state word: bits 0-3 / 4-7 the
+  // current signed indices + 7, bits 8-11 / 12-15 the original ones + 7,
+  // bits 16-23 the scale byte
+  double g[P][2];
+  uint32_t st[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int64_t k = 2 * ((int64_t)tid + (int64_t)kFlipThreads * i);
+    if (k < K) {
+      const double2 gv = *reinterpret_cast<const double2*>(G + n * K + k);
+      g[i][0] = gv.x;
+      g[i][1] = gv.y;
+      const uint32_t byte = codes[tiled_code_offset(n, k, kpad)];
+      const uint32_t lo = (uint32_t)(code_index(byte & 0xF) + 7), hi = (uint32_t)(code_index(byte >> 4) + 7);
+      st[i] = lo | (hi << 4) | (lo << 8) | (hi << 12) | ((uint32_t)scales[tiled_scale_offset(n, k, kpad)] << 16);
+    } else {
+      g[i][0] = g[i][1] = 0.0;
+      st[i] = 7u | (7u << 4) | (7u << 8) | (7u << 12);
+    }
+  }
+  int moves = 0;
+  for (int par = 0; moves < max_flips; par ^= 1) {
+    Cand best{0.0, (int)K, 0};
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int64_t k = 2 * ((int64_t)tid + (int64_t)kFlipThreads * i);
+      if (k >= K) continue;
+      const double2 hk = *reinterpret_cast<const double2*>(hdiag + k);
+      const double hkk[2] = {hk.x, hk.y};
+      const int sc = (int)((st[i] >> 16) & 0xFF);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int mc = (int)((st[i] >> (4 * s)) & 0xF) - 7;
+#pragma unroll
+        for (int dir = -1; dir <= 1; dir += 2) {
+          const int mn = mc + dir;
+          if (mn < -7 || mn > 7) continue;
+          const double d = ldexp(index_value(mn) - index_value(mc), sc - 127);
+          const double D = d * d * hkk[s] - 2.0 * d * g[i][s];
+          if (D < best.D) best = Cand{D, (int)(k + s), dir};
+        }
+      }
+    }
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) {
+      const Cand o = shfl_xor_cand(best, msk);
+      if (better(o, best)) best = o;
+    }
+    if (lane == 0) slot[par][wave] = best;
+    __syncthreads();
+    best = slot[par][0];
+#pragma unroll
+    for (int w = 1; w < kFlipThreads / 64; ++w)
+      if (better(slot[par][w], best)) best = slot[par][w];
+    if (best.k >= K) break;  // no move lowers the objective (uniform)
+    // the owner of element best.k applies the move and publishes its step
+    const int64_t pidx = best.k >> 1;
+    if (pidx % kFlipThreads == tid) {
+      const int i = (int)(pidx / kFlipThreads), s = best.k & 1;
+#pragma unroll
+      for (int ii = 0; ii < P; ++ii)
+        if (ii == i) {
+          const int mc = (int)((st[ii] >> (4 * s)) & 0xF) - 7;
+          const int mn = mc + best.dir;
+          dsh[par] = ldexp(index_value(mn) - index_value(mc), (int)((st[ii] >> 16) & 0xFF) - 127);
+          st[ii] = (st[ii] & ~(0xFu << (4 * s))) | ((uint32_t)(mn + 7) << (4 * s));
+        }
+    }
+    __syncthreads();
+    const double d = dsh[par];
+    const double* hr = H + (int64_t)best.k * K;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int64_t k = 2 * ((int64_t)tid + (int64_t)kFlipThreads * i);
+      if (k >= K) continue;
+      const double2 hv = *reinterpret_cast<const double2*>(hr + k);
+      g[i][0] = g[i][0] - d * hv.x;
+      g[i][1] = g[i][1] - d * hv.y;
+    }
+    ++moves;
+  }
+  // moved elements take the canonical code of their index; the rest keep their bits
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int64_t k = 2 * ((int64_t)tid + (int64_t)kFlipThreads * i);
+    const uint32_t cur = st[i] & 0xFF, orig = (st[i] >> 8) & 0xFF;
+    if (k >= K || cur == orig) continue;
+    uint8_t* bp = codes + tiled_code_offset(n, k, kpad);
+    uint32_t byte = *bp;
+    if ((cur & 0xF) != (orig & 0xF)) byte = (byte & 0xF0u) | index_code((int)(cur & 0xF) - 7);
+    if ((cur >> 4) != (orig >> 4)) byte = (byte & 0x0Fu) | (index_code((int)(cur >> 4) - 7) << 4);
+    *bp = (uint8_t)byte;
+  }
+  if (tid == 0 && flips) flips[n] = moves;
+}
+
+template <bool F32_IN, bool OUT_E>
+hipError_t launch_transform(const void* x, int64_t M, int64_t K, int64_t ldx, const float* mult, int b,
+                            const uint8_t* codes, const uint8_t* scales, float* out32, double* out64,
+                            hipStream_t stream) {
+  const dim3 grid((unsigned)((M + kGroupRows - 1) / kGroupRows), (unsigned)((K + kBlockK - 1) / kBlockK));
+  switch (b) {
+    case 0: hipLaunchKernelGGL((transform_kernel<F32_IN, 0, OUT_E>), grid, dim3(256), 0, stream, x, M, K, ldx, mult,
+                               codes, scales, out32, out64); break;
+    case 32: hipLaunchKernelGGL((transform_kernel<F32_IN, 32, OUT_E>), grid, dim3(256), 0, stream, x, M, K, ldx, mult,
+                                codes, scales, out32, out64); break;
+    case 64: hipLaunchKernelGGL((transform_kernel<F32_IN, 64, OUT_E>), grid, dim3(256), 0, stream, x, M, K, ldx, mult,
+                                codes, scales, out32, out64); break;
+    default: hipLaunchKernelGGL((transform_kernel<F32_IN, 128, OUT_E>), grid, dim3(256), 0, stream, x, M, K, ldx,
+                                mult, codes, scales, out32, out64); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_hessian(const void* xcal, int64_t R, int64_t K, int64_t ldx, const float* a, int b, float* xt,
+                          double* H, hipStream_t stream) {
+  hipError_t e = launch_transform<false, false>(xcal, R, K, ldx, a, b, nullptr, nullptr, xt, nullptr, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((K + kTile - 1) / kTile), (unsigned)((K + kTile - 1) / kTile));
+  hipLaunchKernelGGL((gram_kernel<true>), grid, dim3(256), 0, stream, xt, nullptr, nullptr, K, K, R, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_flip_refine(const void* W, bool w_f32, int64_t N, int64_t K, int64_t ldw, const float* r, int b,
+                              const double* H, int max_flips, uint8_t* codes, const uint8_t* scales, int32_t* flips,
+                              double* E, double* G, double* hdiag, hipStream_t stream) {
+  hipError_t e = w_f32 ? launch_transform<true, true>(W, N, K, ldw, r, b, codes, scales, nullptr, E, stream)
+                       : launch_transform<false, true>(W, N, K, ldw, r, b, codes, scales, nullptr, E, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((K + kTile - 1) / kTile), (unsigned)((N + kTile - 1) / kTile));
+  hipLaunchKernelGGL((gram_kernel<false>), grid, dim3(256), 0, stream, nullptr, E, H, N, K, K, G);
+  hipLaunchKernelGGL(hdiag_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream, H, K, hdiag);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t pairs = (K / 2 + kFlipThreads - 1) / kFlipThreads;
+  const dim3 fg((unsigned)N), fb(kFlipThreads);
+  if (pairs <= 1) hipLaunchKernelGGL(flip_kernel<1>, fg, fb, 0, stream, G, H, hdiag, N, K, max_flips, codes, scales, flips);
+  else if (pairs <= 2) hipLaunchKernelGGL(flip_kernel<2>, fg, fb, 0, stream, G, H, hdiag, N, K, max_flips, codes, scales, flips);
+  else if (pairs <= 4) hipLaunchKernelGGL(flip_kernel<4>, fg, fb, 0, stream, G, H, hdiag, N, K, max_flips, codes, scales, flips);
+  else if (pairs <= 8) hipLaunchKernelGGL(flip_kernel<8>, fg, fb, 0, stream, G, H, hdiag, N, K, max_flips, codes, scales, flips);
+  else hipLaunchKernelGGL(flip_kernel<16>, fg, fb, 0, stream, G, H, hdiag, N, K, max_flips, codes, scales, flips);
+  return hipGetLastError();
+}
+
+}  // namespace macaq

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding._SIGNATURES), "binding signatures out of sync with the header"
@@ -191,3 +191,28 @@ def test_moe_calls_reject(lib):
     need = lib.macaq_moe_workspace_size(16, 2, 8, 256, 128)
     assert need > 0 and block(wsb=need - 1) == EWORKSPACE
     assert lib.macaq_moe_workspace_size(0, 2, 8, 256, 128) == 0
+
+
+def test_refine_calls_reject(lib):
+    ws = 1 << 30
+    H = lib.macaq_hessian
+    assert H(FAKE, 0, 64, 64, FAKE, 32, FAKE, FAKE, ws, None) == EINVAL      # R < 1
+    assert H(FAKE, 8, 48, 48, FAKE, 32, FAKE, FAKE, ws, None) == EINVAL      # K % 32
+    assert H(FAKE, 8, 65536, 65536, FAKE, 32, FAKE, FAKE, ws, None) == EINVAL  # K too large
+    assert H(FAKE, 8, 64, 64, None, 32, FAKE, FAKE, ws, None) == EINVAL      # a needed
+    assert H(FAKE, 8, 64, 64, FAKE, 32, FAKE + 8, FAKE, ws, None) == EALIGN
+    assert H(FAKE, 8, 64, 64, FAKE, 32, FAKE, FAKE, 16, None) == EWORKSPACE
+    assert lib.macaq_hessian_workspace_size(8, 64) == 8 * 64 * 4 + (256 - 8 * 64 * 4 % 256) % 256
+    F = lib.macaq_flip_refine
+
+    def f(N=8, K=64, ldw=64, dt=0, b=32, cap=4, r=FAKE, W=FAKE, wsb=ws):
+        return F(W, dt, N, K, ldw, r, b, FAKE, cap, FAKE, FAKE, None, FAKE, wsb, None)
+
+    assert f(cap=-1) == EINVAL
+    assert f(dt=7) == EINVAL
+    assert f(r=None) == EINVAL
+    assert f(K=96, ldw=96, b=64) == EINVAL
+    assert f(W=FAKE + 4) == EALIGN
+    assert f(dt=1, ldw=66) == EALIGN
+    assert f(wsb=100) == EWORKSPACE
+    assert lib.macaq_flip_refine_workspace_size(8, 64) >= 2 * 8 * 64 * 8 + 64 * 8
