@@ -10,7 +10,9 @@ decode-32b (M = 1, 8, 32, 64 through 5120x25600 and 25600x5120), moe-128e
 experts), moe-block (the same 4096 tokens through the whole MoE block:
 routing, gathered gate/up with the SwiGLU epilogue that quantizes the down
 input, down, weighted top-8 combine), prefill-large (M = 8192 through
-8192x28672 and 28672x8192, Hadamard block from --block) and tiny.
+8192x28672 and 28672x8192, Hadamard block from --block), refine-8b (offline
+Flip-Refinement of the prefill layers' weights: Hessian of 512 transformed
+calibration rows, up to 64 greedy code moves per weight row) and tiny.
 
 Inputs are resident in HBM; the timed steps rotate through several copies of
 activations and weights so that no step finds its operands in the 256 MB
@@ -39,7 +41,12 @@ PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ROTATE = 4                  # operand copies cycled through by the timed steps
 ORACLE_THREADS_CAP = 16     # the GPU machine's CPU share for one GPU
-WORKLOADS = {"tiny": 1, "prefill-8b": 2, "decode-32b": 3, "moe-128e": 4, "prefill-large": 5, "moe-block": 6}
+WORKLOADS = {"tiny": 1, "prefill-8b": 2, "decode-32b": 3, "moe-128e": 4, "prefill-large": 5, "moe-block": 6,
+             "refine-8b": 7}
+REFINE = 7  # offline Flip-Refinement of the prefill 8B-shaped layers' weights
+REFINE_ROWS = 512  # calibration rows of the Hessian
+REFINE_CAP = 64    # moves per weight row
+PEAK_FP64_TFLOPS = 78.6
 MOE_BLOCK = 6  # the MoE workload as a whole block: routing, gathered gate/up + SwiGLU, down, combine
 
 
@@ -225,6 +232,101 @@ def moe_block_entries(torch, binding, inputs, b, dev):
     return [e]
 
 
+def refine_main(args, torch, binding, inputs, dev):
+    """Offline Flip-Refinement of the prefill 8B-shaped layers: per step and
+    layer, the Hessian of the calibration rows and the refinement of freshly
+    prepared (round-to-nearest) codes. Timed with HIP events, eagerly."""
+    import numpy as np
+    spec = inputs.CONFIGS[2]
+    b = args.block if args.block is not None else spec["blocks"][0]
+    layers = []
+    for si, (K, N) in enumerate(spec["shapes"]):
+        case = inputs.linear_case(2, si, M=16, b=b)
+        w = case.w.to(dev)
+        a, r = binding.make_multipliers(binding.calibrate(case.xcal.to(dev)), b)
+        xcal = inputs.activations(2, si, REFINE_ROWS, K, stream=1).to(dev)
+        rtn = binding.prepare_weights(w, r, b)
+        work = torch.empty(binding.load_library().macaq_flip_refine_workspace_size(N, K), dtype=torch.uint8,
+                           device=dev)
+        layers.append(dict(K=K, N=N, w=w, a=a, r=r, xcal=xcal, rtn=rtn, work=work,
+                           packed=packed_clone(binding, rtn)))
+    flops_h = sum(2.0 * REFINE_ROWS * L["K"] ** 2 for L in layers)
+    flops_g = sum(2.0 * L["N"] * L["K"] ** 2 for L in layers)
+
+    def step(parts=("hessian", "refine")):
+        out = []
+        for L in layers:
+            L["packed"].codes.copy_(L["rtn"].codes)
+            if "hessian" in parts:
+                L["H"] = binding.hessian(L["xcal"], L["a"], b)
+            if "refine" in parts:
+                out.append(binding.flip_refine(L["w"], L["r"], b, L["H"], REFINE_CAP, L["packed"],
+                                               workspace=L["work"]))
+        return out
+
+    flips = step()
+    for _ in range(max(args.warmup, 1) - 1):
+        step()
+    torch.cuda.synchronize()
+
+    def timed(parts):
+        with Timer(torch) as t:
+            for _ in range(args.steps):
+                step(parts)
+        torch.cuda.synchronize()
+        return t.ms() / args.steps
+
+    steps = args.steps = max(1, min(args.steps, 10))
+    ms = timed(("hessian", "refine"))
+    ms_h = timed(("hessian",))
+    ms_r = max(ms - ms_h, 1e-6)
+    fl = torch.cat(flips).float().cpu().numpy()
+    value = (flops_h + flops_g) / (ms * 1e-3) / 1e12
+    g_tf = flops_g / (ms_r * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64 (Hessian, gradient and move decisions), MXFP4 codes",
+        "data": "synthetic (seeded prefill 8B-shaped weights and calibration rows; recipe in inputs.py)",
+        "config": {"workload": "refine-8b: Flip-Refinement of the prefill 8B-shaped layers (K, N) in %s, Hessian of "
+                               "%d calibration rows, up to %d moves per row, Hadamard block %d"
+                               % (spec["shapes"], REFINE_ROWS, REFINE_CAP, b),
+                   "layers": [list(x) for x in spec["shapes"]], "calibration_rows": REFINE_ROWS,
+                   "max_flips": REFINE_CAP, "hadamard_block": b},
+        "hessian_ms_per_step": round(ms_h, 4), "refine_ms_per_step": round(ms_r, 4),
+        "weight_rows_per_s": round(sum(L["N"] for L in layers) / (ms * 1e-3), 1),
+        "moves_per_row_mean": round(float(fl.mean()), 2), "rows_at_cap_pct": round(100.0 * float((fl >= REFINE_CAP).mean()), 2),
+        "roofline": {"bound": "alu", "achieved": round(g_tf, 3), "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(g_tf / PEAK_FP64_TFLOPS, 4), "traffic": None,
+                     "kernel": "macaq_flip_refine (flops: the gradient G = E H, 2 N K^2 in fp64, per call)"},
+        "timing": "HIP events on the launch stream around %d eager steps; each step restores the round-to-nearest "
+                  "codes (a device copy) before refining" % steps,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        L = layers[0]
+        K = L["K"]
+        threads = min(oracle.default_threads(), ORACLE_THREADS_CAP)
+        case = inputs.linear_case(2, 0, M=16, b=b)
+        a_o, r_o = oracle.multipliers(oracle.calibrate(inputs.bf16_bits(case.xcal)), b)
+        t0 = time.perf_counter()
+        hrows = 128
+        H = oracle.hessian(inputs.bf16_bits(inputs.activations(2, 0, hrows, K, stream=1)), a_o, b)
+        th = time.perf_counter() - t0
+        wb = inputs.bf16_bits(case.w)
+        codes, scales = oracle.prepare_weights(wb, r_o, b)
+        rows = 4
+        t0 = time.perf_counter()
+        oracle.flip_refine(wb[:rows], r_o, b, H, REFINE_CAP, codes[:rows], scales[:rows])
+        tr = time.perf_counter() - t0
+        fl_cpu = 2.0 * hrows * K * K + 2.0 * rows * K * K
+        out["cpu_baseline"] = dict(value=round(fl_cpu / (th + tr) / 1e12, 6), unit="TFLOP/s", cores=1,
+                                   kind="oracle",
+                                   sample="Hessian of %d rows at K=%d (%.1f s) and the refinement of %d weight rows "
+                                          "(%.1f s), single-threaded C" % (hrows, K, th, rows, tr))
+    print(json.dumps(out), flush=True)
+
+
 def capture(torch, fn):
     """A HIP graph of the kernels that fn enqueues on the current stream."""
     s = torch.cuda.Stream()
@@ -385,6 +487,9 @@ def main():
         print(json.dumps({"copied_bytes": n, "copies": 3}), flush=True)
         return
     wl = WORKLOADS[args.workload]
+    if wl == REFINE:
+        refine_main(args, torch, binding, inputs, dev)
+        return
     spec = inputs.CONFIGS[4 if wl == MOE_BLOCK else wl]
     b = args.block if args.block is not None else spec["blocks"][0]
     moe = wl == 4

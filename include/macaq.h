@@ -293,9 +293,9 @@ macaq_status macaq_moe_block(const void* X, int64_t T, int64_t H, int64_t ldx, c
  *     d*d*H[k][k] - 2*d*g[k] with g = H e; each step takes the most negative
  *     change (ties: lowest k, then the downward move) until none is negative
  *     or max_flips moves are made;
- *   - everything in fp64 with sums in index order, so the result is
- *     reproducible bit for bit; moved elements get the canonical code of
- *     their index, the others keep their bits.
+ *   - everything in fp64 with sums in index order, one fused multiply-add
+ *     per term, so the result is reproducible bit for bit; moved elements
+ *     get the canonical code of their index, the others keep their bits.
  */
 
 /* Bytes of workspace for macaq_hessian: R x K fp32. */

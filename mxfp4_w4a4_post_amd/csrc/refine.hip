@@ -13,8 +13,8 @@
 // the transformed calibration rows; a step takes the adjacent move with the
 // most negative change d^2 H[k][k] - 2 d g[k] (g = H e; ties: lowest k, then
 // the downward move) until none is negative or max_flips moves are made.
-// Every sum runs in index order in fp64 with separate multiply and add, so the
-// decisions are reproducible bit for bit.
+// Every sum runs in index order in fp64, one fused multiply-add per term, so
+// the decisions are reproducible bit for bit.
 #include "mx_lane.hpp"
 
 namespace macaq {
@@ -109,8 +109,8 @@ __global__ __launch_bounds__(256) void transform_kernel(const void* __restrict__
 
 // C[i][j] = sum over t (ascending) of A(t, i) * B(t, j) in fp64, one 64 x 64
 // output tile per workgroup, each thread 4 x 4 outputs, t staged 16 at a time
-// through LDS. The products and the running sums round one at a time, in t
-// order, so every output equals the plain sequential sum. The two instances:
+// through LDS. Each term is added by one fused multiply-add, in t order, so
+// every output equals the plain sequential sum of fused steps. The two instances:
 //   Hessian: A = B = the fp32 transformed rows [R, K]:  H[j][k] = sum_r x~[r][j] x~[r][k];
 //   gradient: A = E^T (E [N, K] fp64), B = H:          G[n][j] = sum_k E[n][k] H[k][j].
 constexpr int kTile = 64, kChunk = 16;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt,
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = acc[a][b] + av[a] * bv[b];
+        for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fma(av[a], bv[b], acc[a][b]);
     }
     __syncthreads();
   }

@@ -541,9 +541,11 @@ int oracle_moe_block(const uint16_t* x, int64_t T, int64_t H, const int32_t* ids
  *   - each step takes the move with the most negative D (ties: lowest k,
  *     then the downward move), and the row stops when no move has D < 0 or
  *     after max_flips moves;
- *   - all of it in fp64 with sums in index order: g[j] = sum over k of
- *     e[k] * H[k][j] (k ascending), H[j][k] = sum over r of x~[r][j] *
- *     x~[r][k] (r ascending); after a move g[j] -= d * H[k][j];
+ *   - all of it in fp64 with sums in index order, each term added with one
+ *     rounding (fused multiply-add): g[j] = sum over k of e[k] * H[k][j]
+ *     (k ascending), H[j][k] = sum over r of x~[r][j] * x~[r][k] (r
+ *     ascending; these products are exact); after a move g[j] -= d * H[k][j]
+ *     (d is a power of two, so that product is exact too);
  *   - an element that is moved gets its canonical code (m = 0 is code 0);
  *     elements never moved keep their code bits (a -0 stays 0x8).
  */
@@ -559,7 +561,7 @@ int oracle_hessian(const uint16_t* x, int64_t R, int64_t K, int64_t ldx, const f
   for (int64_t j = 0; j < K; ++j)
     for (int64_t k = 0; k < K; ++k) {
       double acc = 0.0;
-      for (int64_t r = 0; r < R; ++r) acc += (double)t[r * K + j] * (double)t[r * K + k];
+      for (int64_t r = 0; r < R; ++r) acc = fma((double)t[r * K + j], (double)t[r * K + k], acc);
       H[j * K + k] = acc;
     }
   free(t);
@@ -600,7 +602,7 @@ int oracle_flip_refine(const void* W, int dtype, int64_t N, int64_t K, int64_t l
     }
     for (int64_t j = 0; j < K; ++j) {
       double acc = 0.0;
-      for (int64_t k = 0; k < K; ++k) acc += e[k] * H[k * K + j];
+      for (int64_t k = 0; k < K; ++k) acc = fma(e[k], H[k * K + j], acc);
       g[j] = acc;
     }
     int moves = 0;
