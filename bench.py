@@ -12,7 +12,10 @@ routing, gathered gate/up with the SwiGLU epilogue that quantizes the down
 input, down, weighted top-8 combine), prefill-large (M = 8192 through
 8192x28672 and 28672x8192, Hadamard block from --block), refine-8b (offline
 Flip-Refinement of the prefill layers' weights: Hessian of 512 transformed
-calibration rows, up to 64 greedy code moves per weight row) and tiny.
+calibration rows, up to 64 greedy code moves per weight row), quant-error
+(relative output error of the layer against the exact bf16 product for the
+calibration variants s = max^(q/4) and Hadamard blocks b in {0, 32, 64, 128}
+on three activation recipes) and tiny.
 
 Inputs are resident in HBM; the timed steps rotate through several copies of
 activations and weights so that no step finds its operands in the 256 MB
@@ -42,7 +45,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ROTATE = 4                  # operand copies cycled through by the timed steps
 ORACLE_THREADS_CAP = 16     # the GPU machine's CPU share for one GPU
 WORKLOADS = {"tiny": 1, "prefill-8b": 2, "decode-32b": 3, "moe-128e": 4, "prefill-large": 5, "moe-block": 6,
-             "refine-8b": 7}
+             "refine-8b": 7, "quant-error": 8}
+QUANT_ERROR = 8  # study: layer output error against the calibration variant and the Hadamard block
 REFINE = 7  # offline Flip-Refinement of the prefill 8B-shaped layers' weights
 REFINE_ROWS = 512  # calibration rows of the Hessian
 REFINE_CAP = 64    # moves per weight row
@@ -327,6 +331,62 @@ def refine_main(args, torch, binding, inputs, dev):
     print(json.dumps(out), flush=True)
 
 
+def quant_error_main(args, torch, binding, inputs, dev):
+    """Relative L2 error of the W4A4 layer's fp32 output against the exact
+    product of the same bf16 activations and weights (fp64 on the host), for
+    every calibration variant q (s = max^(q/4)) and Hadamard block b."""
+    import numpy as np
+    cases = [("normal, 4 channels x50 (K=N=256, M=256)", inputs.linear_case(1, 0, M=256)),
+             ("student-t(3), 1% channels x30 (prefill 4096 x 4096, M=512)", inputs.linear_case(2, 0, M=512)),
+             ("student-t(3), 0.5% channels x100 (8192 -> first 2048 of 28672 rows, M=256)",
+              inputs.linear_case(5, 0, M=256, N=2048))]
+    table = {}
+    t0 = time.perf_counter()
+    for name, c in cases:
+        x64 = (inputs.bf16_bits(c.x).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        w64 = (inputs.bf16_bits(c.w).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        exact = x64 @ w64.T
+        x, w, xcal = c.x.to(dev), c.w.to(dev), c.xcal.to(dev)
+        row = {}
+        for q in (0, 1, 2, 4):
+            s = binding.calibrate(xcal, q)
+            for b in (0, 32, 64, 128):
+                a, r = binding.make_multipliers(s, b)
+                y = binding.linear(x, a, b, binding.prepare_weights(w, r, b), out_dtype=torch.float32)
+                err = float(np.linalg.norm(y.double().cpu().numpy() - exact) / np.linalg.norm(exact))
+                row["q=%d/4 b=%d" % (q, b)] = round(err, 5)
+        table[name] = row
+    wall = time.perf_counter() - t0
+    default = table[cases[1][0]]["q=2/4 b=32"]
+    best = {n: min(r, key=r.get) for n, r in table.items()}
+    out = {
+        "metric": METRIC, "value": default, "unit": "rel-L2 output error (prefill recipe, q=2/4, b=32)",
+        "n_gpus": 1, "steps": 1, "warmup": 0, "ms_per_step": round(wall * 1e3, 1), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp4 (MXFP4 E2M1/E8M0 operands, fp32 accumulate), fp32 out",
+        "data": "synthetic (seeded activations with outlier channels, N(0,sigma^2) weights; recipe in inputs.py)",
+        "config": {"workload": "quant-error: calibration variants s = max|x|^(q/4), q in {0,1,2,4}, x Hadamard "
+                               "blocks b in {0,32,64,128} on three activation recipes",
+                   "calibration_rows": inputs.CALIB_ROWS},
+        "error_table": table, "best_setting": best,
+        "timing": "one pass over the grid (GPU layers plus the host's exact fp64 products)",
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        c = cases[1][1]
+        threads = min(oracle.default_threads(), ORACLE_THREADS_CAP)
+        a_o, r_o = oracle.multipliers(oracle.calibrate(inputs.bf16_bits(c.xcal)), c.b)
+        wc, ws = oracle.prepare_weights(inputs.bf16_bits(c.w), r_o, c.b)
+        rows = 64
+        t1 = time.perf_counter()
+        oracle.linear(np.ascontiguousarray(inputs.bf16_bits(c.x)[:rows]), a_o, c.b, wc, ws, threads=threads)
+        dt = time.perf_counter() - t1
+        out["cpu_baseline"] = dict(value=round(2.0 * rows * c.K * c.N / dt / 1e12, 6), unit="TFLOP/s",
+                                   cores=threads, kind="oracle",
+                                   sample="%d rows of the prefill recipe's layer (quantize + fp64 GEMM over codes), "
+                                          "%.1f s" % (rows, dt))
+    print(json.dumps(out), flush=True)
+
+
 def capture(torch, fn):
     """A HIP graph of the kernels that fn enqueues on the current stream."""
     s = torch.cuda.Stream()
@@ -489,6 +549,9 @@ def main():
     wl = WORKLOADS[args.workload]
     if wl == REFINE:
         refine_main(args, torch, binding, inputs, dev)
+        return
+    if wl == QUANT_ERROR:
+        quant_error_main(args, torch, binding, inputs, dev)
         return
     spec = inputs.CONFIGS[4 if wl == MOE_BLOCK else wl]
     b = args.block if args.block is not None else spec["blocks"][0]

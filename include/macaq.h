@@ -104,6 +104,16 @@ macaq_status macaq_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx
                              macaq_stream_t stream);
 
 /*
+ * Calibration variants (the paper card's title calls the method calibrated;
+ * the form of the scale is a reading): s[k] = (max_r |xcal[r, k]|)^(q/4) for
+ * q = quarters in {0, 1, 2, 4}: 0 gives s = 1 (no per-channel scale), 1 two
+ * correctly rounded square roots in turn, 2 is macaq_calibrate, 4 the maximum
+ * itself (the whole range moved into the weights); 1 for an all-zero column.
+ */
+macaq_status macaq_calibrate_pow(const void* xcal, int64_t R, int64_t K, int64_t ldx, int32_t quarters, float* s,
+                                 macaq_stream_t stream);
+
+/*
  * Folded multipliers for one layer: a[k] = RN32(c_b / s[k]) for the
  * activations and r[k] = RN32(c_b * s[k]) for the weights, c_b =
  * RN32(1/sqrt(b)) (1 when b = 0). s, a, r: device fp32 [K]; a or r may be

@@ -34,6 +34,7 @@ _SIGNATURES = {
     "macaq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "macaq_last_error": (ctypes.c_char_p, []),
     "macaq_calibrate": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    "macaq_calibrate_pow": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp]),
     "macaq_make_multipliers": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
     "macaq_prepare_weights": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp]),
     "macaq_quant_act": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, ctypes.c_int, _vp, _vp, _vp]),
@@ -134,14 +135,19 @@ def _dtype_code(dt: torch.dtype) -> int:
     raise ValueError("macaq: dtype %s is not bf16 or fp32" % dt)
 
 
-def calibrate(xcal: torch.Tensor) -> torch.Tensor:
-    """Per-channel scale s[k] = sqrt(max_r |xcal[r, k]|) of bf16 calibration rows."""
+def calibrate(xcal: torch.Tensor, quarters: int = 2) -> torch.Tensor:
+    """Per-channel scale s[k] = (max_r |xcal[r, k]|)^(quarters / 4) of bf16
+    calibration rows (quarters 2, the default: the square root)."""
     _need_cuda(xcal)
     assert xcal.dtype == torch.bfloat16 and xcal.dim() == 2 and xcal.stride(1) == 1
     R, K = xcal.shape
     s = torch.empty(K, dtype=torch.float32, device=xcal.device)
-    _check(load_library().macaq_calibrate(_ptr(xcal), R, K, xcal.stride(0), _ptr(s), _stream(xcal)),
-           "macaq_calibrate")
+    if quarters == 2:
+        _check(load_library().macaq_calibrate(_ptr(xcal), R, K, xcal.stride(0), _ptr(s), _stream(xcal)),
+               "macaq_calibrate")
+    else:
+        _check(load_library().macaq_calibrate_pow(_ptr(xcal), R, K, xcal.stride(0), quarters, _ptr(s),
+                                                  _stream(xcal)), "macaq_calibrate_pow")
     return s
 
 

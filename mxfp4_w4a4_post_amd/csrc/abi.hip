@@ -243,14 +243,21 @@ const char* macaq_status_string(macaq_status s) {
 
 const char* macaq_last_error(void) { return g_last_error; }
 
-macaq_status macaq_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx, float* s, macaq_stream_t stream) {
+macaq_status macaq_calibrate_pow(const void* xcal, int64_t R, int64_t K, int64_t ldx, int32_t quarters, float* s,
+                                 macaq_stream_t stream) {
+  if (quarters != 0 && quarters != 1 && quarters != 2 && quarters != 4)
+    return fail(MACAQ_EINVAL, "macaq_calibrate: quarters = %d not in {0, 1, 2, 4}", quarters);
   if (!xcal || !s) return fail(MACAQ_EINVAL, "macaq_calibrate: NULL pointer");
   if (R < 1 || K < 1 || ldx < K) return fail(MACAQ_EINVAL, "macaq_calibrate: need R >= 1, K >= 1, ldx >= K");
   if (!aligned(xcal, 2) || !aligned(s, 4)) return fail(MACAQ_EALIGN, "macaq_calibrate: misaligned pointer");
   macaq_status st = check_device();
   if (st != MACAQ_OK) return st;
-  hipError_t e = launch_calibrate(xcal, R, K, ldx, s, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = launch_calibrate(xcal, R, K, ldx, quarters, s, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_calibrate launch");
+}
+
+macaq_status macaq_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx, float* s, macaq_stream_t stream) {
+  return macaq_calibrate_pow(xcal, R, K, ldx, 2, s, stream);
 }
 
 macaq_status macaq_make_multipliers(const float* s, int64_t K, int32_t b, float* a, float* r, macaq_stream_t stream) {

@@ -69,7 +69,9 @@ struct QuantArgs {
   int64_t src_rows;
 };
 
-hipError_t launch_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx, float* s, hipStream_t stream);
+// s = (column max of |xcal|)^(quarters / 4), quarters in {0, 1, 2, 4}
+hipError_t launch_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx, int quarters, float* s,
+                            hipStream_t stream);
 hipError_t launch_multipliers(const float* s, int64_t K, float cb, float* a, float* r, hipStream_t stream);
 // x_is_f32: input rows are fp32 (weights) instead of bf16.
 hipError_t launch_quant_rows(const QuantArgs& q, int b, bool x_is_f32, hipStream_t stream);

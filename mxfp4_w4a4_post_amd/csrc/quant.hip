@@ -172,13 +172,22 @@ __device__ float div_rn(float c, float s) {  // c > 0, s > 0, finite
   return y;
 }
 
+// s[k] = (column max)^(quarters / 4): quarters 0 gives 1, 1 two correctly
+// rounded square roots in turn, 2 one, 4 the maximum itself; an all-zero
+// column gives 1.
 __global__ __launch_bounds__(kThreads) void calibrate_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t K,
-                                                             int64_t ldx, float* __restrict__ s) {
+                                                             int64_t ldx, int quarters, float* __restrict__ s) {
   const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (k >= K) return;
   float mx = 0.0f;
   for (int64_t r = 0; r < R; ++r) mx = fmaxf(mx, fabsf(__uint_as_float((uint32_t)x[r * ldx + k] << 16)));
-  s[k] = (mx == 0.0f) ? 1.0f : sqrt_rn(mx);
+  float v = 1.0f;
+  if (mx != 0.0f) {
+    if (quarters == 1) v = sqrt_rn(sqrt_rn(mx));
+    else if (quarters == 2) v = sqrt_rn(mx);
+    else if (quarters == 4) v = mx;
+  }
+  s[k] = v;
 }
 
 __global__ __launch_bounds__(kThreads) void multipliers_kernel(const float* __restrict__ s, int64_t K, float cb,
@@ -232,10 +241,11 @@ hipError_t launch_quant_rows(const QuantArgs& q, int b, bool x_is_f32, hipStream
   return q.tiled ? launch_layout<true>(q, b, x_is_f32, stream) : launch_layout<false>(q, b, x_is_f32, stream);
 }
 
-hipError_t launch_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx, float* s, hipStream_t stream) {
+hipError_t launch_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx, int quarters, float* s,
+                            hipStream_t stream) {
   const int64_t blocks = (K + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(calibrate_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(xcal), R, K, ldx, s);
+                     static_cast<const uint16_t*>(xcal), R, K, ldx, quarters, s);
   return hipGetLastError();
 }
 

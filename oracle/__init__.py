@@ -87,6 +87,8 @@ def _load():
     lib.oracle_moe_block.argtypes = [vp, _i64, _i64, _i32p, _f32p, _int, _int, _f32p, _u8p, _u8p, _f32p, _u8p,
                                      _u8p, _i64, _int, _u8p, _u8p, _u8p, _f64p, _int]
     lib.oracle_hessian.argtypes = [vp, _i64, _i64, _i64, _f32p, _int, _f64p]
+    lib.oracle_calibrate_pow.argtypes = [vp, _int, _i64, _i64, _i64, _int, _f32p]
+    lib.oracle_calibrate_pow.restype = _int
     lib.oracle_flip_refine.argtypes = [vp, _int, _i64, _i64, _i64, _f32p, _int, _f64p, _int, _u8p, _u8p, _i32p]
     for f in (lib.oracle_calibrate, lib.oracle_multipliers, lib.oracle_transform_rows, lib.oracle_quant_rows,
               lib.oracle_dequant_rows, lib.oracle_gemm_codes, lib.oracle_linear, lib.oracle_linear_grouped,
@@ -136,6 +138,16 @@ def calibrate(xcal: np.ndarray) -> np.ndarray:
     R, K = x.shape
     s = np.empty(K, np.float32)
     _check(lib.oracle_calibrate(x.ctypes.data, dt, R, K, K, _ptr(s, _f32p)), "calibrate")
+    return s
+
+
+def calibrate_pow(xcal: np.ndarray, quarters: int) -> np.ndarray:
+    """s[k] = (max_r |xcal[r, k]|)^(quarters / 4), quarters in {0, 1, 2, 4}."""
+    lib = _load()
+    x, dt = _elems(xcal)
+    R, K = x.shape
+    s = np.empty(K, np.float32)
+    _check(lib.oracle_calibrate_pow(x.ctypes.data, dt, R, K, K, quarters, _ptr(s, _f32p)), "calibrate_pow")
     return s
 
 

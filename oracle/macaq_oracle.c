@@ -89,6 +89,30 @@ int oracle_calibrate(const void* xcal, int dtype, int64_t R, int64_t K, int64_t 
   return ORACLE_OK;
 }
 
+/* Calibration variants (the pages leave the form of the calibrated scale
+   open): s_k = max_r |x_rk| raised to quarters/4, for quarters 0 (no scale,
+   s = 1), 1 (two correctly rounded square roots in turn), 2 (one, as
+   oracle_calibrate) or 4 (the maximum itself); 1 for an all-zero channel. */
+int oracle_calibrate_pow(const void* xcal, int dtype, int64_t R, int64_t K, int64_t ld, int quarters, float* s) {
+  if (quarters != 0 && quarters != 1 && quarters != 2 && quarters != 4) return ORACLE_EINVAL;
+  if (!xcal || !s || R < 1 || K < 1 || ld < K) return ORACLE_EINVAL;
+  for (int64_t k = 0; k < K; ++k) {
+    float mx = 0.0f;
+    for (int64_t r = 0; r < R; ++r) {
+      float v = fabsf(load_elem(xcal, dtype, r * ld + k));
+      if (v > mx) mx = v;
+    }
+    float v = 1.0f;
+    if (mx != 0.0f) {
+      if (quarters == 1) v = sqrtf(sqrtf(mx));
+      else if (quarters == 2) v = sqrtf(mx);
+      else if (quarters == 4) v = mx;
+    }
+    s[k] = v;
+  }
+  return ORACLE_OK;
+}
+
 /* c_b = RN32(1/sqrt(b)) (1 when b == 0); a_k = RN32(c_b / s_k),
    r_k = RN32(c_b * s_k). Either output may be NULL. */
 int oracle_multipliers(const float* s, int64_t K, int b, float* a, float* r) {

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding._SIGNATURES), "binding signatures out of sync with the header"
@@ -216,3 +216,10 @@ def test_refine_calls_reject(lib):
     assert f(dt=1, ldw=66) == EALIGN
     assert f(wsb=100) == EWORKSPACE
     assert lib.macaq_flip_refine_workspace_size(8, 64) >= 2 * 8 * 64 * 8 + 64 * 8
+
+
+def test_calibrate_pow_rejects(lib):
+    assert lib.macaq_calibrate_pow(FAKE, 4, 64, 64, 3, FAKE, None) == EINVAL
+    assert lib.macaq_calibrate_pow(None, 4, 64, 64, 1, FAKE, None) == EINVAL
+    assert lib.macaq_calibrate_pow(FAKE, 0, 64, 64, 4, FAKE, None) == EINVAL
+    assert lib.macaq_calibrate_pow(FAKE + 1, 4, 64, 64, 0, FAKE, None) == EALIGN

@@ -60,6 +60,16 @@ def oracle_layer(case, b=None):
 # Calibration and multipliers: bit-exact
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("quarters", [0, 1, 2, 4])
+def test_calibrate_variants_bit_exact(dev, quarters):
+    log("calibrate variant quarters=%d" % quarters)
+    xcal = inputs.calibration(2, 0, 4096)
+    x = xcal.clone()
+    x[:, 7] = 0
+    s_g = binding.calibrate(x.to(dev), quarters)
+    s_o = oracle.calibrate_pow(bits(x), quarters)
+    assert np.array_equal(s_g.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+
 @pytest.mark.parametrize("cfg,shape,K", [(1, 0, 256), (2, 0, 4096), (3, 1, 25600), (5, 1, 28672)])
 def test_calibrate_and_multipliers_bit_exact(dev, cfg, shape, K):
     log("calibrate cfg=%d K=%d" % (cfg, K))
