@@ -15,7 +15,9 @@ Flip-Refinement of the prefill layers' weights: Hessian of 512 transformed
 calibration rows, up to 64 greedy code moves per weight row), quant-error
 (relative output error of the layer against the exact bf16 product for the
 calibration variants s = max^(q/4) and Hadamard blocks b in {0, 32, 64, 128}
-on three activation recipes) and tiny.
+on three activation recipes), prepare-stream (weights of 8 blocks of 8B-shaped
+linears prepared from pinned host memory back to pinned host memory with one
+layer resident, copies overlapped with preparation) and tiny.
 
 Inputs are resident in HBM; the timed steps rotate through several copies of
 activations and weights so that no step finds its operands in the 256 MB
@@ -45,7 +47,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ROTATE = 4                  # operand copies cycled through by the timed steps
 ORACLE_THREADS_CAP = 16     # the GPU machine's CPU share for one GPU
 WORKLOADS = {"tiny": 1, "prefill-8b": 2, "decode-32b": 3, "moe-128e": 4, "prefill-large": 5, "moe-block": 6,
-             "refine-8b": 7, "quant-error": 8}
+             "refine-8b": 7, "quant-error": 8, "prepare-stream": 9}
+PREPARE_STREAM = 9  # offline: a stack of 8B-shaped blocks prepared from pinned host memory, one layer resident
+STREAM_BLOCKS = 8
+BLOCK_SHAPES = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096), (4096, 14336)]
 QUANT_ERROR = 8  # study: layer output error against the calibration variant and the Hadamard block
 REFINE = 7  # offline Flip-Refinement of the prefill 8B-shaped layers' weights
 REFINE_ROWS = 512  # calibration rows of the Hessian
@@ -387,6 +392,92 @@ def quant_error_main(args, torch, binding, inputs, dev):
     print(json.dumps(out), flush=True)
 
 
+def prepare_stream_main(args, torch, binding, inputs, dev):
+    """Streaming preparation of a synthetic stack: (N, K) per linear of an
+    8B-shaped block (q, k, v, o, gate, up, down), STREAM_BLOCKS blocks, bf16
+    weights and 64 calibration rows per layer in pinned host memory (drawn on
+    the device from a seeded generator, then copied out)."""
+    from mxfp4_w4a4_post_amd import streaming
+    b = args.block if args.block is not None else 32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
+    layers = []
+    for blk in range(STREAM_BLOCKS):
+        for (N, K) in BLOCK_SHAPES:
+            w = (torch.randn(N, K, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            x = torch.randn(inputs.CALIB_ROWS, K, generator=gen, device=dev).to(torch.bfloat16)
+            layers.append(streaming.HostLayer(w.cpu().pin_memory(), x.cpu().pin_memory()))
+    del w, x
+    torch.cuda.synchronize()
+    max_n = max(L.w.shape[0] for L in layers)
+    max_k = max(L.w.shape[1] for L in layers)
+    wbytes = sum(2 * L.w.numel() for L in layers)
+    pbytes = sum(L.w.numel() * 17 / 32 for L in layers)
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    prep = streaming.StreamingPreparer(dev, max_n, max_k, inputs.CALIB_ROWS)
+    prep.run(layers[:2], b)  # warm
+    t0 = time.perf_counter()
+    out = prep.run(layers, b)
+    t_stream = time.perf_counter() - t0
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    # the same work without overlap: each copy and preparation waits for the one before
+    t0 = time.perf_counter()
+    for L in layers:
+        w = L.w.to(dev)
+        x = L.xcal.to(dev)
+        a, r = binding.make_multipliers(binding.calibrate(x), b)
+        p = binding.prepare_weights(w, r, b)
+        p.codes.cpu(), p.scales.cpu(), a.cpu(), r.cpu()
+        torch.cuda.synchronize()
+    t_seq = time.perf_counter() - t0
+    # the device work alone (weights resident): the prepare kernel's roofline
+    dw = [L.w.to(dev) for L in layers[:len(BLOCK_SHAPES)]]
+    rr = [torch.ones(L.w.shape[1], dtype=torch.float32, device=dev) for L in layers[:len(BLOCK_SHAPES)]]
+    outs = [binding.prepare_weights(w, r, b) for w, r in zip(dw, rr)]
+    torch.cuda.synchronize()
+    with Timer(torch) as t:
+        for w, r, o in zip(dw, rr, outs):
+            binding.prepare_weights(w, r, b, out=o)
+    torch.cuda.synchronize()
+    ms_dev = t.ms()
+    dev_bytes = sum(w.numel() * (2 + 17 / 32) for w in dw)
+    gbs_dev = dev_bytes / (ms_dev * 1e-3) / 1e9
+    flips_note = len(out)
+    res = {
+        "metric": METRIC, "value": round(wbytes / t_stream / 1e9, 2),
+        "unit": "GB/s of bf16 weights, pinned host in -> prepared pinned host out", "n_gpus": 1, "steps": 1,
+        "warmup": 1, "ms_per_step": round(t_stream * 1e3, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 weights in, MXFP4 (codes + E8M0 scales) out",
+        "data": "synthetic (seeded device generator, N(0, 0.02^2) weights, N(0, 1) calibration rows)",
+        "config": {"workload": "prepare-stream: %d blocks x %d linears of an 8B-shaped block %s, %d calibration rows "
+                               "each, Hadamard block %d" % (STREAM_BLOCKS, len(BLOCK_SHAPES), BLOCK_SHAPES,
+                                                            inputs.CALIB_ROWS, b),
+                   "layers": flips_note, "weight_bytes": int(wbytes), "packed_bytes": int(pbytes)},
+        "sequential_s": round(t_seq, 3), "overlap_speedup": round(t_seq / t_stream, 2),
+        "peak_device_bytes": int(peak), "largest_layer_bytes": int(2 * max_n * max_k),
+        "roofline": {"bound": "hbm", "achieved": round(gbs_dev, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs_dev / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "quant_rows_kernel as macaq_prepare_weights (2 B read + 17/32 B written per weight), "
+                               "one block's seven layers resident"},
+        "timing": "wall clock around the streamed run (host in to host out); device work timed with HIP events",
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        L = layers[0]
+        wb = inputs.bf16_bits(L.w[:256])
+        t0 = time.perf_counter()
+        a_o, r_o = oracle.multipliers(oracle.calibrate(inputs.bf16_bits(L.xcal)), b)
+        oracle.prepare_weights(wb, r_o, b)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = dict(value=round(wb.size * 2 / dt / 1e9, 4), unit="GB/s of bf16 weights", cores=1,
+                                   kind="oracle", sample="256 rows of a 4096 x 4096 layer (calibrate, multipliers, "
+                                                         "prepare), %.2f s" % dt)
+    print(json.dumps(res), flush=True)
+
+
 def capture(torch, fn):
     """A HIP graph of the kernels that fn enqueues on the current stream."""
     s = torch.cuda.Stream()
@@ -552,6 +643,9 @@ def main():
         return
     if wl == QUANT_ERROR:
         quant_error_main(args, torch, binding, inputs, dev)
+        return
+    if wl == PREPARE_STREAM:
+        prepare_stream_main(args, torch, binding, inputs, dev)
         return
     spec = inputs.CONFIGS[4 if wl == MOE_BLOCK else wl]
     b = args.block if args.block is not None else spec["blocks"][0]
