@@ -48,6 +48,21 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
   const int64_t k0 = (int64_t)blockIdx.y * kBlockK + c * 32;
   const bool valid = row < q.M && k0 < q.K;
 
+  // the row's raw values first, so their loads are in flight while the
+  // multipliers are staged
+  uint4 raw[F32_IN ? 8 : 4];
+  if (valid) {
+    int64_t src = row;
+    if (q.gather) {  // MoE rows read their token's activations
+      src = q.gather[row];
+      src = src < 0 ? 0 : (src >= q.src_rows ? q.src_rows - 1 : src);
+    }
+    const uint4* p = F32_IN ? reinterpret_cast<const uint4*>(static_cast<const float*>(q.x) + src * q.ldx + k0)
+                            : reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.x) + src * q.ldx + k0);
+#pragma unroll
+    for (int i = 0; i < (F32_IN ? 8 : 4); ++i) raw[i] = p[i];
+  }
+
   // the block's 256 multipliers are shared by its 32 rows: stage them in LDS
   // once. MoE rows take their expert's multipliers; a block whose rows span
   // two experts (rows are expert-major) has each lane read its own.
@@ -72,26 +87,18 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
 
   float v[32];
   if (valid) {
-    int64_t src = row;
-    if (q.gather) {  // MoE rows read their token's activations
-      src = q.gather[row];
-      src = src < 0 ? 0 : (src >= q.src_rows ? q.src_rows - 1 : src);
-    }
     if constexpr (F32_IN) {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q.x) + src * q.ldx + k0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float4 u = p[i];
-        v[4 * i] = u.x;
-        v[4 * i + 1] = u.y;
-        v[4 * i + 2] = u.z;
-        v[4 * i + 3] = u.w;
+        v[4 * i] = __uint_as_float(raw[i].x);
+        v[4 * i + 1] = __uint_as_float(raw[i].y);
+        v[4 * i + 2] = __uint_as_float(raw[i].z);
+        v[4 * i + 3] = __uint_as_float(raw[i].w);
       }
     } else {
-      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.x) + src * q.ldx + k0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4 w = p[i];
+        const uint4 w = raw[i];
         v[8 * i] = bf16_lo(w.x);
         v[8 * i + 1] = bf16_hi(w.x);
         v[8 * i + 2] = bf16_lo(w.y);
@@ -104,8 +111,8 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
     }
     if constexpr (SCALE) {
       const float4* mp;
-      if (GROUPED && !staged)
-        mp = reinterpret_cast<const float4*>(q.mult + (int64_t)expert_of_row(q.offsets, q.E, row) * q.K + k0);
+      if (!staged)
+        mp = reinterpret_cast<const float4*>(q.mult + (GROUPED ? (int64_t)expert_of_row(q.offsets, q.E, row) * q.K : 0) + k0);
       else
         mp = reinterpret_cast<const float4*>(msh + c * 32);
 #pragma unroll
