@@ -70,6 +70,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="if > 0: only run this many eager steps of the fused path (for rocprofv3) and exit")
+    p.add_argument("--gemm-only", default=None, metavar="MxNxK",
+                   help="only run the GEMM (macaq_gemm) on random MXFP4 operands of this shape --profile-steps "
+                        "times (for counter collection) and exit")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="if > 0: only copy a MIB-MiB device buffer 3 times (the known-size reference for the "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -636,6 +639,25 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copied_bytes": n, "copies": 3}), flush=True)
+        return
+    if args.gemm_only:
+        M, N, K = (int(v) for v in args.gemm_only.split("x"))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(5)
+
+        def packed(rows):
+            return binding.Packed(
+                torch.randint(0, 256, (binding.packed_codes_bytes(rows, K),), dtype=torch.uint8, device=dev,
+                              generator=gen),
+                torch.randint(120, 130, (binding.packed_scales_bytes(rows, K),), dtype=torch.uint8, device=dev,
+                              generator=gen), rows, K)
+        a, w = packed(M), packed(N)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        work = torch.empty(max(binding.gemm_workspace_size(M, K, N), 1), dtype=torch.uint8, device=dev)
+        for _ in range(max(args.profile_steps, 1)):
+            binding.linear_plain_gemm(a, w, out=y, workspace=work)
+        torch.cuda.synchronize()
+        print(json.dumps({"gemm_only": [M, N, K], "launches": max(args.profile_steps, 1)}), flush=True)
         return
     wl = WORKLOADS[args.workload]
     if wl == REFINE:
