@@ -142,6 +142,7 @@ def dense_entries(torch, binding, inputs, wl, b, dev):
             e = Entry("M=%d K=%d N=%d" % (M, K, N), 2.0 * M * N * K, 2 * M * K + wbytes + 2 * M * N,
                       M * K * 17 / 32 + wbytes + 2 * M * N)
             y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            y32 = torch.empty(M, N, dtype=torch.float32, device=dev)
             work = torch.empty(max(binding.linear_workspace_size(M, K, N), 1), dtype=torch.uint8, device=dev)
             gwork = torch.empty(max(binding.gemm_workspace_size(M, K, N), 1), dtype=torch.uint8, device=dev)
             qa = binding.Packed(torch.empty(binding.packed_codes_bytes(M, K), dtype=torch.uint8, device=dev),
@@ -153,6 +154,8 @@ def dense_entries(torch, binding, inputs, wl, b, dev):
                                                                                    workspace=work)
             e.plain = lambda c, xs=xs, wp=wp, y=y, work=work: binding.linear(xs[c], None, 0, wp[c], out=y,
                                                                               workspace=work)
+            e.fused_f32 = lambda c, xs=xs, a=a, wf=wf, y32=y32, work=work: binding.linear(xs[c], a, b, wf[c], out=y32,
+                                                                                       workspace=work)
             e.quant = lambda c, xs=xs, a=a, qa=qa: binding.quant_act(xs[c], a, b, layout="gemm", codes=qa.codes,
                                                                      scales=qa.scales)
             e.quant_plain = lambda c, xs=xs, qp=qp: binding.quant_act(xs[c], None, 0, layout="gemm",
@@ -513,6 +516,35 @@ def timed_steps(torch, step, steps, warmup):
     return t.ms() / steps, time.perf_counter() - t0
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def step_distribution(torch, step, reps, warmup):
+    """Per-step times: one HIP graph per operand copy (one step each),
+    replayed in turn, each replay bracketed by its own HIP events. Returns
+    (p10, median, p90) in ms."""
+    graphs = [capture(torch, lambda c=c: step(c)) for c in range(ROTATE)]
+    for i in range(warmup):
+        graphs[i % ROTATE].replay()
+    timers = []
+    for i in range(reps):
+        with Timer(torch) as t:
+            graphs[i % ROTATE].replay()
+        timers.append(t)
+    torch.cuda.synchronize()
+    ms = sorted(t.ms() for t in timers)
+    pick = lambda q: ms[min(len(ms) - 1, int(round(q * (len(ms) - 1))))]
+    return pick(0.1), pick(0.5), pick(0.9)
+
+
 def cpu_baseline(entries, target_s, moe):
     """The oracle (C, fp64 GEMM over codes, as it stands) on a bounded sample
     of the step's rows: rows of every dense layer, or the first experts."""
@@ -762,6 +794,12 @@ def main():
         out["kernels_ms_per_step"] = {"calls": len(entries), "quant": round(q, 5), "gemm": round(g, 5),
                                       "quant_plain": round(qp, 5), "gemm_plain": round(gp, 5)}
         out["overhead_split_ms"] = {"quantize": round(q - qp, 5), "gemm_on_transformed_codes": round(g - gp, 5)}
+        # the same fused step one step at a time (median and spread), and with
+        # fp32 output (the precision the parity tests compare)
+        p10, p50, p90 = step_distribution(torch, step, max(args.steps, 50), args.warmup)
+        out["step_ms_p10_median_p90"] = [round(p10, 5), round(p50, 5), round(p90, 5)]
+        ms32, _ = timed_steps(torch, lambda c: [e.fused_f32(c) for e in entries], args.steps, args.warmup)
+        out["fp32_out"] = {"ms_per_step": round(ms32, 5), "tflops": round(flops / (ms32 * 1e-3) / 1e12, 2)}
         gemm_ms = g
         if wl == 3:  # decode: the GEMM streams the weights
             gb = sum(e.gemm_bytes for e in entries) / (gemm_ms * 1e-3) / 1e9
@@ -788,6 +826,7 @@ def main():
                            "kernel_source_digest": digest}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(entries, args.cpu_seconds, "block" if wl == MOE_BLOCK else moe)
+        out["cpu_baseline"]["cpu_model"] = host_cpu_model()
     print(json.dumps(out), flush=True)
 
 
