@@ -67,7 +67,7 @@ def parse():
     p.add_argument("--workload", default="prefill-8b", choices=sorted(WORKLOADS))
     p.add_argument("--block", type=int, default=None, help="Hadamard block (default: the workload's first)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="if > 0: only run this many eager steps of the fused path (for rocprofv3) and exit")
     p.add_argument("--gemm-only", default=None, metavar="MxNxK",
@@ -583,7 +583,7 @@ def cpu_baseline(entries, target_s, moe):
                              threads=threads)
             dt = time.perf_counter() - t0
             flops = 2.0 * n * case.k * (2 * case.F * case.H + case.H * case.F)
-            if dt >= target_s * 0.5 or n >= case.T:
+            if dt >= target_s * 0.7 or n >= case.T:
                 break
             n = min(case.T, n * max(2, int(target_s / max(dt, 1e-3))))
         return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
@@ -628,7 +628,7 @@ def cpu_baseline(entries, target_s, moe):
             rows_done += rows
             rows_all += M
         dt = time.perf_counter() - t0
-        if dt >= target_s * 0.5 or frac >= 1.0:
+        if dt >= target_s * 0.7 or frac >= 1.0:
             break
         frac = min(1.0, frac * max(2.0, target_s / max(dt, 1e-3)))
     return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
