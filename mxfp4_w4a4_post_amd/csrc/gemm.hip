@@ -34,6 +34,9 @@ constexpr int epi_pitch(int wn) { return wn * 2 + 16; }
 constexpr int epi_region(int wn) { return 32 * epi_pitch(wn); }
 constexpr int NT = 256;           // 4 waves
 constexpr int kNumCu = 256;
+// Deferred output keeps a tile's rows within 32-bit buffer offsets (128 rows
+// of ldy bf16 below 2 GiB).
+constexpr int64_t kDeferMaxLd = int64_t(1) << 22;
 
 constexpr int lcm2(int a, int b) {
   int x = a, y = b;
@@ -49,10 +52,13 @@ constexpr int lcm2(int a, int b) {
 // (hides their latency; keeps both tiles' registers live at once).
 // OCC: resident workgroups per CU (waves per SIMD) the register budget is
 // sized for; the persistent grid is OCC workgroups per CU.
-template <int BM_, int BN_, int PW_, int PA_, bool OVERLAP_ = true, int OCC_ = 1>
+// DEFER: a tile's bf16 output goes to an LDS region of its own and is written
+// to memory during the first steps of the workgroup's next tile, between its
+// MFMAs, instead of in a store phase that every CU reaches at the same time.
+template <int BM_, int BN_, int PW_, int PA_, bool OVERLAP_ = true, int OCC_ = 1, bool DEFER_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, PW = PW_, PA = PA_, OCC = OCC_;
-  static constexpr bool OVERLAP = OVERLAP_;
+  static constexpr bool OVERLAP = OVERLAP_, DEFER = DEFER_;
   static constexpr int FM = BM / kGroupRows;  // activation fragments (32 rows each)
   static constexpr int WN = BN / 4;           // weight rows per wave
   static constexpr int FN = WN / kGroupRows;  // weight fragments per wave
@@ -64,10 +70,19 @@ struct TileCfg {
   static constexpr int LDS_TRASH = NT * 4;
   static constexpr int STAGE = A_CODES + A_SCALES + LDS_TRASH;
   static constexpr int NBUF = 3;  // LDS buffers: compute s, read s+1, write s+2
+  // deferred output: BM rows of BN bf16 (padded by 16 bytes) after the
+  // buffers, written in 1 KiB pieces of PIECE_ROWS rows, PIECES_W per wave
+  static constexpr int OUT_PITCH = BN * 2 + 16;
+  static constexpr int OUT_OFF = NBUF * STAGE;
+  static constexpr int OUT_BYTES = DEFER ? BM * OUT_PITCH : 0;
+  static constexpr int PIECE_ROWS = 1024 / (BN * 2);
+  static constexpr int PIECES_W = BM / PIECE_ROWS / 4;
   // the epilogue reuses the LDS: one staging region per wave
-  static constexpr int LDS_BYTES = (NBUF * STAGE > 4 * epi_region(WN)) ? NBUF * STAGE : 4 * epi_region(WN);
+  static constexpr int LDS_BYTES =
+      (NBUF * STAGE + OUT_BYTES > 4 * epi_region(WN)) ? NBUF * STAGE + OUT_BYTES : 4 * epi_region(WN);
   // main-loop unroll: register slots static
   static constexpr int U = lcm2(PW, PA);
+  static_assert(!DEFER || (BN == 256 && OCC == 1 && (PIECES_W & (PIECES_W - 1)) == 0), "deferred output pieces");
   static constexpr int N_MFMA = FM * FN;  // per half step
   static_assert(BM % kGroupRows == 0 && BN % (4 * kGroupRows) == 0, "tile shape");
   static_assert(FM <= 4, "at most one scale dword per thread");
@@ -139,19 +154,22 @@ __device__ __forceinline__ v16f mfma(v4i a, v4i b, v16f c, int sa, int sb, int h
 // Scheduling hints: each MFMA is followed by a share of the half step's LDS
 // reads, LDS writes and buffer loads, so the matrix core stays busy while the
 // memory traffic is issued.
-constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedVmemWrite = 0x040, kSchedDsRead = 0x100,
+              kSchedDsWrite = 0x200;
 
-template <int T, int NM, int NR, int NW, int NV>
+template <int T, int NM, int NR, int NW, int NV, int NS = 0>
 __device__ __forceinline__ void interleave() {
   if constexpr (T < NM) {
     constexpr int r0 = T * NR / NM, r1 = (T + 1) * NR / NM;
     constexpr int w0 = T * NW / NM, w1 = (T + 1) * NW / NM;
     constexpr int v0 = T * NV / NM, v1 = (T + 1) * NV / NM;
+    constexpr int s0 = T * NS / NM, s1 = (T + 1) * NS / NM;
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     if constexpr (r1 > r0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, r1 - r0, 0);
     if constexpr (w1 > w0) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, w1 - w0, 0);
     if constexpr (v1 > v0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, v1 - v0, 0);
-    interleave<T + 1, NM, NR, NW, NV>();
+    if constexpr (s1 > s0) __builtin_amdgcn_sched_group_barrier(kSchedVmemWrite, s1 - s0, 0);
+    interleave<T + 1, NM, NR, NW, NV, NS>();
   }
 }
 
@@ -357,13 +375,15 @@ enum OutMode {
   kOutSwiGlu0 = 4,
   kOutSwiGlu32 = 5,
   kOutSwiGlu64 = 6,
-  kOutSwiGlu128 = 7
+  kOutSwiGlu128 = 7,
+  kOutBf16Defer = 8
 };
+constexpr bool is_swiglu(int mode) { return mode >= kOutSwiGlu0 && mode <= kOutSwiGlu128; }
 
 template <class C, int MODE>
 __device__ __forceinline__ void store_out(const Acc<C>& acc, const GemmArgs& g, const TileCoord& tc, int expert,
                                           int wave, int lane, uint8_t* smem) {
-  if constexpr (MODE >= kOutSwiGlu0) {
+  if constexpr (is_swiglu(MODE)) {
     constexpr int B = MODE == kOutSwiGlu0 ? 0 : (32 << (MODE - kOutSwiGlu32));
     store_swiglu_quant<C, B>(acc, g, tc, expert, wave, lane, smem);
     return;
@@ -427,6 +447,13 @@ struct Pipe {
 
   AStage<C> t0, t1;  // activation steps 0 and 1 on their way to LDS buffers 0 and 1
   int wave, lane;
+  // deferred output of the previous tile (DEFER): rows [0, y_rows) of the
+  // LDS output region go to the resource yr (its first row at offset 0);
+  // lane offset yo of piece 0 (kOob for a column past N), y_step bytes
+  // between a wave's successive pieces
+  Rsrc yr;
+  uint32_t yo;
+  int y_rows, y_step;
 
   __device__ __forceinline__ Pipe(uint8_t* smem_, int wave_, int lane_) : smem(smem_), wave(wave_), lane(lane_) {
     const int tid = threadIdx.x;
@@ -518,6 +545,59 @@ struct Pipe {
     for (int i = 0; i < C::FM; ++i) s[i] = lds_at<uint32_t>(smem, buf + lrs + i * kScaleBlock);
   }
 
+  // Piece j of this wave's share of the deferred output: rows
+  // PIECE_ROWS * (wave + 4 j) + lane / (64 / PIECE_ROWS), 16 bytes per lane.
+  __device__ __forceinline__ int piece_row(int j) const {
+    return C::PIECE_ROWS * (wave + 4 * j) + lane / (64 / C::PIECE_ROWS);
+  }
+  __device__ __forceinline__ v4i read_piece(int j) const {
+    const int col = lane % (64 / C::PIECE_ROWS);
+    return lds_at<v4i>(smem, C::OUT_OFF + piece_row(j) * C::OUT_PITCH + col * 16);
+  }
+  // live == false: the store goes through an empty resource (writes nothing).
+  __device__ __forceinline__ void store_piece(int j, v4i d, bool live = true) const {
+    const uint32_t off = piece_row(j) < y_rows ? yo + (uint32_t)(j * y_step) : kOob;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, d),
+                                           live ? yr : make_rsrc(nullptr, 0), (int)off, 0, 0);
+  }
+  // Nothing pending (the first tile of the workgroup): the stores of the
+  // first steps go through an empty resource and write nothing.
+  __device__ __forceinline__ void clear_pending() {
+    yr = make_rsrc(nullptr, 0);
+    yo = kOob;
+    y_rows = 0;
+    y_step = 0;
+  }
+  // The tile's accumulators as bf16 into the LDS output region (the caller
+  // makes it visible with a barrier), and the tile becomes the pending one.
+  __device__ __forceinline__ void stage_out(const GemmArgs& g, const TileCoord& tc) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < C::FN; ++jn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v16f& a = acc.v[i][jn];
+          const int m = i * 32 + (lane & 31);
+          const int n = wave * C::WN + jn * 32 + 8 * q + 4 * (lane >> 5);
+          uint2 w;
+          w.x = f32_to_bf16_rne(a[4 * q]) | (f32_to_bf16_rne(a[4 * q + 1]) << 16);
+          w.y = f32_to_bf16_rne(a[4 * q + 2]) | (f32_to_bf16_rne(a[4 * q + 3]) << 16);
+          lds_at<uint2>(smem, C::OUT_OFF + m * C::OUT_PITCH + n * 2) = w;
+        }
+    const int64_t m_lim = tc.m_end - tc.m0, n_lim = g.N - tc.n0;
+    uint16_t* base = static_cast<uint16_t*>(g.y) + tc.m0 * g.ldy;
+    yr = make_rsrc(base, ((m_lim - 1) * g.ldy + g.N) * 2);
+    const int col = (lane % (64 / C::PIECE_ROWS)) * 8;
+    yo = col < n_lim ? (uint32_t)((piece_row(0) * g.ldy + tc.n0 + col) * 2) : kOob;
+    y_rows = (int)m_lim;
+    y_step = (int)(4 * C::PIECE_ROWS * g.ldy * 2);
+  }
+  // Pieces [j0, PIECES_W) of the pending output.
+  __device__ __forceinline__ void flush(int64_t j0 = 0) {
+    for (int j = (int)j0; j < C::PIECES_W; ++j) store_piece(j, read_piece(j));
+  }
+
   template <int H, int WS, int FS>
   __device__ __forceinline__ void mfma_half() {
 #pragma unroll
@@ -527,8 +607,9 @@ struct Pipe {
         acc.v[i][j] = mfma(w[WS].c[j][H], af[FS].c[i], acc.v[i][j], (int)w[WS].s[j], (int)asc[i], H);
   }
 
-  // Half H of step s (J = s % U).
-  template <int J, int H>
+  // Half H of step s (J = s % U). DEF: half 0 also stores piece s of the
+  // deferred output (none once s >= PIECES_W).
+  template <int J, int H, bool DEF = false>
   __device__ __forceinline__ void half(int64_t s) {
     constexpr int WS = J % C::PW, AS = (J + 2) % C::PA;
     constexpr int FS = H & 1;
@@ -543,25 +624,32 @@ struct Pipe {
     }
     if constexpr (H == 0) store_a(a[AS], b_fill);
     if constexpr (H == 1) load_a(a[AS], kt_at(s + 2 + C::PA), live(ac, s + 2 + C::PA), live(as, s + 2 + C::PA));
+    constexpr bool PIECE = DEF && H == 0;
     mfma_half<H, WS, FS>();
+    // read late so the piece does not hold registers across the MFMAs
+    if constexpr (PIECE) store_piece((int)s & (C::PIECES_W - 1), read_piece((int)s & (C::PIECES_W - 1)), s < C::PIECES_W);
     load_w_half(w[WS], kt_at(s + C::PW), H, live(bc, s + C::PW));
     if constexpr (H == NH - 1) load_w_scales(w[WS], kt_at(s + C::PW), live(bs, s + C::PW));
     // the next half's LDS reads go first (they complete under this half's
     // MFMAs); the LDS writes and buffer loads are spread between the MFMAs
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NR, 0);
     interleave<0, C::N_MFMA, 0, NW, NV>();
+    if constexpr (PIECE) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemWrite, 1, 0);
+    }
     // keep this half's MFMAs on this side of the fence (they touch no memory,
     // so the scheduler would otherwise sink them and keep every half's
     // operands live at once)
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  template <int J>
+  template <int J, bool DEF = false>
   __device__ __forceinline__ void step(int64_t s) {
-    half<J, 0>(s);
-    half<J, 1>(s);
-    half<J, 2>(s);
-    half<J, 3>(s);
+    half<J, 0, DEF>(s);
+    half<J, 1, DEF>(s);
+    half<J, 2, DEF>(s);
+    half<J, 3, DEF>(s);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -572,11 +660,11 @@ struct Pipe {
     b_fill = t;
   }
 
-  template <int J>
+  template <int J, bool DEF = false>
   __device__ __forceinline__ void steps(int64_t s0) {
     if constexpr (J < C::U) {
-      step<J>(s0 + J);
-      steps<J + 1>(s0);
+      step<J, DEF>(s0 + J);
+      steps<J + 1, DEF>(s0);
     }
   }
 
@@ -627,9 +715,18 @@ struct Pipe {
       for (int j = 0; j < C::FN; ++j) acc.v[i][j] = {};
   }
 
-  // The K loop; its last barrier leaves every LDS buffer idle.
+  // The K loop; its last barrier leaves every LDS buffer idle. DEF: step s
+  // also writes piece s of the pending output, and the pieces a short tile
+  // did not reach follow the loop, fenced from the next staging by a barrier.
+  template <bool DEF = false>
   __device__ __forceinline__ void loop() {
-    for (int64_t s0 = 0; s0 < nsteps; s0 += C::U) steps<0>(s0);
+    for (int64_t s0 = 0; s0 < nsteps; s0 += C::U) steps<0, DEF>(s0);
+    if constexpr (DEF) {
+      if (nsteps < C::PIECES_W) {
+        flush(nsteps);
+        __syncthreads();
+      }
+    }
   }
 };
 
@@ -710,9 +807,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& g, int64_t total, uin
   if (t >= total) return;
   p.set_tile(g, cur.tc, g.M, cur.bc, cur.bs);
   p.prologue_loads();
+  constexpr bool DEF = MODE == kOutBf16Defer;
+  if constexpr (DEF) p.clear_pending();
   for (;;) {
     p.prologue_lds();
-    p.loop();
+    p.template loop<DEF>();
     TileRef nxt;
     int64_t tn = t + gridDim.x;
     while (tn < total && !tile_at<C, GROUPED>(g, xcd_remap(tn, total), nxt)) tn += gridDim.x;
@@ -720,8 +819,19 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& g, int64_t total, uin
       p.set_tile(g, nxt.tc, g.M, nxt.bc, nxt.bs);
       p.prologue_loads();
     }
-    store_out<C, MODE>(p.acc, g, cur.tc, cur.expert, wave, lane, smem);
-    if (tn >= total) break;
+    if constexpr (DEF) {
+      // the pending output was read from LDS during this tile's steps, whose
+      // barriers every wave has passed
+      p.stage_out(g, cur.tc);
+      __syncthreads();
+      if (tn >= total) {
+        p.flush();
+        break;
+      }
+    } else {
+      store_out<C, MODE>(p.acc, g, cur.tc, cur.expert, wave, lane, smem);
+      if (tn >= total) break;
+    }
     if (!C::OVERLAP) {
       p.set_tile(g, nxt.tc, g.M, nxt.bc, nxt.bs);
       p.prologue_loads();
@@ -743,7 +853,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::O
 // the expert and the first row; unused entries are skipped.
 template <class C, int MODE>
 constexpr int grouped_lds() {
-  return (MODE >= kOutSwiGlu0 && swiglu_lds<C>() > C::LDS_BYTES) ? swiglu_lds<C>() : C::LDS_BYTES;
+  return (is_swiglu(MODE) && swiglu_lds<C>() > C::LDS_BYTES) ? swiglu_lds<C>() : C::LDS_BYTES;
 }
 
 template <class C, int MODE>
@@ -812,7 +922,7 @@ using CfgM = TileCfg<CFGM>;  // prefill
 using CfgS64 = TileCfg<CFGS64>;  // decode, M <= 64
 using CfgS32 = TileCfg<CFGS32>;  // decode, M <= 32
 #ifndef CFGG
-#define CFGG 128, 256, 2, 2
+#define CFGG 128, 256, 2, 2, true, 1, true
 #endif
 using CfgG = TileCfg<CFGG>;  // grouped (MoE experts), bf16 / fp32 output
 #ifndef CFGGS
@@ -829,6 +939,12 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
   const int64_t resident = (int64_t)kNumCu * C::OCC;
   const int64_t grid = total < resident ? total : resident;
   const dim3 gd((unsigned)grid), bd(NT);
+  if constexpr (C::DEFER) {
+    if (g.splits == 1 && g.y_bf16 && g.vec16_y && g.N % 8 == 0 && g.ldy < kDeferMaxLd) {
+      hipLaunchKernelGGL((gemm_kernel<C, kOutBf16Defer>), gd, bd, 0, stream, g);
+      return hipGetLastError();
+    }
+  }
   if (g.splits > 1) hipLaunchKernelGGL((gemm_kernel<C, kOutPartial>), gd, bd, 0, stream, g);
   else if (g.y_bf16 && g.vec16_y) hipLaunchKernelGGL((gemm_kernel<C, kOutBf16Staged>), gd, bd, 0, stream, g);
   else if (g.y_bf16) hipLaunchKernelGGL((gemm_kernel<C, kOutBf16>), gd, bd, 0, stream, g);
@@ -858,6 +974,12 @@ hipError_t launch_grouped_cfg(const GemmArgs& g, hipStream_t stream) {
       default: hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutSwiGlu128>), gd, bd, 0, stream, g); break;
     }
   } else {
+    if constexpr (C::DEFER) {
+      if (g.y_bf16 && g.vec16_y && g.N % 8 == 0 && g.ldy < kDeferMaxLd) {
+        hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutBf16Defer>), gd, bd, 0, stream, g);
+        return hipGetLastError();
+      }
+    }
     if (g.y_bf16 && g.vec16_y) hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutBf16Staged>), gd, bd, 0, stream, g);
     else if (g.y_bf16) hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutBf16>), gd, bd, 0, stream, g);
     else hipLaunchKernelGGL((gemm_grouped_kernel<C, kOutF32>), gd, bd, 0, stream, g);

@@ -395,3 +395,43 @@ def test_linear_grouped_moe_full(dev, proj):
         y_o = oracle.linear(bits(mc.x)[rows], a_o, 32, wc_o, ws_o)
         err = rel_l2(yc[rows], y_o)
         assert err <= REL_L2_TOL, (e, err)
+
+
+def _grouped_bf16_vs_f32(dev, x, off, a, pw):
+    """The grouped layer's bf16 output is its fp32 output rounded to nearest
+    even: the same accumulators, only the epilogue differs (bf16 rows go out
+    through LDS and are written during the next tile's steps)."""
+    y32 = binding.linear_grouped(x, off, a, 32, pw, out_dtype=torch.float32)
+    y16 = binding.linear_grouped(x, off, a, 32, pw, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    want = y32.to(torch.bfloat16)
+    bad = int((y16.view(torch.int16) != want.view(torch.int16)).sum())
+    assert bad == 0, "%d of %d bf16 outputs differ from the rounded fp32 outputs" % (bad, y16.numel())
+
+
+def test_linear_grouped_bf16_output_moe_down(dev):
+    """MoE down projection (32768 expert rows, N = 2048, K = 768): many tiles
+    per workgroup and ragged expert tails."""
+    mc = inputs.moe_case("down")
+    log("grouped bf16 vs fp32 output, down T=%d E=%d K=%d N=%d" % (mc.T, mc.E, mc.K, mc.N))
+    _, a, pw = grouped_gpu(mc, dev, 32)
+    _grouped_bf16_vs_f32(dev, mc.x.to(dev), torch.from_numpy(mc.offsets).to(dev), a, pw)
+
+
+@pytest.mark.parametrize("N", [96, 200, 100])
+def test_linear_grouped_bf16_output_ragged(dev, N):
+    """Ragged N (a partial last column tile; N = 100 takes the path without
+    16-byte row alignment), empty and single-row experts."""
+    E, K = 6, 512
+    off = np.array([0, 0, 300, 301, 301, 700, 1000], np.int32)
+    T = int(off[-1])
+    log("grouped bf16 vs fp32 output, ragged N=%d T=%d" % (N, T))
+    rng = np.random.default_rng(N)
+    x = inputs.to_bf16(rng.standard_normal((T, K)).astype(np.float32))
+    a = torch.from_numpy((rng.random((E, K)) + 0.5).astype(np.float32)).to(dev)
+    wc = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    ws = rng.integers(118, 134, size=(E, N, K // 32), dtype=np.uint8)
+    tiles = [row_major_to_gemm_layout(wc[e], ws[e]) for e in range(E)]
+    pw = binding.Packed(torch.from_numpy(np.stack([t[0] for t in tiles])).to(dev),
+                        torch.from_numpy(np.stack([t[1] for t in tiles])).to(dev), N, K)
+    _grouped_bf16_vs_f32(dev, x.to(dev), torch.from_numpy(off).to(dev), a, pw)
