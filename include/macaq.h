@@ -232,15 +232,21 @@ macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t
    macaq_moe_gate_up, macaq_moe_down_combine and macaq_moe_block). */
 size_t macaq_moe_workspace_size(int64_t T, int32_t k, int32_t E, int64_t H, int64_t F);
 
+/* Bytes of workspace macaq_moe_route needs (0 for arguments it rejects). */
+size_t macaq_moe_route_workspace_size(int64_t T, int32_t k, int32_t E);
+
 /*
  * Routing: the stable sort of the T*k entries of ids by expert.
- * ids: device int32 [T, k], 16-byte aligned; offsets: device int32 [E+1]
+ * ids: device int32 [T, k], 16-byte aligned (may be NULL when T == 0); offsets: device int32 [E+1]
  * (rows of expert e are [offsets[e], offsets[e+1])); row_token: device int32
  * [T*k], the token of each row (rows past offsets[E] get token 0); pos:
- * device int32 [T*k], the row of entry i = t*k + j, or -1.
+ * device int32 [T*k], the row of entry i = t*k + j, or -1 for an id outside
+ * [0, E). workspace: macaq_moe_route_workspace_size bytes, 256-byte aligned
+ * (per-chunk expert counts; contents need not be cleared).
  */
 macaq_status macaq_moe_route(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* offsets,
-                             int32_t* row_token, int32_t* pos, macaq_stream_t stream);
+                             int32_t* row_token, int32_t* pos, void* workspace, size_t workspace_bytes,
+                             macaq_stream_t stream);
 
 /*
  * Gate/up of every routed row and the down projection's quantized input:

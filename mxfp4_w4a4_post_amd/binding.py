@@ -47,7 +47,8 @@ _SIGNATURES = {
     "macaq_linear_grouped": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _i64, _vp,
                                             ctypes.c_int, _vp, _sz, _vp]),
     "macaq_moe_workspace_size": (_sz, [_i64, _i32, _i32, _i64, _i64]),
-    "macaq_moe_route": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "macaq_moe_route_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "macaq_moe_route": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "macaq_moe_gate_up": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i64,
                                          _vp, _vp, _vp, _vp, _sz, _vp]),
     "macaq_moe_down_combine": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _i64, _i64, _vp,
@@ -323,7 +324,11 @@ def moe_workspace_size(T: int, k: int, E: int, H: int, F: int) -> int:
     return int(load_library().macaq_moe_workspace_size(T, k, E, H, F))
 
 
-def moe_route(ids: torch.Tensor, E: int):
+def moe_route_workspace_size(T: int, k: int, E: int) -> int:
+    return int(load_library().macaq_moe_route_workspace_size(T, k, E))
+
+
+def moe_route(ids: torch.Tensor, E: int, workspace: torch.Tensor | None = None):
     """(offsets [E+1], row_token [T*k], pos [T*k]) of the stable sort of the
     top-k entries ids [T, k] (int32) by expert."""
     _need_cuda(ids)
@@ -333,8 +338,9 @@ def moe_route(ids: torch.Tensor, E: int):
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     row_token = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
     pos = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
-    _check(load_library().macaq_moe_route(_ptr(ids), T, k, E, _ptr(offsets), _ptr(row_token), _ptr(pos),
-                                          _stream(ids)), "macaq_moe_route")
+    ws = _workspace(moe_route_workspace_size(T, k, E), dev, workspace)
+    _check(load_library().macaq_moe_route(_ptr(ids), T, k, E, _ptr(offsets), _ptr(row_token), _ptr(pos), _ptr(ws),
+                                          ws.numel(), _stream(ids)), "macaq_moe_route")
     return offsets, row_token[:T * k], pos[:T * k]
 
 

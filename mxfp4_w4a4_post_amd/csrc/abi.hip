@@ -103,13 +103,15 @@ macaq_status check_out(const void* Y, macaq_dtype dt, int64_t N, int64_t ldy, co
   return MACAQ_OK;
 }
 
-// Workspace of the MoE calls, R = T*k rows: routing arrays, the tile map of
-// the grouped GEMMs, the gathered gate/up input, the down input and the bf16
-// expert rows.
+// Workspace of the MoE calls, R = T*k rows: routing arrays and the routing
+// counts, the tile map of the grouped GEMMs, the gathered gate/up input, the
+// down input and the bf16 expert rows.
 struct MoeWs {
-  size_t offsets, row_token, pos, map, agu_codes, agu_scales, dn_codes, dn_scales, rows, total;
+  size_t offsets, row_token, pos, counts, map, agu_codes, agu_scales, dn_codes, dn_scales, rows, total;
   int64_t max_mtiles;
 };
+
+size_t route_counts_bytes(int64_t n, int32_t E) { return (size_t)moe_route_chunks(n) * (size_t)E * 4; }
 
 MoeWs moe_ws(int64_t T, int32_t k, int32_t E, int64_t H, int64_t F) {
   const int64_t R = T * k;
@@ -126,6 +128,7 @@ MoeWs moe_ws(int64_t T, int32_t k, int32_t E, int64_t H, int64_t F) {
   w.offsets = take((size_t)(E + 1) * 4);
   w.row_token = take((size_t)R * 4);
   w.pos = take((size_t)R * 4);
+  w.counts = take(route_counts_bytes(R, E));
   w.map = take(((size_t)w.max_mtiles * 2 + 1) * 4);
   w.agu_codes = take((size_t)tiled_codes_bytes(R, H));
   w.agu_scales = take((size_t)tiled_scales_bytes(R, H));
@@ -511,18 +514,29 @@ size_t macaq_moe_workspace_size(int64_t T, int32_t k, int32_t E, int64_t H, int6
   return moe_ws(T, k, E, H, F).total;
 }
 
+size_t macaq_moe_route_workspace_size(int64_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1 || E > kMaxExperts || T * (int64_t)k > 0x7FFFFFFF) return 0;
+  return round_up(route_counts_bytes(T * k, E), kWsAlign);
+}
+
 macaq_status macaq_moe_route(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* offsets,
-                             int32_t* row_token, int32_t* pos, macaq_stream_t stream) {
+                             int32_t* row_token, int32_t* pos, void* workspace, size_t workspace_bytes,
+                             macaq_stream_t stream) {
   const char* who = "macaq_moe_route";
   if (T < 0 || k < 1) return fail(MACAQ_EINVAL, "%s: T = %lld, k = %d", who, (long long)T, k);
   if (E < 1 || E > kMaxExperts) return fail(MACAQ_EINVAL, "%s: E = %d not in [1, %d]", who, E, kMaxExperts);
   if (T * (int64_t)k > 0x7FFFFFFF) return fail(MACAQ_EINVAL, "%s: T*k exceeds int32", who);
-  if (!ids || !offsets || !row_token || !pos) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
-  if (!aligned(ids, 16) || !aligned(offsets, 4) || !aligned(row_token, 4) || !aligned(pos, 4))
+  // with no entries ids is never read (an empty tensor may have no storage)
+  if ((!ids && T > 0) || !offsets || !row_token || !pos) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if ((ids && !aligned(ids, 16)) || !aligned(offsets, 4) || !aligned(row_token, 4) || !aligned(pos, 4))
     return fail(MACAQ_EALIGN, "%s: ids must be 16-byte aligned, the other int32 arrays 4-byte aligned", who);
+  const size_t need = macaq_moe_route_workspace_size(T, k, E);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign))
+    return fail(MACAQ_EWORKSPACE, "%s: need %zu workspace bytes, 256-byte aligned", who, need);
   macaq_status st = check_device();
   if (st != MACAQ_OK) return st;
-  hipError_t e = launch_moe_route(ids, T, k, E, offsets, row_token, pos, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = launch_moe_route(ids, T, k, E, offsets, row_token, pos, static_cast<int32_t*>(workspace),
+                                  reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_route launch");
 }
 
@@ -610,7 +624,8 @@ macaq_status macaq_moe_block(const void* X, int64_t T, int64_t H, int64_t ldx, c
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + w.offsets);
   int32_t* row_token = reinterpret_cast<int32_t*>(ws + w.row_token);
   int32_t* pos = reinterpret_cast<int32_t*>(ws + w.pos);
-  hipError_t e = launch_moe_route(ids, T, k, E, offsets, row_token, pos, s);
+  hipError_t e =
+      launch_moe_route(ids, T, k, E, offsets, row_token, pos, reinterpret_cast<int32_t*>(ws + w.counts), s);
   if (e != hipSuccess) return hip_fail(e, "macaq_moe_block routing launch");
   e = moe_gate_up_launch(X, T, H, ldx, k, row_token, offsets, E, a_gu, b, wgu_codes, wgu_scales, F, a_dn,
                          ws + w.dn_codes, ws + w.dn_scales, ws, w, true, s);

@@ -139,11 +139,13 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) 
   return incl - v;
 }
 
-// MoE block: routing (one workgroup per expert, at most kMaxExperts) and the
-// weighted combine of bf16 expert rows.
+// MoE block: routing (chunks of 1024 entries, at most kMaxExperts experts;
+// counts: int32 scratch [moe_route_chunks(T*k), E]) and the weighted combine
+// of bf16 expert rows.
 constexpr int kMaxExperts = 4096;
+int64_t moe_route_chunks(int64_t n);
 hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
-                            int32_t* pos, hipStream_t stream);
+                            int32_t* pos, int32_t* counts, hipStream_t stream);
 hipError_t launch_moe_combine(const uint16_t* rows, int64_t H, const int32_t* pos, const float* w, int64_t T, int k,
                               void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
 

@@ -15,209 +15,159 @@ namespace {
 
 constexpr int kRouteThreads = 256;
 
-// Entries are read in rounds of 1024 (16 bytes per thread, one coalesced
-// KiB per wave and round): entry i = 1024 j + 4 t + s lies in round j with
-// thread t, slot s. In that order (round, wave, lane, slot) the entries keep
-// their index order, so a rank among expert e's entries is the matches of
-// earlier rounds, then of lower waves in the round, then of lower lanes of
-// the wave (ballots), then of lower slots of the lane.
-constexpr int kRouteRound = 4 * kRouteThreads;
-constexpr int kRouteSegRounds = 1024;  // rounds whose wave counts sit in LDS at once
+// Routing works on chunks of kRouteChunk consecutive entries, 4 per thread
+// (thread t holds entries 4t .. 4t+3 of its chunk), one workgroup per chunk.
+// Pass one counts each chunk's entries per expert; pass two gives every
+// chunk the rows of its entries: expert e's rows start at the entries of all
+// chunks with an id below e, then come the chunk's predecessors' entries of
+// e, then the chunk's own in index order (a stable sort of the chunk by id).
+constexpr int kRouteChunk = 4 * kRouteThreads;
+constexpr int kRouteIdxBits = 10;  // an entry's place in its chunk
+static_assert(kRouteChunk == 1 << kRouteIdxBits, "chunk index bits");
 
-// Rounds are loaded kRouteBatch at a time, all loads of a batch in flight
-// together (a full batch is unconditional 16-byte loads).
-constexpr int kRouteBatch = 8;
-
-__device__ __forceinline__ void load_batch(const int32_t* __restrict__ ids, int64_t n, int64_t j,
-                                           int4 (&v)[kRouteBatch]) {
-  const int64_t i = j * kRouteRound + 4 * threadIdx.x;
-  if ((j + kRouteBatch) * kRouteRound <= n) {
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 #pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b) v[b] = *reinterpret_cast<const int4*>(ids + i + (int64_t)b * kRouteRound);
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// Exclusive scan of one int per thread over the workgroup (4 waves); *total
+// gets the sum. sh: 4 ints of LDS. Every thread must call it.
+__device__ __forceinline__ int route_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_inclusive_scan(v, lane);
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) before += w < wave ? sh[w] : 0;
+  *total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return before + incl - v;
+}
+
+// The 4 ids of this thread in chunk g: -2 past the end of the array.
+__device__ __forceinline__ void chunk_ids(const int32_t* __restrict__ ids, int64_t n, int64_t g, int (&v)[4]) {
+  const int64_t i = g * kRouteChunk + 4 * threadIdx.x;
+  if (i + 3 < n) {
+    const int4 q = *reinterpret_cast<const int4*>(ids + i);  // ids is 16-byte aligned
+    v[0] = q.x;
+    v[1] = q.y;
+    v[2] = q.z;
+    v[3] = q.w;
   } else {
 #pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b) {
-      const int64_t ib = i + (int64_t)b * kRouteRound;
-      v[b].x = ib < n ? ids[ib] : -1;
-      v[b].y = ib + 1 < n ? ids[ib + 1] : -1;
-      v[b].z = ib + 2 < n ? ids[ib + 2] : -1;
-      v[b].w = ib + 3 < n ? ids[ib + 3] : -1;
-    }
+    for (int s = 0; s < 4; ++s) v[s] = i + s < n ? ids[i + s] : -2;
   }
 }
 
-// Round j of this thread: from memory (batched loads) or from the LDS copy.
-struct RouteSrcGlobal {
-  const int32_t* ids;
-  int64_t n;
-  __device__ __forceinline__ void batch(int64_t j, int4 (&v)[kRouteBatch]) const { load_batch(ids, n, j, v); }
-};
-struct RouteSrcLds {
-  const int* sh;
-  __device__ __forceinline__ void batch(int64_t j, int4 (&v)[kRouteBatch]) const {
-#pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b)
-      v[b] = *reinterpret_cast<const int4*>(sh + (j + b) * kRouteRound + 4 * threadIdx.x);
-  }
-};
-
-// One workgroup per expert e: the entries with an id below e give where
-// expert e's rows start (offsets[e]); the entries with id e get their rows in
-// index order. Workgroup 0 also writes pos = -1 for ids outside [0, E);
-// workgroup E-1 writes offsets[E] and token 0 for the rows past the routed
-// ones (so every gather index stays in range).
-template <class Src>
-__device__ __forceinline__ void route_expert(const Src& src, int64_t n, int k, int E, int32_t* __restrict__ offsets,
-                                             int32_t* __restrict__ row_token, int32_t* __restrict__ pos, int* sh,
-                                             int* cnt) {
-  const int tid = threadIdx.x, e = blockIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint64_t below_mask = (uint64_t(1) << lane) - 1;
-  const int64_t rounds = (n + kRouteRound - 1) / kRouteRound;
-  int below = 0;
-  for (int64_t j = 0; j < rounds; j += kRouteBatch) {
-    int4 v[kRouteBatch];
-    src.batch(j, v);
-#pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b)
-      below += ((v[b].x >= 0) & (v[b].x < e)) + ((v[b].y >= 0) & (v[b].y < e)) + ((v[b].z >= 0) & (v[b].z < e)) +
-               ((v[b].w >= 0) & (v[b].w < e));
-  }
-  int first = 0;
-  block_exclusive_scan<kRouteThreads>(below, sh, &first);
-  int row0 = first;  // first row of the current segment
-  for (int64_t j0 = 0; j0 < rounds; j0 += kRouteSegRounds) {
-    const int nr = (int)(rounds - j0 < kRouteSegRounds ? rounds - j0 : kRouteSegRounds);
-    // matches of each (round, wave)
-    for (int r0 = 0; r0 < nr; r0 += kRouteBatch) {
-      int4 v[kRouteBatch];
-      src.batch(j0 + r0, v);
-#pragma unroll
-      for (int b = 0; b < kRouteBatch; ++b) {
-        const int c = __popcll(__ballot(v[b].x == e)) + __popcll(__ballot(v[b].y == e)) +
-                      __popcll(__ballot(v[b].z == e)) + __popcll(__ballot(v[b].w == e));
-        if (lane == 0 && r0 + b < nr) cnt[4 * (r0 + b) + wave] = c;
-      }
-    }
-    __syncthreads();
-    // exclusive prefix over (round, wave) in place: thread t scans a slice
-    const int m = 4 * nr, per = (m + kRouteThreads - 1) / kRouteThreads;
-    const int a0 = tid * per < m ? tid * per : m, a1 = a0 + per < m ? a0 + per : m;
-    int part = 0;
-    for (int i = a0; i < a1; ++i) part += cnt[i];
-    int seg_total = 0;
-    int acc = block_exclusive_scan<kRouteThreads>(part, sh, &seg_total);
-    for (int i = a0; i < a1; ++i) {
-      const int c = cnt[i];
-      cnt[i] = acc;
-      acc += c;
-    }
-    __syncthreads();
-    for (int r0 = 0; r0 < nr; r0 += kRouteBatch) {
-      int4 v[kRouteBatch];
-      src.batch(j0 + r0, v);
-#pragma unroll
-      for (int b = 0; b < kRouteBatch; ++b) {
-        if (r0 + b >= nr) break;
-        const int vv[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
-        const int64_t i0 = (j0 + r0 + b) * kRouteRound + 4 * tid;
-        const bool any = (vv[0] == e) | (vv[1] == e) | (vv[2] == e) | (vv[3] == e);
-        int rank = row0 + cnt[4 * (r0 + b) + wave];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) rank += __popcll(__ballot(vv[q] == e) & below_mask);
-        if (any) {
-          // token of entry i0 + q: one 32-bit division for the quad, then carries
-          const uint32_t i32 = (uint32_t)i0;
-          uint32_t tok = i32 / (uint32_t)k, rem = i32 - tok * (uint32_t)k;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (vv[q] == e) {
-              row_token[rank] = (int32_t)tok;
-              pos[i0 + q] = rank;
-              ++rank;
-            }
-            if (++rem == (uint32_t)k) {
-              rem = 0;
-              ++tok;
-            }
-          }
-        }
-        if (e == 0) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (i0 + q < n && (vv[q] < 0 || vv[q] >= E)) pos[i0 + q] = -1;
-        }
-      }
-    }
-    row0 += seg_total;
-    __syncthreads();  // cnt is rewritten by the next segment
-  }
-  if (tid == 0) offsets[e] = first;
-  if (e == E - 1) {
-    if (tid == 0) offsets[E] = row0;
-    for (int64_t r = row0 + tid; r < n; r += kRouteThreads) row_token[r] = 0;
-  }
-}
-
-__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t* __restrict__ ids, int64_t n, int k,
-                                                                 int E, int32_t* __restrict__ offsets,
-                                                                 int32_t* __restrict__ row_token,
-                                                                 int32_t* __restrict__ pos) {
-  __shared__ int sh[kRouteThreads];
-  __shared__ int cnt[kRouteSegRounds * 4];
-  route_expert(RouteSrcGlobal{ids, n}, n, k, E, offsets, row_token, pos, sh, cnt);
-}
-
-// Up to kRouteLdsEntries entries: the workgroup first copies all of them to
-// LDS with coalesced, unconditional loads (addresses clamped into the array,
-// values past n replaced by -1), all in flight at once, so every pass after
-// that reads LDS. QUAD: n is a multiple of 4, so the copy moves 16 bytes per
-// load (entries 4t + 1024r .. +3 of round r); otherwise 4 bytes per load.
-constexpr int kRouteLdsEntries = 32 * kRouteRound;  // 32768
-
-template <bool QUAD>
-__global__ __launch_bounds__(kRouteThreads) void moe_route_lds_kernel(const int32_t* __restrict__ ids, int64_t n,
-                                                                     int k, int E, int32_t* __restrict__ offsets,
-                                                                     int32_t* __restrict__ row_token,
-                                                                     int32_t* __restrict__ pos) {
-  __shared__ int sh[kRouteThreads];
-  __shared__ int cnt[32 * 4];
-  __shared__ __attribute__((aligned(16))) int all[kRouteLdsEntries];
+// counts[g * E + e] = entries of chunk g with id e.
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_t* __restrict__ ids, int64_t n, int E,
+                                                                    int32_t* __restrict__ counts) {
+  __shared__ int hist[kMaxExperts];
   const int tid = threadIdx.x;
-  const int rounds = (int)((n + kRouteRound - 1) / kRouteRound);
-  const int padded = ((rounds + kRouteBatch - 1) / kRouteBatch) * kRouteBatch * kRouteRound;
-  if constexpr (QUAD) {
-    constexpr int R = kRouteLdsEntries / kRouteRound;  // 32 rounds
-    int4 v[R];
+  for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
+  __syncthreads();
+  int v[4];
+  chunk_ids(ids, n, blockIdx.x, v);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t q = (int64_t)r * kRouteRound + 4 * tid;
-      v[r] = *reinterpret_cast<const int4*>(ids + (q < n ? q : n - 4));
+  for (int s = 0; s < 4; ++s)
+    if (v[s] >= 0 && v[s] < E) atomicAdd(&hist[v[s]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += kRouteThreads) counts[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Rows of chunk g's entries (G chunks). Workgroup 0 writes offsets; ids
+// outside [0, E) get pos = -1; rows past the routed ones get token 0.
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int32_t* __restrict__ ids, int64_t n,
+                                                                      int k, int E, const int32_t* __restrict__ counts,
+                                                                      int G, int32_t* __restrict__ offsets,
+                                                                      int32_t* __restrict__ row_token,
+                                                                      int32_t* __restrict__ pos) {
+  __shared__ int base[kMaxExperts];   // first row of this chunk's entries of e
+  __shared__ int first[kMaxExperts];  // expert totals, then the sorted place of e's first entry
+  __shared__ int buf[kRouteChunk];
+  __shared__ int sh[4];
+  const int tid = threadIdx.x, g = blockIdx.x;
+  // entries of e in earlier chunks and in all chunks
+  for (int e = tid; e < E; e += kRouteThreads) {
+    int bef = 0, tot = 0;
+    for (int c = 0; c < G; ++c) {
+      const int v = counts[(int64_t)c * E + e];
+      tot += v;
+      bef += c < g ? v : 0;
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int q = r * kRouteRound + 4 * tid;
-      if (q < padded) {
-        const bool in = q < n;
-        *reinterpret_cast<int4*>(all + q) =
-            make_int4(in ? v[r].x : -1, in ? v[r].y : -1, in ? v[r].z : -1, in ? v[r].w : -1);
-      }
-    }
-  } else {
-    constexpr int PER = kRouteLdsEntries / kRouteThreads;  // 128
-    int v[PER];
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int64_t i = tid + (int64_t)m * kRouteThreads;
-      v[m] = ids[i < n ? i : n - 1];
-    }
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int i = tid + m * kRouteThreads;
-      if (i < padded) all[i] = i < n ? v[m] : -1;
-    }
+    base[e] = bef;
+    first[e] = tot;
   }
   __syncthreads();
-  route_expert(RouteSrcLds{all}, n, k, E, offsets, row_token, pos, sh, cnt);
+  // offsets: exclusive scan of the totals, thread t over experts [t*EP, (t+1)*EP)
+  const int EP = (E + kRouteThreads - 1) / kRouteThreads;
+  const int e0 = tid * EP < E ? tid * EP : E, e1 = e0 + EP < E ? e0 + EP : E;
+  int part = 0;
+  for (int e = e0; e < e1; ++e) part += first[e];
+  int routed = 0;
+  int acc = route_scan(part, sh, &routed);
+  for (int e = e0; e < e1; ++e) {
+    const int c = first[e];
+    if (g == 0) offsets[e] = acc;
+    base[e] += acc;
+    acc += c;
+  }
+  if (g == 0 && tid == 0) offsets[E] = routed;
+  // stable sort of the chunk by key (id; E for an id out of range, E + 1 past
+  // the end), one key bit per pass; a key and the entry's place pack into one int
+  int v[4], pk[4];
+  chunk_ids(ids, n, g, v);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int key = v[s] == -2 ? E + 1 : (v[s] >= 0 && v[s] < E ? v[s] : E);
+    pk[s] = (key << kRouteIdxBits) | (4 * tid + s);
+  }
+  const int bits = 32 - __clz(E + 1);
+  for (int bit = 0; bit < bits; ++bit) {
+    bool zero[4];
+    int z = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      zero[s] = ((pk[s] >> (kRouteIdxBits + bit)) & 1) == 0;
+      z += zero[s];
+    }
+    int zeros = 0;
+    int zp = route_scan(z, sh, &zeros);
+    int op = zeros + 4 * tid - zp;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) buf[zero[s] ? zp++ : op++] = pk[s];
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) pk[s] = buf[4 * tid + s];
+    __syncthreads();
+  }
+  // sorted place p = 4t + s; the first place of each expert's run
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int p = 4 * tid + s, key = pk[s] >> kRouteIdxBits;
+    const int prev = p == 0 ? -1 : (s > 0 ? pk[s - 1] : buf[p - 1]) >> kRouteIdxBits;
+    if (key < E && key != prev) first[key] = p;
+  }
+  __syncthreads();
+  const int64_t c0 = (int64_t)g * kRouteChunk;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int key = pk[s] >> kRouteIdxBits;
+    const int64_t i = c0 + (pk[s] & (kRouteChunk - 1));
+    if (key < E) {
+      const int row = base[key] + (4 * tid + s - first[key]);
+      pos[i] = row;
+      row_token[row] = (int32_t)((uint32_t)i / (uint32_t)k);
+    } else if (key == E) {
+      pos[i] = -1;
+    }
+  }
+  for (int64_t r = routed + (int64_t)g * kRouteThreads + tid; r < n; r += (int64_t)G * kRouteThreads) row_token[r] = 0;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -279,22 +229,16 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __rest
 
 }  // namespace
 
+int64_t moe_route_chunks(int64_t n) { return n > 0 ? (n + kRouteChunk - 1) / kRouteChunk : 1; }
+
 hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
-                            int32_t* pos, hipStream_t stream) {
-  const int64_t n = T * k;
-  if (n == 0) {
-    hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)E), dim3(kRouteThreads), 0, stream, ids, n, k, E, offsets,
-                       row_token, pos);
-  } else if (n <= kRouteLdsEntries && n % 4 == 0) {
-    hipLaunchKernelGGL(moe_route_lds_kernel<true>, dim3((unsigned)E), dim3(kRouteThreads), 0, stream, ids, n, k, E,
-                       offsets, row_token, pos);
-  } else if (n <= kRouteLdsEntries) {
-    hipLaunchKernelGGL(moe_route_lds_kernel<false>, dim3((unsigned)E), dim3(kRouteThreads), 0, stream, ids, n, k, E,
-                       offsets, row_token, pos);
-  } else {
-    hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)E), dim3(kRouteThreads), 0, stream, ids, n, k, E, offsets,
-                       row_token, pos);
-  }
+                            int32_t* pos, int32_t* counts, hipStream_t stream) {
+  const int64_t n = T * k, G = moe_route_chunks(n);
+  hipLaunchKernelGGL(route_count_kernel, dim3((unsigned)G), dim3(kRouteThreads), 0, stream, ids, n, E, counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)G), dim3(kRouteThreads), 0, stream, ids, n, k, E, counts,
+                     (int)G, offsets, row_token, pos);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding._SIGNATURES), "binding signatures out of sync with the header"
@@ -146,13 +146,18 @@ def test_binding_has_no_cpu_fallback():
 def test_moe_calls_reject(lib):
     """Host checks of the MoE block calls (nothing is dereferenced)."""
     ws = 1 << 30
-    # route: bad E, k, T*k overflow, NULL, misaligned
-    assert lib.macaq_moe_route(FAKE, 16, 2, 0, FAKE, FAKE, FAKE, None) == EINVAL
-    assert lib.macaq_moe_route(FAKE, 16, 2, 5000, FAKE, FAKE, FAKE, None) == EINVAL
-    assert lib.macaq_moe_route(FAKE, 16, 0, 8, FAKE, FAKE, FAKE, None) == EINVAL
-    assert lib.macaq_moe_route(FAKE, 1 << 30, 8, 8, FAKE, FAKE, FAKE, None) == EINVAL
-    assert lib.macaq_moe_route(None, 16, 2, 8, FAKE, FAKE, FAKE, None) == EINVAL
-    assert lib.macaq_moe_route(FAKE + 2, 16, 2, 8, FAKE, FAKE, FAKE, None) == EALIGN
+    # route: bad E, k, T*k overflow, NULL, misaligned, short or missing workspace
+    assert lib.macaq_moe_route(FAKE, 16, 2, 0, FAKE, FAKE, FAKE, FAKE, ws, None) == EINVAL
+    assert lib.macaq_moe_route(FAKE, 16, 2, 5000, FAKE, FAKE, FAKE, FAKE, ws, None) == EINVAL
+    assert lib.macaq_moe_route(FAKE, 16, 0, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == EINVAL
+    assert lib.macaq_moe_route(FAKE, 1 << 30, 8, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == EINVAL
+    assert lib.macaq_moe_route(None, 16, 2, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == EINVAL
+    assert lib.macaq_moe_route(FAKE + 2, 16, 2, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == EALIGN
+    need = lib.macaq_moe_route_workspace_size(16, 2, 8)
+    assert need >= 8 * 4 and lib.macaq_moe_route_workspace_size(16, 2, 0) == 0
+    assert lib.macaq_moe_route(FAKE, 16, 2, 8, FAKE, FAKE, FAKE, FAKE, need - 1, None) == EWORKSPACE
+    assert lib.macaq_moe_route(FAKE, 16, 2, 8, FAKE, FAKE, FAKE, None, need, None) == EWORKSPACE
+    assert lib.macaq_moe_route(FAKE, 16, 2, 8, FAKE, FAKE, FAKE, FAKE + 16, need, None) == EWORKSPACE
 
     def gate_up(X=FAKE, T=16, H=256, ldx=256, k=2, E=8, a_gu=FAKE, b=32, F=128, a_dn=FAKE, dn=FAKE, wsb=ws,
                 wsp=FAKE):

@@ -101,7 +101,11 @@ def assert_dn_close(gc, gs, oc, os_, what):
 # Routing: bit-exact
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("T,k,E,bad", [(1, 1, 1, False), (37, 3, 5, True), (64, 8, 16, False), (300, 2, 700, True)])
+@pytest.mark.parametrize("T,k,E,bad", [(1, 1, 1, False), (37, 3, 5, True), (64, 8, 16, False), (300, 2, 700, True),
+                                       (0, 4, 8, False),       # no entries
+                                       (700, 3, 4096, True),   # 3 chunks of 1024 entries, the last ragged
+                                       (5001, 8, 64, True),    # 40 chunks, ragged tail
+                                       (2048, 8, 1, False)])   # one expert takes every entry
 def test_route_bit_exact(dev, T, k, E, bad):
     log("route T=%d k=%d E=%d bad=%s" % (T, k, E, bad))
     rng = np.random.default_rng(T + 10 * k + E)
