@@ -107,7 +107,7 @@ macaq_status check_out(const void* Y, macaq_dtype dt, int64_t N, int64_t ldy, co
 // counts, the tile map of the grouped GEMMs, the gathered gate/up input, the
 // down input and the bf16 expert rows.
 struct MoeWs {
-  size_t offsets, row_token, pos, counts, map, agu_codes, agu_scales, dn_codes, dn_scales, rows, total;
+  size_t offsets, row_token, pos, counts, map, map2, agu_codes, agu_scales, dn_codes, dn_scales, rows, total;
   int64_t max_mtiles;
 };
 
@@ -130,6 +130,7 @@ MoeWs moe_ws(int64_t T, int32_t k, int32_t E, int64_t H, int64_t F) {
   w.pos = take((size_t)R * 4);
   w.counts = take(route_counts_bytes(R, E));
   w.map = take(((size_t)w.max_mtiles * 2 + 1) * 4);
+  w.map2 = take(((size_t)w.max_mtiles * 2 + 1) * 4);  // the down GEMM's, when its tile rows differ
   w.agu_codes = take((size_t)tiled_codes_bytes(R, H));
   w.agu_scales = take((size_t)tiled_scales_bytes(R, H));
   w.dn_codes = take((size_t)tiled_codes_bytes(R, F));
@@ -157,8 +158,8 @@ macaq_status check_moe_shape(int64_t T, int32_t k, int32_t E, int64_t H, int64_t
 hipError_t moe_gate_up_launch(const void* X, int64_t T, int64_t H, int64_t ldx, int32_t k, const int32_t* row_token,
                               const int32_t* offsets, int32_t E, const float* a_gu, int32_t b,
                               const uint8_t* wgu_codes, const uint8_t* wgu_scales, int64_t F, const float* a_dn,
-                              uint8_t* dn_codes, uint8_t* dn_scales, uint8_t* ws, const MoeWs& w, bool build_map,
-                              hipStream_t s) {
+                              uint8_t* dn_codes, uint8_t* dn_scales, uint8_t* ws, const MoeWs& w, int32_t* map,
+                              bool build_map, hipStream_t s) {
   const int64_t R = T * k;
   QuantArgs q{};
   q.x = X;
@@ -186,7 +187,7 @@ hipError_t moe_gate_up_launch(const void* X, int64_t T, int64_t H, int64_t ldx, 
   g.K = H;
   g.splits = 1;
   g.offsets = offsets;
-  g.tile_map = reinterpret_cast<int32_t*>(ws + w.map);
+  g.tile_map = map;
   g.E = E;
   g.max_mtiles = w.max_mtiles;
   g.map_ready = !build_map;
@@ -203,7 +204,7 @@ hipError_t moe_down_combine_launch(const uint8_t* dn_codes, const uint8_t* dn_sc
                                    const int32_t* pos, const float* w_route, int64_t T, int32_t k, int32_t E,
                                    const uint8_t* wdn_codes, const uint8_t* wdn_scales, int64_t H, int64_t F,
                                    void* Y, macaq_dtype y_dtype, int64_t ldy, uint8_t* ws, const MoeWs& w,
-                                   bool build_map, hipStream_t s) {
+                                   int32_t* map, bool build_map, hipStream_t s) {
   const int64_t R = T * k;
   uint16_t* rows = reinterpret_cast<uint16_t*>(ws + w.rows);
   GemmArgs g{};
@@ -219,7 +220,7 @@ hipError_t moe_down_combine_launch(const uint8_t* dn_codes, const uint8_t* dn_sc
   g.y_bf16 = true;
   g.splits = 1;
   g.offsets = offsets;
-  g.tile_map = reinterpret_cast<int32_t*>(ws + w.map);
+  g.tile_map = map;
   g.E = E;
   g.max_mtiles = w.max_mtiles;
   g.map_ready = !build_map;
@@ -536,7 +537,7 @@ macaq_status macaq_moe_route(const int32_t* ids, int64_t T, int32_t k, int32_t E
   macaq_status st = check_device();
   if (st != MACAQ_OK) return st;
   hipError_t e = launch_moe_route(ids, T, k, E, offsets, row_token, pos, static_cast<int32_t*>(workspace),
-                                  reinterpret_cast<hipStream_t>(stream));
+                                  RouteMaps{{nullptr, nullptr}, {0, 0}, 0}, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_route launch");
 }
 
@@ -563,7 +564,8 @@ macaq_status macaq_moe_gate_up(const void* X, int64_t T, int64_t H, int64_t ldx,
   st = check_device();
   if (st != MACAQ_OK) return st;
   hipError_t e = moe_gate_up_launch(X, T, H, ldx, k, row_token, offsets, E, a_gu, b, wgu_codes, wgu_scales, F, a_dn,
-                                    dn_codes, dn_scales, static_cast<uint8_t*>(workspace), w, true,
+                                    dn_codes, dn_scales, static_cast<uint8_t*>(workspace), w,
+                                    reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + w.map), true,
                                     reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_gate_up launch");
 }
@@ -590,7 +592,8 @@ macaq_status macaq_moe_down_combine(const uint8_t* dn_codes, const uint8_t* dn_s
   st = check_device();
   if (st != MACAQ_OK) return st;
   hipError_t e = moe_down_combine_launch(dn_codes, dn_scales, offsets, pos, w_route, T, k, E, wdn_codes, wdn_scales,
-                                         H, F, Y, y_dtype, ldy, static_cast<uint8_t*>(workspace), w, true,
+                                         H, F, Y, y_dtype, ldy, static_cast<uint8_t*>(workspace), w,
+                                         reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + w.map), true,
                                          reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_down_combine launch");
 }
@@ -624,16 +627,20 @@ macaq_status macaq_moe_block(const void* X, int64_t T, int64_t H, int64_t ldx, c
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + w.offsets);
   int32_t* row_token = reinterpret_cast<int32_t*>(ws + w.row_token);
   int32_t* pos = reinterpret_cast<int32_t*>(ws + w.pos);
+  // the routing also writes the tile maps of both grouped GEMMs (one map when
+  // their tiles have the same rows)
+  const int bm_gu = plan_gemm_grouped(T * k, E, 2 * F, H, true).bm, bm_dn = plan_gemm_grouped(T * k, E, H, F).bm;
+  int32_t* map_gu = reinterpret_cast<int32_t*>(ws + w.map);
+  int32_t* map_dn = bm_dn == bm_gu ? map_gu : reinterpret_cast<int32_t*>(ws + w.map2);
+  const RouteMaps maps{{map_gu, bm_dn == bm_gu ? nullptr : map_dn}, {bm_gu, bm_dn}, w.max_mtiles};
   hipError_t e =
-      launch_moe_route(ids, T, k, E, offsets, row_token, pos, reinterpret_cast<int32_t*>(ws + w.counts), s);
+      launch_moe_route(ids, T, k, E, offsets, row_token, pos, reinterpret_cast<int32_t*>(ws + w.counts), maps, s);
   if (e != hipSuccess) return hip_fail(e, "macaq_moe_block routing launch");
   e = moe_gate_up_launch(X, T, H, ldx, k, row_token, offsets, E, a_gu, b, wgu_codes, wgu_scales, F, a_dn,
-                         ws + w.dn_codes, ws + w.dn_scales, ws, w, true, s);
+                         ws + w.dn_codes, ws + w.dn_scales, ws, w, map_gu, false, s);
   if (e != hipSuccess) return hip_fail(e, "macaq_moe_block gate/up launch");
-  // the map built for the gate/up GEMM serves the down GEMM when both use the same tile rows
-  const bool same_bm = plan_gemm_grouped(T * k, E, 2 * F, H, true).bm == plan_gemm_grouped(T * k, E, H, F).bm;
   e = moe_down_combine_launch(ws + w.dn_codes, ws + w.dn_scales, offsets, pos, w_route, T, k, E, wdn_codes,
-                              wdn_scales, H, F, Y, y_dtype, ldy, ws, w, !same_bm, s);
+                              wdn_scales, H, F, Y, y_dtype, ldy, ws, w, map_dn, false, s);
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_block down/combine launch");
 }
 

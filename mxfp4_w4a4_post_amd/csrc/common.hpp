@@ -144,8 +144,15 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) 
 // of bf16 expert rows.
 constexpr int kMaxExperts = 4096;
 int64_t moe_route_chunks(int64_t n);
+// Tile maps of grouped GEMMs over the routed rows that the routing can write
+// as it goes (map[i] == nullptr: none), each of max_mtiles entries.
+struct RouteMaps {
+  int32_t* map[2];
+  int bm[2];
+  int64_t max_mtiles;
+};
 hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
-                            int32_t* pos, int32_t* counts, hipStream_t stream);
+                            int32_t* pos, int32_t* counts, const RouteMaps& maps, hipStream_t stream);
 hipError_t launch_moe_combine(const uint16_t* rows, int64_t H, const int32_t* pos, const float* w, int64_t T, int k,
                               void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
 

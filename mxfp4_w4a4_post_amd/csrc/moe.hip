@@ -80,13 +80,40 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_
   for (int e = tid; e < E; e += kRouteThreads) counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// Rows of chunk g's entries (G chunks). Workgroup 0 writes offsets; ids
-// outside [0, E) get pos = -1; rows past the routed ones get token 0.
+// The tile map of a grouped GEMM with tiles of bm rows from the expert
+// totals and first rows of experts [e0, e1) of this thread: m-tile j of
+// expert e gets entry (tiles of experts before e) + j, the remaining entries
+// expert -1, and map[2 * max_mtiles] the number of used entries (the format
+// build_tile_map_kernel writes). Every thread of the workgroup calls it.
+__device__ __forceinline__ void route_tile_map(int32_t* __restrict__ map, int bm, int64_t max_mtiles, int e0, int e1,
+                                               const int* tot, const int* first_row, int* sh) {
+  int cnt = 0;
+  for (int e = e0; e < e1; ++e) cnt += (tot[e] + bm - 1) / bm;
+  int used = 0;
+  int64_t acc = route_scan(cnt, sh, &used);
+  for (int e = e0; e < e1; ++e) {
+    const int tiles = (tot[e] + bm - 1) / bm;
+    for (int j = 0; j < tiles && acc < max_mtiles; ++j, ++acc) {
+      map[2 * acc] = e;
+      map[2 * acc + 1] = first_row[e] + j * bm;
+    }
+  }
+  const int64_t n_used = used < max_mtiles ? used : max_mtiles;
+  for (int64_t i = n_used + threadIdx.x; i < max_mtiles; i += kRouteThreads) {
+    map[2 * i] = -1;
+    map[2 * i + 1] = 0;
+  }
+  if (threadIdx.x == 0) map[2 * max_mtiles] = (int32_t)n_used;
+}
+
+// Rows of chunk g's entries (G chunks). Workgroup 0 writes offsets (and the
+// tile maps m.map[i] of tiles of m.bm[i] rows, where given); ids outside
+// [0, E) get pos = -1; rows past the routed ones get token 0.
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int32_t* __restrict__ ids, int64_t n,
                                                                       int k, int E, const int32_t* __restrict__ counts,
                                                                       int G, int32_t* __restrict__ offsets,
                                                                       int32_t* __restrict__ row_token,
-                                                                      int32_t* __restrict__ pos) {
+                                                                      int32_t* __restrict__ pos, RouteMaps m) {
   __shared__ int base[kMaxExperts];   // first row of this chunk's entries of e
   __shared__ int first[kMaxExperts];  // expert totals, then the sorted place of e's first entry
   __shared__ int buf[kRouteChunk];
@@ -118,6 +145,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int3
     acc += c;
   }
   if (g == 0 && tid == 0) offsets[E] = routed;
+  if (g == 0) {  // base[e] is offsets[e] here (no earlier chunks)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (m.map[i]) route_tile_map(m.map[i], m.bm[i], m.max_mtiles, e0, e1, first, base, sh);
+  }
   // stable sort of the chunk by key (id; E for an id out of range, E + 1 past
   // the end), one key bit per pass; a key and the entry's place pack into one int
   int v[4], pk[4];
@@ -232,13 +264,13 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __rest
 int64_t moe_route_chunks(int64_t n) { return n > 0 ? (n + kRouteChunk - 1) / kRouteChunk : 1; }
 
 hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
-                            int32_t* pos, int32_t* counts, hipStream_t stream) {
+                            int32_t* pos, int32_t* counts, const RouteMaps& maps, hipStream_t stream) {
   const int64_t n = T * k, G = moe_route_chunks(n);
   hipLaunchKernelGGL(route_count_kernel, dim3((unsigned)G), dim3(kRouteThreads), 0, stream, ids, n, E, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)G), dim3(kRouteThreads), 0, stream, ids, n, k, E, counts,
-                     (int)G, offsets, row_token, pos);
+                     (int)G, offsets, row_token, pos, maps);
   return hipGetLastError();
 }
 
