@@ -45,7 +45,7 @@ METRIC = "W4A4 fused linear TFLOPS (% MXFP4 peak); transform overhead vs plain M
 PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ROTATE = 4                  # operand copies cycled through by the timed steps
-ORACLE_THREADS_CAP = 16     # the GPU machine's CPU share for one GPU
+ORACLE_THREADS_CAP = 16     # one GPU's share of the host CPU
 WORKLOADS = {"tiny": 1, "prefill-8b": 2, "decode-32b": 3, "moe-128e": 4, "prefill-large": 5, "moe-block": 6,
              "refine-8b": 7, "quant-error": 8, "prepare-stream": 9}
 PREPARE_STREAM = 9  # offline: a stack of 8B-shaped blocks prepared from pinned host memory, one layer resident
@@ -122,7 +122,7 @@ class Entry:
 
 
 def dense_entries(torch, binding, inputs, wl, b, dev):
-    spec = inputs.CONFIGS[wl]
+    spec = inputs.WORKLOAD_SPECS[wl]
     Ms = [spec["M"]] if "M" in spec else list(spec["Ms"])
     entries = []
     for si, (K, N) in enumerate(spec["shapes"]):
@@ -252,7 +252,7 @@ def refine_main(args, torch, binding, inputs, dev):
     layer, the Hessian of the calibration rows and the refinement of freshly
     prepared (round-to-nearest) codes. Timed with HIP events, eagerly."""
     import numpy as np
-    spec = inputs.CONFIGS[2]
+    spec = inputs.WORKLOAD_SPECS[2]
     b = args.block if args.block is not None else spec["blocks"][0]
     layers = []
     for si, (K, N) in enumerate(spec["shapes"]):
@@ -654,7 +654,7 @@ def load_traffic(workload, kernel_digest):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the design notes describe how the "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the design notes describe how the "
               "layer would shard); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
@@ -701,7 +701,7 @@ def main():
     if wl == PREPARE_STREAM:
         prepare_stream_main(args, torch, binding, inputs, dev)
         return
-    spec = inputs.CONFIGS[4 if wl == MOE_BLOCK else wl]
+    spec = inputs.WORKLOAD_SPECS[4 if wl == MOE_BLOCK else wl]
     b = args.block if args.block is not None else spec["blocks"][0]
     moe = wl == 4
     if wl == MOE_BLOCK:

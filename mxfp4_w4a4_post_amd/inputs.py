@@ -37,7 +37,7 @@ DECODE_32B = dict(name="decode-32b", Ms=[1, 8, 32, 64], shapes=[(5120, 25600), (
 MOE = dict(name="moe-128e", tokens=4096, experts=128, top_k=8, hidden=2048, ffn=768, zipf=1.1, blocks=[32])
 PREFILL_LARGE = dict(name="prefill-large", M=8192, shapes=[(8192, 28672), (28672, 8192)], blocks=[32, 64, 128])
 
-CONFIGS = {1: TINY, 2: PREFILL_8B, 3: DECODE_32B, 4: MOE, 5: PREFILL_LARGE}
+WORKLOAD_SPECS = {1: TINY, 2: PREFILL_8B, 3: DECODE_32B, 4: MOE, 5: PREFILL_LARGE}
 
 
 def _rng(cfg: int, shape_idx: int, stream: int) -> np.random.Generator:
@@ -116,7 +116,7 @@ class LinearCase:
 
     @property
     def name(self) -> str:
-        return "%s M=%d K=%d N=%d b=%d" % (CONFIGS[self.cfg]["name"], self.M, self.K, self.N, self.b)
+        return "%s M=%d K=%d N=%d b=%d" % (WORKLOAD_SPECS[self.cfg]["name"], self.M, self.K, self.N, self.b)
 
 
 def linear_case(cfg: int, shape_idx: int = 0, M: int | None = None, b: int | None = None,
@@ -126,7 +126,7 @@ def linear_case(cfg: int, shape_idx: int = 0, M: int | None = None, b: int | Non
     ``M``/``K``/``N`` override the workload's sizes (smaller parity cases keep
     the same distributions); ``b`` picks the Hadamard block.
     """
-    spec = CONFIGS[cfg]
+    spec = WORKLOAD_SPECS[cfg]
     if cfg == 4:
         raise ValueError("the MoE workload is built by moe_case")
     k0, n0 = spec["shapes"][shape_idx]

@@ -50,7 +50,7 @@ def assert_quant_equal(g_codes, g_scales, o_codes, o_scales, t_oracle=None, what
     gu, ou = unpack(g_codes), unpack(o_codes)
     bad = np.argwhere(gu != ou)
     frac = len(bad) / gu.size
-    assert t_oracle is not None, "%s: %d codes differ and no pre-quant values to judge ties" % (what, len(bad))
+    assert t_oracle is not None, "%s: %d codes differ and no pre-quant values to check ties against" % (what, len(bad))
     assert frac <= CODE_SLIP_FRACTION, "%s: %d codes differ (%.2e of all)" % (what, len(bad), frac)
     sc = np.asarray(o_scales).astype(np.int64)
     for r, k in bad:
