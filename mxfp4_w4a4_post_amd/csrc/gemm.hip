@@ -684,17 +684,20 @@ struct Pipe {
   }
 
   // Issue order: activation steps 0 and 1 (to LDS buffers 0 and 1 through
-  // registers of their own), the activation slots of steps 2 .. PA+1, the
-  // weight slots of steps 0 .. PW-1. The fences keep that order, which is
-  // the order of the steady state, so the first waits of the loop cover
-  // only loads as old as they need.
+  // registers of their own) and the weight slot of step 0, which is all the
+  // first step waits for, then the activation slots of steps 2 .. PA+1 and
+  // the weight slots of steps 1 .. PW-1. The fences keep that order, so the
+  // first step starts once its own operands are in, not behind the loads of
+  // later steps (every CU issues its prologue at the same moment).
   __device__ __forceinline__ void prologue_loads() {
     load_a(t0, kt_at(0), pro(ac, 0), pro(as, 0));
     load_a(t1, kt_at(1), pro(ac, 1), pro(as, 1));
     __builtin_amdgcn_sched_barrier(0);
+    load_w(w[0], kt_at(0), pro(bc, 0), pro(bs, 0));
+    __builtin_amdgcn_sched_barrier(0);
     prologue_a<0>();
     __builtin_amdgcn_sched_barrier(0);
-    prologue_w<0>();
+    prologue_w<1>();
     __builtin_amdgcn_sched_barrier(0);
   }
 
