@@ -81,29 +81,44 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_
 }
 
 // The tile map of a grouped GEMM with tiles of bm rows from the expert
-// totals and first rows of experts [e0, e1) of this thread: m-tile j of
-// expert e gets entry (tiles of experts before e) + j, the remaining entries
-// expert -1, and map[2 * max_mtiles] the number of used entries (the format
-// build_tile_map_kernel writes). Every thread of the workgroup calls it.
-__device__ __forceinline__ void route_tile_map(int32_t* __restrict__ map, int bm, int64_t max_mtiles, int e0, int e1,
-                                               const int* tot, const int* first_row, int* sh) {
+// totals tot[] and first rows first_row[] (LDS, all E experts; this thread
+// sums experts [e0, e1)): m-tile j of expert e gets entry (tiles of experts
+// before e) + j, the remaining entries expert -1, and map[2 * max_mtiles] the
+// number of used entries (the format build_tile_map_kernel writes). Each
+// thread writes entries tid, tid + 256, ..., finding an entry's expert by
+// binary search of the tile prefix tpre[] (LDS, E ints). Every thread of the
+// workgroup calls it.
+__device__ __forceinline__ void route_tile_map(int32_t* __restrict__ map, int bm, int64_t max_mtiles, int E, int e0,
+                                               int e1, const int* tot, const int* first_row, int* tpre, int* sh) {
   int cnt = 0;
   for (int e = e0; e < e1; ++e) cnt += (tot[e] + bm - 1) / bm;
   int used = 0;
-  int64_t acc = route_scan(cnt, sh, &used);
+  int acc = route_scan(cnt, sh, &used);
   for (int e = e0; e < e1; ++e) {
-    const int tiles = (tot[e] + bm - 1) / bm;
-    for (int j = 0; j < tiles && acc < max_mtiles; ++j, ++acc) {
-      map[2 * acc] = e;
-      map[2 * acc + 1] = first_row[e] + j * bm;
-    }
+    tpre[e] = acc;
+    acc += (tot[e] + bm - 1) / bm;
   }
+  __syncthreads();
   const int64_t n_used = used < max_mtiles ? used : max_mtiles;
-  for (int64_t i = n_used + threadIdx.x; i < max_mtiles; i += kRouteThreads) {
-    map[2 * i] = -1;
-    map[2 * i + 1] = 0;
+  for (int64_t i = threadIdx.x; i < max_mtiles; i += kRouteThreads) {
+    int e = -1, row = 0;
+    if (i < n_used) {
+      // the last expert whose tiles start at or before entry i (an expert
+      // with no tiles shares its start with the next one, so it is skipped)
+      int lo = 0, hi = E;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tpre[mid] <= i) lo = mid;
+        else hi = mid;
+      }
+      e = lo;
+      row = first_row[lo] + (int)(i - tpre[lo]) * bm;
+    }
+    map[2 * i] = e;
+    map[2 * i + 1] = row;
   }
   if (threadIdx.x == 0) map[2 * max_mtiles] = (int32_t)n_used;
+  __syncthreads();  // tpre is reused
 }
 
 // Rows of chunk g's entries (G chunks). Workgroup 0 writes offsets (and the
@@ -116,6 +131,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int3
                                                                       int32_t* __restrict__ pos, RouteMaps m) {
   __shared__ int base[kMaxExperts];   // first row of this chunk's entries of e
   __shared__ int first[kMaxExperts];  // expert totals, then the sorted place of e's first entry
+  __shared__ int offs[kMaxExperts];   // offsets[e]
+  __shared__ int tpre[kMaxExperts];   // tile maps: first entry of each expert
   __shared__ int buf[kRouteChunk];
   __shared__ int sh[4];
   const int tid = threadIdx.x, g = blockIdx.x;
@@ -141,14 +158,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int3
   for (int e = e0; e < e1; ++e) {
     const int c = first[e];
     if (g == 0) offsets[e] = acc;
+    offs[e] = acc;
     base[e] += acc;
     acc += c;
   }
   if (g == 0 && tid == 0) offsets[E] = routed;
-  if (g == 0) {  // base[e] is offsets[e] here (no earlier chunks)
+  // tile map i from workgroup i % G
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (m.map[i]) route_tile_map(m.map[i], m.bm[i], m.max_mtiles, e0, e1, first, base, sh);
+  for (int i = 0; i < 2; ++i) {
+    if (m.map[i] && g == i % G) {
+      __syncthreads();  // offs and the totals of every expert
+      route_tile_map(m.map[i], m.bm[i], m.max_mtiles, E, e0, e1, first, offs, tpre, sh);
+    }
   }
   // stable sort of the chunk by key (id; E for an id out of range, E + 1 past
   // the end), one key bit per pass; a key and the entry's place pack into one int
