@@ -435,3 +435,30 @@ def test_linear_grouped_bf16_output_ragged(dev, N):
     pw = binding.Packed(torch.from_numpy(np.stack([t[0] for t in tiles])).to(dev),
                         torch.from_numpy(np.stack([t[1] for t in tiles])).to(dev), N, K)
     _grouped_bf16_vs_f32(dev, x.to(dev), torch.from_numpy(off).to(dev), a, pw)
+
+
+@pytest.mark.parametrize("E", [4096, 4100])
+def test_linear_grouped_many_experts(dev, E):
+    """Thousands of experts, most empty or with a single row: the tile map is
+    written entry by entry from the experts' tile prefix (up to 4096 experts)
+    or by each expert's own thread beyond that."""
+    K, N = 64, 32
+    rng = np.random.default_rng(E)
+    counts = np.zeros(E, np.int64)
+    hot = rng.choice(E, 40, replace=False)
+    counts[hot] = rng.integers(1, 300, size=40)
+    counts[rng.choice(E, 200, replace=False)] += 1
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(off[-1])
+    log("grouped E=%d T=%d" % (E, T))
+    x = inputs.to_bf16(rng.standard_normal((T, K)).astype(np.float32))
+    a_o = (rng.random((E, K)) + 0.5).astype(np.float32)
+    wc_o = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    ws_o = rng.integers(118, 134, size=(E, N, K // 32), dtype=np.uint8)
+    tiles = [row_major_to_gemm_layout(wc_o[e], ws_o[e]) for e in range(E)]
+    pw = binding.Packed(torch.from_numpy(np.stack([t[0] for t in tiles])).to(dev),
+                        torch.from_numpy(np.stack([t[1] for t in tiles])).to(dev), N, K)
+    y = binding.linear_grouped(x.to(dev), torch.from_numpy(off).to(dev), torch.from_numpy(a_o).to(dev), 32, pw,
+                               out_dtype=torch.float32)
+    y_o = oracle.linear_grouped(bits(x), off, a_o, 32, wc_o, ws_o)
+    assert rel_l2(y.cpu().numpy(), y_o) <= REL_L2_TOL
