@@ -107,13 +107,16 @@ __global__ __launch_bounds__(256) void transform_kernel(const void* __restrict__
   }
 }
 
-// C[i][j] = sum over t (ascending) of A(t, i) * B(t, j) in fp64, one 64 x 64
-// output tile per workgroup, each thread 4 x 4 outputs, t staged 16 at a time
-// through LDS. Each term is added by one fused multiply-add, in t order, so
+// C[i][j] = sum over t (ascending) of A(t, i) * B(t, j) in fp64, one 128 x 128
+// output tile per workgroup, each thread 8 x 8 outputs (two fp64 LDS reads per
+// eight fused multiply-adds), t staged 32 at a time through LDS, the next
+// chunk loaded into registers while the current one is multiplied. Each term is added by one fused multiply-add, in t order, so
 // every output equals the plain sequential sum of fused steps. The two instances:
 //   Hessian: A = B = the fp32 transformed rows [R, K]:  H[j][k] = sum_r x~[r][j] x~[r][k];
 //   gradient: A = E^T (E [N, K] fp64), B = H:          G[n][j] = sum_k E[n][k] H[k][j].
-constexpr int kTile = 64, kChunk = 16;
+constexpr int kTile = 128, kChunk = 16;
+constexpr int kPer = kTile / 16;                // outputs per thread along each side
+constexpr int kStage = kChunk * kTile / 256;    // staged values per thread and matrix
 
 template <bool HESSIAN>
 __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt, const double* __restrict__ e,
@@ -123,53 +126,74 @@ __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt,
   __shared__ double bs[kChunk][kTile];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int64_t i0 = (int64_t)blockIdx.y * kTile, j0 = (int64_t)blockIdx.x * kTile;
-  double acc[4][4];
+  // this thread's staged values of a chunk: A then B, kStage each; loads run
+  // along the contiguous dimension (i of the rows x~, t of E, j of H)
+  double ra[kStage], rb[kStage];
+  auto load = [&](int64_t t0) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-  for (int64_t t0 = 0; t0 < len_t; t0 += kChunk) {
-    // stage 16 x 64 values of A and of B, 4 each per thread; loads run along
-    // the contiguous dimension (i of the rows x~, t of E, j of H)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kStage; ++q) {
       const int idx = tid + 256 * q;
       if constexpr (HESSIAN) {
-        const int tt = idx >> 6, col = idx & 63;
+        const int tt = idx / kTile, col = idx % kTile;
         const int64_t t = t0 + tt;
-        as[tt][col] = (t < len_t && i0 + col < rows_i) ? (double)xt[t * rows_i + i0 + col] : 0.0;
-        bs[tt][col] = (t < len_t && j0 + col < cols_j) ? (double)xt[t * cols_j + j0 + col] : 0.0;
+        ra[q] = (t < len_t && i0 + col < rows_i) ? (double)xt[t * rows_i + i0 + col] : 0.0;
+        rb[q] = (t < len_t && j0 + col < cols_j) ? (double)xt[t * cols_j + j0 + col] : 0.0;
       } else {
-        const int tt_a = idx & 15, col_a = idx >> 4;
+        const int tt_a = idx % kChunk, col_a = idx / kChunk;
         const int64_t ta = t0 + tt_a;
-        as[tt_a][col_a] = (ta < len_t && i0 + col_a < rows_i) ? e[(i0 + col_a) * len_t + ta] : 0.0;
-        const int tt_b = idx >> 6, col_b = idx & 63;
+        ra[q] = (ta < len_t && i0 + col_a < rows_i) ? e[(i0 + col_a) * len_t + ta] : 0.0;
+        const int tt_b = idx / kTile, col_b = idx % kTile;
         const int64_t tb = t0 + tt_b;
-        bs[tt_b][col_b] = (tb < len_t && j0 + col_b < cols_j) ? h[tb * cols_j + j0 + col_b] : 0.0;
+        rb[q] = (tb < len_t && j0 + col_b < cols_j) ? h[tb * cols_j + j0 + col_b] : 0.0;
       }
     }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int q = 0; q < kStage; ++q) {
+      const int idx = tid + 256 * q;
+      if constexpr (HESSIAN) {
+        as[idx / kTile][idx % kTile] = ra[q];
+      } else {
+        as[idx % kChunk][idx / kChunk] = ra[q];
+      }
+      bs[idx / kTile][idx % kTile] = rb[q];
+    }
+  };
+  // thread (ty, tx) owns rows i0 + ty + 16 a and columns j0 + tx + 16 b: the
+  // 16 threads of a row group read 16 consecutive doubles of each LDS row
+  double acc[kPer][kPer];
+#pragma unroll
+  for (int a = 0; a < kPer; ++a)
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) acc[a][b] = 0.0;
+  load(0);
+  for (int64_t t0 = 0; t0 < len_t; t0 += kChunk) {
+    store();
     __syncthreads();
+    // the next chunk's loads are in flight during this chunk's products
+    if (t0 + kChunk < len_t) load(t0 + kChunk);
     const int nt = (int)(len_t - t0 < kChunk ? len_t - t0 : kChunk);
     for (int tt = 0; tt < nt; ++tt) {
-      double av[4], bv[4];
+      double av[kPer], bv[kPer];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = as[tt][ty * 4 + a];
+      for (int a = 0; a < kPer; ++a) av[a] = as[tt][ty + 16 * a];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = bs[tt][tx * 4 + b];
+      for (int b = 0; b < kPer; ++b) bv[b] = bs[tt][tx + 16 * b];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < kPer; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fma(av[a], bv[b], acc[a][b]);
+        for (int b = 0; b < kPer; ++b) acc[a][b] = __builtin_fma(av[a], bv[b], acc[a][b]);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int64_t i = i0 + ty * 4 + a;
+  for (int a = 0; a < kPer; ++a) {
+    const int64_t i = i0 + ty + 16 * a;
     if (i >= rows_i) continue;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t j = j0 + tx * 4 + b;
+    for (int b = 0; b < kPer; ++b) {
+      const int64_t j = j0 + tx + 16 * b;
       if (j < cols_j) out[i * cols_j + j] = acc[a][b];
     }
   }
