@@ -79,7 +79,7 @@ LinearWs linear_ws(int64_t M, int64_t K, size_t extra_bytes) {
   return w;
 }
 
-// Flip-Refinement keeps a row's state in the registers of 1024 threads.
+// Flip-Refinement keeps a row's state in the registers of one workgroup (at most 1024 threads).
 constexpr int64_t kMaxRefineK = 32768;
 
 // The GEMM addresses each packed operand through a 32-bit buffer range.

@@ -204,49 +204,74 @@ __global__ void hdiag_kernel(const double* __restrict__ h, int64_t K, double* __
   if (k < K) d[k] = h[k * K + k];
 }
 
-// The greedy moves of one weight row per workgroup (1024 threads). Thread t
-// owns the element pairs p = t + 1024 i (elements 2p, 2p + 1, one code byte,
-// one scale) for i < P, holding g and the signed indices in registers.
-constexpr int kFlipThreads = 1024;
+// Exponent of the step from signed index m up to m + 1, per u = m + 7 in
+// 0 .. 13 as two bits holding exponent + 1: the E2M1 grid spacing is 2 between
+// magnitudes 4 and 6, 1 between 1 and 4 and 1/2 below 1. The step from m down
+// to m - 1 is minus the step from m - 1 up. Every step is a power of two, so
+// d = +-2^(e + scale - 127) is exactly the difference of the two dequantized
+// values.
+constexpr uint32_t kUpExp = (2u << 0) | (1u << 2) | (1u << 4) | (1u << 22) | (1u << 24) | (2u << 26);
+__device__ __forceinline__ int up_exp(uint32_t u) { return (int)((kUpExp >> (2 * (u & 15u))) & 3u) - 1; }
 
+// A candidate move: the change D of the objective, the element k, and the
+// step d as (exponent + 512) * 2 + 1 for an upward move, + 0 for a downward one.
 struct Cand {
   double D;
-  int k, dir;
+  int k, step;
 };
+// Candidates order by D, then by k. A thread scans its elements in ascending k,
+// the downward move first, and keeps only a strictly lower D, so its winner is
+// the first of its equals in index order; no two threads hold the same k.
 __device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
-  return a.D < b.D || (a.D == b.D && (a.k < b.k || (a.k == b.k && a.dir < b.dir)));
+  return a.D < b.D || (a.D == b.D && a.k < b.k);
 }
 __device__ __forceinline__ Cand shfl_xor_cand(const Cand& c, int m) {
   Cand o;
   o.D = __shfl_xor(c.D, m);
   o.k = __shfl_xor(c.k, m);
-  o.dir = __shfl_xor(c.dir, m);
+  o.step = __shfl_xor(c.step, m);
   return o;
 }
+__device__ __forceinline__ double step_value(int step) {
+  const double m = ldexp(1.0, (step >> 1) - 512);
+  return (step & 1) ? m : -m;
+}
 
-template <int P>
-__global__ __launch_bounds__(kFlipThreads) void flip_kernel(const double* __restrict__ G, const double* __restrict__ H,
-                                                           const double* __restrict__ hdiag, int64_t N, int64_t K,
-                                                           int max_flips, uint8_t* __restrict__ codes,
-                                                           const uint8_t* __restrict__ scales,
-                                                           int32_t* __restrict__ flips) {
-  __shared__ Cand slot[2][kFlipThreads / 64];
-  __shared__ double dsh[2];
+// The greedy moves of one weight row per workgroup of T threads. Thread t owns
+// the element pairs p = t + T i (elements 2p, 2p + 1, one code byte, one scale)
+// for i < P and holds their g, H[k][k] (HD_REG) and signed indices in
+// registers. Per move: the scan of every element's two moves (no branches), a
+// wave argmin by shuffles, one barrier for the per-wave winners, the argmin of
+// those in every wave, the owner's index update and the g update from one row
+// of H.
+template <int P, int T, bool HD_REG>
+__global__ __launch_bounds__(T) void flip_kernel(const double* __restrict__ G, const double* __restrict__ H,
+                                                 const double* __restrict__ hdiag, int64_t N, int64_t K,
+                                                 int max_flips, uint8_t* __restrict__ codes,
+                                                 const uint8_t* __restrict__ scales, int32_t* __restrict__ flips) {
+  constexpr int kWaves = T / 64;
+  __shared__ Cand slot[2][kWaves];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t n = blockIdx.x;
   const int64_t kpad = pad_k(K);
-  // per pair: g of both elements, and one state word: bits 0-3 / 4-7 the
-  // current signed indices + 7, bits 8-11 / 12-15 the original ones + 7,
-  // bits 16-23 the scale byte
-  double g[P][2];
+  const int Ki = (int)K;  // K <= 32768: element indices fit 32 bits
+  // per pair: g and H[k][k] of both elements, and one state word: bits 0-3 /
+  // 4-7 the current signed indices + 7, bits 8-11 / 12-15 the original ones
+  // + 7, bits 16-23 the scale byte. Elements past K get H[k][k] = +inf, so
+  // their moves never lower the objective.
+  double g[P][2], hd[HD_REG ? P : 1][2];
   uint32_t st[P];
 #pragma unroll
   for (int i = 0; i < P; ++i) {
-    const int64_t k = 2 * ((int64_t)tid + (int64_t)kFlipThreads * i);
-    if (k < K) {
+    const int k = 2 * (tid + T * i);
+    double h0 = __builtin_inf(), h1 = __builtin_inf();
+    if (k < Ki) {
       const double2 gv = *reinterpret_cast<const double2*>(G + n * K + k);
       g[i][0] = gv.x;
       g[i][1] = gv.y;
+      const double2 hk = *reinterpret_cast<const double2*>(hdiag + k);
+      h0 = hk.x;
+      h1 = hk.y;
       const uint32_t byte = codes[tiled_code_offset(n, k, kpad)];
       const uint32_t lo = (uint32_t)(code_index(byte & 0xF) + 7), hi = (uint32_t)(code_index(byte >> 4) + 7);
       st[i] = lo | (hi << 4) | (lo << 8) | (hi << 12) | ((uint32_t)scales[tiled_scale_offset(n, k, kpad)] << 16);
@@ -254,29 +279,42 @@ __global__ __launch_bounds__(kFlipThreads) void flip_kernel(const double* __rest
       g[i][0] = g[i][1] = 0.0;
       st[i] = 7u | (7u << 4) | (7u << 8) | (7u << 12);
     }
+    if constexpr (HD_REG) {
+      hd[i][0] = h0;
+      hd[i][1] = h1;
+    }
   }
   int moves = 0;
   for (int par = 0; moves < max_flips; par ^= 1) {
-    Cand best{0.0, (int)K, 0};
+    Cand best{0.0, Ki, 0};
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      const int64_t k = 2 * ((int64_t)tid + (int64_t)kFlipThreads * i);
-      if (k >= K) continue;
-      const double2 hk = *reinterpret_cast<const double2*>(hdiag + k);
-      const double hkk[2] = {hk.x, hk.y};
-      const int sc = (int)((st[i] >> 16) & 0xFF);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int mc = (int)((st[i] >> (4 * s)) & 0xF) - 7;
-#pragma unroll
-        for (int dir = -1; dir <= 1; dir += 2) {
-          const int mn = mc + dir;
-          if (mn < -7 || mn > 7) continue;
-          const double d = ldexp(index_value(mn) - index_value(mc), sc - 127);
-          const double D = d * d * hkk[s] - 2.0 * d * g[i][s];
-          if (D < best.D) best = Cand{D, (int)(k + s), dir};
+      const int k = 2 * (tid + T * i);
+      double hkk[2];
+      if constexpr (HD_REG) {
+        hkk[0] = hd[i][0];
+        hkk[1] = hd[i][1];
+      } else {
+        hkk[0] = hkk[1] = __builtin_inf();
+        if (k < Ki) {
+          const double2 hk = *reinterpret_cast<const double2*>(hdiag + k);
+          hkk[0] = hk.x;
+          hkk[1] = hk.y;
         }
       }
+      const int sc = (int)((st[i] >> 16) & 0xFF) - 127;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint32_t u = (st[i] >> (4 * s)) & 0xF;
+        const int edn = up_exp(u - 1) + sc, eup = up_exp(u) + sc;
+        const double ddn = -ldexp(1.0, edn), dup = ldexp(1.0, eup);
+        const double Ddn = ddn * ddn * hkk[s] - 2.0 * ddn * g[i][s];
+        const double Dup = dup * dup * hkk[s] - 2.0 * dup * g[i][s];
+        if (u > 0 && Ddn < best.D) best = Cand{Ddn, k + s, (edn + 512) << 1};
+        if (u < 14 && Dup < best.D) best = Cand{Dup, k + s, ((eup + 512) << 1) | 1};
+      }
+      if constexpr (!HD_REG)
+        if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int msk = 32; msk >= 1; msk >>= 1) {
@@ -285,41 +323,46 @@ __global__ __launch_bounds__(kFlipThreads) void flip_kernel(const double* __rest
     }
     if (lane == 0) slot[par][wave] = best;
     __syncthreads();
-    best = slot[par][0];
+    // every aligned group of kWaves lanes reduces the per-wave winners
+    best = slot[par][lane % kWaves];
 #pragma unroll
-    for (int w = 1; w < kFlipThreads / 64; ++w)
-      if (better(slot[par][w], best)) best = slot[par][w];
-    if (best.k >= K) break;  // no move lowers the objective (uniform)
-    // the owner of element best.k applies the move and publishes its step
-    const int64_t pidx = best.k >> 1;
-    if (pidx % kFlipThreads == tid) {
-      const int i = (int)(pidx / kFlipThreads), s = best.k & 1;
+    for (int msk = kWaves / 2; msk >= 1; msk >>= 1) {
+      const Cand o = shfl_xor_cand(best, msk);
+      if (better(o, best)) best = o;
+    }
+    const int bk = __builtin_amdgcn_readfirstlane(best.k);
+    const int bstep = __builtin_amdgcn_readfirstlane(best.step);
+    if (bk >= Ki) break;  // no move lowers the objective
+    // the owner of element bk applies the move to its signed index
+    const int pidx = bk >> 1;
+    if (pidx % T == tid) {
+      const int i = pidx / T;
+      const uint32_t delta = 1u << (4 * (bk & 1));
 #pragma unroll
       for (int ii = 0; ii < P; ++ii)
-        if (ii == i) {
-          const int mc = (int)((st[ii] >> (4 * s)) & 0xF) - 7;
-          const int mn = mc + best.dir;
-          dsh[par] = ldexp(index_value(mn) - index_value(mc), (int)((st[ii] >> 16) & 0xFF) - 127);
-          st[ii] = (st[ii] & ~(0xFu << (4 * s))) | ((uint32_t)(mn + 7) << (4 * s));
-        }
+        if (ii == i) st[ii] = (bstep & 1) ? st[ii] + delta : st[ii] - delta;
     }
-    __syncthreads();
-    const double d = dsh[par];
-    const double* hr = H + (int64_t)best.k * K;
+    const double d = step_value(bstep);
+    const double* hr = H + (int64_t)bk * K;
+    // without H[k][k] in registers the row (like H[k][k] in the scan) is read
+    // in groups of 4 pairs, which bounds the registers its loads hold
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      const int64_t k = 2 * ((int64_t)tid + (int64_t)kFlipThreads * i);
-      if (k >= K) continue;
-      const double2 hv = *reinterpret_cast<const double2*>(hr + k);
-      g[i][0] = g[i][0] - d * hv.x;
-      g[i][1] = g[i][1] - d * hv.y;
+      const int k = 2 * (tid + T * i);
+      if (k < Ki) {
+        const double2 hv = *reinterpret_cast<const double2*>(hr + k);
+        g[i][0] = g[i][0] - d * hv.x;
+        g[i][1] = g[i][1] - d * hv.y;
+      }
+      if constexpr (!HD_REG)
+        if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
     ++moves;
   }
   // moved elements take the canonical code of their index; the rest keep their bits
 #pragma unroll
   for (int i = 0; i < P; ++i) {
-    const int64_t k = 2 * ((int64_t)tid + (int64_t)kFlipThreads * i);
+    const int k = 2 * (tid + T * i);
     const uint32_t cur = st[i] & 0xFF, orig = (st[i] >> 8) & 0xFF;
     if (k >= K || cur == orig) continue;
     uint8_t* bp = codes + tiled_code_offset(n, k, kpad);
@@ -329,6 +372,13 @@ __global__ __launch_bounds__(kFlipThreads) void flip_kernel(const double* __rest
     *bp = (uint8_t)byte;
   }
   if (tid == 0 && flips) flips[n] = moves;
+}
+
+template <int P, int T>
+void launch_flip(int64_t N, int64_t K, int max_flips, const double* G, const double* H, const double* hdiag,
+                 uint8_t* codes, const uint8_t* scales, int32_t* flips, hipStream_t stream) {
+  hipLaunchKernelGGL((flip_kernel<P, T, (P <= 8)>), dim3((unsigned)N), dim3(T), 0, stream, G, H, hdiag, N, K,
+                     max_flips, codes, scales, flips);
 }
 
 template <bool F32_IN, bool OUT_E>
@@ -371,13 +421,21 @@ hipError_t launch_flip_refine(const void* W, bool w_f32, int64_t N, int64_t K, i
   hipLaunchKernelGGL(hdiag_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream, H, K, hdiag);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t pairs = (K / 2 + kFlipThreads - 1) / kFlipThreads;
-  const dim3 fg((unsigned)N), fb(kFlipThreads);
-  if (pairs <= 1) hipLaunchKernelGGL(flip_kernel<1>, fg, fb, 0, stream, G, H, hdiag, N, K, max_flips, codes, scales, flips);
-  else if (pairs <= 2) hipLaunchKernelGGL(flip_kernel<2>, fg, fb, 0, stream, G, H, hdiag, N, K, max_flips, codes, scales, flips);
-  else if (pairs <= 4) hipLaunchKernelGGL(flip_kernel<4>, fg, fb, 0, stream, G, H, hdiag, N, K, max_flips, codes, scales, flips);
-  else if (pairs <= 8) hipLaunchKernelGGL(flip_kernel<8>, fg, fb, 0, stream, G, H, hdiag, N, K, max_flips, codes, scales, flips);
-  else hipLaunchKernelGGL(flip_kernel<16>, fg, fb, 0, stream, G, H, hdiag, N, K, max_flips, codes, scales, flips);
+  // rows of up to 4096 elements: 256 threads (four rows a compute unit at a
+  // time, each thread 8 pairs); longer rows: 1024 threads
+  const int64_t half = K / 2;
+  if (half <= 256 * 8) {
+    if (half <= 256) launch_flip<1, 256>(N, K, max_flips, G, H, hdiag, codes, scales, flips, stream);
+    else if (half <= 512) launch_flip<2, 256>(N, K, max_flips, G, H, hdiag, codes, scales, flips, stream);
+    else if (half <= 1024) launch_flip<4, 256>(N, K, max_flips, G, H, hdiag, codes, scales, flips, stream);
+    else launch_flip<8, 256>(N, K, max_flips, G, H, hdiag, codes, scales, flips, stream);
+  } else if (half <= 1024 * 4) {
+    launch_flip<4, 1024>(N, K, max_flips, G, H, hdiag, codes, scales, flips, stream);
+  } else if (half <= 1024 * 8) {
+    launch_flip<8, 1024>(N, K, max_flips, G, H, hdiag, codes, scales, flips, stream);
+  } else {
+    launch_flip<16, 1024>(N, K, max_flips, G, H, hdiag, codes, scales, flips, stream);
+  }
   return hipGetLastError();
 }
 
