@@ -212,6 +212,10 @@ __global__ void hdiag_kernel(const double* __restrict__ h, int64_t K, double* __
 // values.
 constexpr uint32_t kUpExp = (2u << 0) | (1u << 2) | (1u << 4) | (1u << 22) | (1u << 24) | (2u << 26);
 __device__ __forceinline__ int up_exp(uint32_t u) { return (int)((kUpExp >> (2 * (u & 15u))) & 3u) - 1; }
+// The step exponents of state u, each + 1: bits 0-1 upward, bits 2-3 downward.
+__device__ __forceinline__ uint32_t step_bits(uint32_t u) {
+  return (uint32_t)(up_exp(u) + 1) | ((uint32_t)(up_exp(u - 1) + 1) << 2);
+}
 
 // A candidate move: the change D of the objective, the element k, and the
 // step d as (exponent + 512) * 2 + 1 for an upward move, + 0 for a downward one.
@@ -257,8 +261,9 @@ __global__ __launch_bounds__(T) void flip_kernel(const double* __restrict__ G, c
   const int Ki = (int)K;  // K <= 32768: element indices fit 32 bits
   // per pair: g and H[k][k] of both elements, and one state word: bits 0-3 /
   // 4-7 the current signed indices + 7, bits 8-11 / 12-15 the original ones
-  // + 7, bits 16-23 the scale byte. Elements past K get H[k][k] = +inf, so
-  // their moves never lower the objective.
+  // + 7, bits 16-23 the scale byte, bits 24-27 / 28-31 the step bits of the
+  // current indices. Elements past K get H[k][k] = +inf, so their moves never
+  // lower the objective.
   double g[P][2], hd[HD_REG ? P : 1][2];
   uint32_t st[P];
 #pragma unroll
@@ -274,10 +279,11 @@ __global__ __launch_bounds__(T) void flip_kernel(const double* __restrict__ G, c
       h1 = hk.y;
       const uint32_t byte = codes[tiled_code_offset(n, k, kpad)];
       const uint32_t lo = (uint32_t)(code_index(byte & 0xF) + 7), hi = (uint32_t)(code_index(byte >> 4) + 7);
-      st[i] = lo | (hi << 4) | (lo << 8) | (hi << 12) | ((uint32_t)scales[tiled_scale_offset(n, k, kpad)] << 16);
+      st[i] = lo | (hi << 4) | (lo << 8) | (hi << 12) | ((uint32_t)scales[tiled_scale_offset(n, k, kpad)] << 16) |
+              (step_bits(lo) << 24) | (step_bits(hi) << 28);
     } else {
       g[i][0] = g[i][1] = 0.0;
-      st[i] = 7u | (7u << 4) | (7u << 8) | (7u << 12);
+      st[i] = 7u | (7u << 4) | (7u << 8) | (7u << 12) | (step_bits(7) << 24) | (step_bits(7) << 28);
     }
     if constexpr (HD_REG) {
       hd[i][0] = h0;
@@ -286,7 +292,10 @@ __global__ __launch_bounds__(T) void flip_kernel(const double* __restrict__ G, c
   }
   int moves = 0;
   for (int par = 0; moves < max_flips; par ^= 1) {
-    Cand best{0.0, Ki, 0};
+    // d = -2^ed (down) or 2^eu (up); (d d) H[k][k] and (2 d) g are products by
+    // powers of two, each one rounding, so ldexp gives the same values
+    double bD = 0.0;
+    int bc = -1;  // 4 i + 2 s + (1 if upward) of the thread's best move
 #pragma unroll
     for (int i = 0; i < P; ++i) {
       const int k = 2 * (tid + T * i);
@@ -295,26 +304,41 @@ __global__ __launch_bounds__(T) void flip_kernel(const double* __restrict__ G, c
         hkk[0] = hd[i][0];
         hkk[1] = hd[i][1];
       } else {
-        hkk[0] = hkk[1] = __builtin_inf();
-        if (k < Ki) {
-          const double2 hk = *reinterpret_cast<const double2*>(hdiag + k);
-          hkk[0] = hk.x;
-          hkk[1] = hk.y;
-        }
+        const double2 hk = *reinterpret_cast<const double2*>(hdiag + (k < Ki ? k : 0));
+        hkk[0] = k < Ki ? hk.x : __builtin_inf();
+        hkk[1] = k < Ki ? hk.y : __builtin_inf();
       }
-      const int sc = (int)((st[i] >> 16) & 0xFF) - 127;
+      const int sc1 = (int)((st[i] >> 16) & 0xFF) - 128;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const uint32_t u = (st[i] >> (4 * s)) & 0xF;
-        const int edn = up_exp(u - 1) + sc, eup = up_exp(u) + sc;
-        const double ddn = -ldexp(1.0, edn), dup = ldexp(1.0, eup);
-        const double Ddn = ddn * ddn * hkk[s] - 2.0 * ddn * g[i][s];
-        const double Dup = dup * dup * hkk[s] - 2.0 * dup * g[i][s];
-        if (u > 0 && Ddn < best.D) best = Cand{Ddn, k + s, (edn + 512) << 1};
-        if (u < 14 && Dup < best.D) best = Cand{Dup, k + s, ((eup + 512) << 1) | 1};
+        const uint32_t sb = st[i] >> (24 + 4 * s);
+        const int eu = (int)(sb & 3u) + sc1, ed = (int)((sb >> 2) & 3u) + sc1;
+        const double Ddn = ldexp(hkk[s], 2 * ed) + ldexp(g[i][s], ed + 1);
+        const double Dup = ldexp(hkk[s], 2 * eu) - ldexp(g[i][s], eu + 1);
+        if (u > 0 && Ddn < bD) {
+          bD = Ddn;
+          bc = 4 * i + 2 * s;
+        }
+        if (u < 14 && Dup < bD) {
+          bD = Dup;
+          bc = 4 * i + 2 * s + 1;
+        }
       }
       if constexpr (!HD_REG)
         if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    Cand best{bD, Ki, 0};
+    if (bc >= 0) {
+      const int bi = bc >> 2, bs = (bc >> 1) & 1, bup = bc & 1;
+      uint32_t w = st[0];
+#pragma unroll
+      for (int i = 1; i < P; ++i)
+        if (bi == i) w = st[i];
+      const uint32_t sb = w >> (24 + 4 * bs);
+      const int e = (int)(bup ? (sb & 3u) : ((sb >> 2) & 3u)) + (int)((w >> 16) & 0xFF) - 128;
+      best.k = 2 * (tid + T * bi) + bs;
+      best.step = ((e + 512) << 1) | bup;
     }
 #pragma unroll
     for (int msk = 32; msk >= 1; msk >>= 1) {
@@ -336,26 +360,36 @@ __global__ __launch_bounds__(T) void flip_kernel(const double* __restrict__ G, c
     // the owner of element bk applies the move to its signed index
     const int pidx = bk >> 1;
     if (pidx % T == tid) {
-      const int i = pidx / T;
-      const uint32_t delta = 1u << (4 * (bk & 1));
+      const int i = pidx / T, sh = 4 * (bk & 1);
 #pragma unroll
       for (int ii = 0; ii < P; ++ii)
-        if (ii == i) st[ii] = (bstep & 1) ? st[ii] + delta : st[ii] - delta;
+        if (ii == i) {
+          const uint32_t u = ((st[ii] >> sh) & 0xFu) + ((bstep & 1) ? 1u : 0xFFFFFFFFu);
+          st[ii] = (st[ii] & ~((0xFu << sh) | (0xFu << (24 + sh)))) | ((u & 0xFu) << sh) | (step_bits(u) << (24 + sh));
+        }
     }
     const double d = step_value(bstep);
     const double* hr = H + (int64_t)bk * K;
-    // without H[k][k] in registers the row (like H[k][k] in the scan) is read
-    // in groups of 4 pairs, which bounds the registers its loads hold
+    // the row's loads are issued together, without branches (elements past K
+    // read element 0; their g never matters), before any of them is used; with
+    // more than 7 pairs per thread of 1024 the row (like H[k][k] in the scan
+    // without HD_REG) is read in groups of 4 pairs, which bounds the registers
+    // its loads hold
+    constexpr int kGroup = (HD_REG && P * T <= 7 * 1024) ? P : 4;
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const int k = 2 * (tid + T * i);
-      if (k < Ki) {
-        const double2 hv = *reinterpret_cast<const double2*>(hr + k);
-        g[i][0] = g[i][0] - d * hv.x;
-        g[i][1] = g[i][1] - d * hv.y;
+    for (int i0 = 0; i0 < P; i0 += kGroup) {
+      double2 hv[kGroup];
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        const int k = 2 * (tid + T * (i0 + j));
+        hv[j] = *reinterpret_cast<const double2*>(hr + (k < Ki ? k : 0));
       }
-      if constexpr (!HD_REG)
-        if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        g[i0 + j][0] = g[i0 + j][0] - d * hv[j].x;
+        g[i0 + j][1] = g[i0 + j][1] - d * hv[j].y;
+      }
     }
     ++moves;
   }
@@ -431,6 +465,10 @@ hipError_t launch_flip_refine(const void* W, bool w_f32, int64_t N, int64_t K, i
     else launch_flip<8, 256>(N, K, max_flips, G, H, hdiag, codes, scales, flips, stream);
   } else if (half <= 1024 * 4) {
     launch_flip<4, 1024>(N, K, max_flips, G, H, hdiag, codes, scales, flips, stream);
+  } else if (half <= 1024 * 6) {
+    launch_flip<6, 1024>(N, K, max_flips, G, H, hdiag, codes, scales, flips, stream);
+  } else if (half <= 1024 * 7) {
+    launch_flip<7, 1024>(N, K, max_flips, G, H, hdiag, codes, scales, flips, stream);
   } else if (half <= 1024 * 8) {
     launch_flip<8, 1024>(N, K, max_flips, G, H, hdiag, codes, scales, flips, stream);
   } else {

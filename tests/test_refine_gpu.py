@@ -94,6 +94,21 @@ def test_flip_refine_wide_rows(dev):
     assert flips.sum() > 0
 
 
+@pytest.mark.parametrize("K", [3072, 6144, 12288, 14336, 16384])
+def test_flip_refine_row_layouts(dev, K):
+    """Row lengths that take each workgroup layout of the move kernel: 256
+    threads with the last pairs past K (3072), 1024 threads with 3, 6, 7 and 8
+    element pairs per thread (6144 ragged, 12288, 14336, 16384). H is the fp64
+    Gram of random rows computed here in numpy."""
+    N = 2
+    log("flip_refine row layout K=%d" % K)
+    rng = np.random.default_rng(K)
+    xt = rng.standard_normal((12, K))
+    H = xt.T @ xt
+    flips = _refine_case(dev, N, K, 32, 24, seed=K, H_np=H)
+    assert flips.sum() > 0
+
+
 def test_flip_refine_prefill_layer_sampled(dev):
     """A prefill 8B-shaped layer (4096 x 4096, b = 32) refined whole on the GPU;
     the oracle refines a sample of rows (rows are independent)."""
