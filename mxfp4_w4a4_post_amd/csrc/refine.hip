@@ -125,7 +125,22 @@ __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt,
   __shared__ double as[kChunk][kTile + 1];  // padded: the gradient's A is written along t
   __shared__ double bs[kChunk][kTile];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int64_t i0 = (int64_t)blockIdx.y * kTile, j0 = (int64_t)blockIdx.x * kTile;
+  // the Hessian is symmetric (x~[r][j] x~[r][k] and x~[r][k] x~[r][j] are the
+  // same product, summed in the same order), so its launch covers only the
+  // tiles with row tile <= column tile, one per workgroup of a 1-D grid, and
+  // writes each off-diagonal tile twice
+  int64_t i0, j0;
+  if constexpr (HESSIAN) {
+    const int64_t L = blockIdx.x;
+    int64_t c = (int64_t)((sqrt(8.0 * (double)L + 1.0) - 1.0) * 0.5);
+    while (c * (c + 1) / 2 > L) --c;
+    while ((c + 1) * (c + 2) / 2 <= L) ++c;
+    i0 = (L - c * (c + 1) / 2) * kTile;
+    j0 = c * kTile;
+  } else {
+    i0 = (int64_t)blockIdx.y * kTile;
+    j0 = (int64_t)blockIdx.x * kTile;
+  }
   // this thread's staged values of a chunk: A then B, kStage each; loads run
   // along the contiguous dimension (i of the rows x~, t of E, j of H)
   double ra[kStage], rb[kStage];
@@ -195,6 +210,18 @@ __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt,
     for (int b = 0; b < kPer; ++b) {
       const int64_t j = j0 + tx + 16 * b;
       if (j < cols_j) out[i * cols_j + j] = acc[a][b];
+    }
+  }
+  if (HESSIAN && i0 != j0) {
+#pragma unroll
+    for (int a = 0; a < kPer; ++a) {
+      const int64_t i = i0 + ty + 16 * a;
+      if (i >= rows_i) continue;
+#pragma unroll
+      for (int b = 0; b < kPer; ++b) {
+        const int64_t j = j0 + tx + 16 * b;
+        if (j < cols_j) out[j * rows_i + i] = acc[a][b];
+      }
     }
   }
 }
@@ -439,8 +466,9 @@ hipError_t launch_hessian(const void* xcal, int64_t R, int64_t K, int64_t ldx, c
                           double* H, hipStream_t stream) {
   hipError_t e = launch_transform<false, false>(xcal, R, K, ldx, a, b, nullptr, nullptr, xt, nullptr, stream);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((K + kTile - 1) / kTile), (unsigned)((K + kTile - 1) / kTile));
-  hipLaunchKernelGGL((gram_kernel<true>), grid, dim3(256), 0, stream, xt, nullptr, nullptr, K, K, R, H);
+  const int64_t tiles = (K + kTile - 1) / kTile;
+  hipLaunchKernelGGL((gram_kernel<true>), dim3((unsigned)(tiles * (tiles + 1) / 2)), dim3(256), 0, stream, xt,
+                     nullptr, nullptr, K, K, R, H);
   return hipGetLastError();
 }
 
