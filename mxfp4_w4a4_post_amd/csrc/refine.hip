@@ -109,9 +109,10 @@ __global__ __launch_bounds__(256) void transform_kernel(const void* __restrict__
 
 // C[i][j] = sum over t (ascending) of A(t, i) * B(t, j) in fp64, one 128 x 128
 // output tile per workgroup, each thread 8 x 8 outputs (two fp64 LDS reads per
-// eight fused multiply-adds), t staged 32 at a time through LDS, the next
-// chunk loaded into registers while the current one is multiplied. Each term is added by one fused multiply-add, in t order, so
-// every output equals the plain sequential sum of fused steps. The two instances:
+// eight fused multiply-adds), t staged 16 at a time through LDS, the next
+// chunk loaded into registers while the current one is multiplied. Each term
+// is added by one fused multiply-add, in t order, so every output equals the
+// plain sequential sum of fused steps. The two instances:
 //   Hessian: A = B = the fp32 transformed rows [R, K]:  H[j][k] = sum_r x~[r][j] x~[r][k];
 //   gradient: A = E^T (E [N, K] fp64), B = H:          G[n][j] = sum_k E[n][k] H[k][j].
 constexpr int kTile = 128, kChunk = 16;
@@ -122,8 +123,11 @@ template <bool HESSIAN>
 __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt, const double* __restrict__ e,
                                                    const double* __restrict__ h, int64_t rows_i, int64_t cols_j,
                                                    int64_t len_t, double* __restrict__ out) {
-  __shared__ double as[kChunk][kTile + 1];  // padded: the gradient's A is written along t
-  __shared__ double bs[kChunk][kTile];
+  // two buffers: chunk c is stored into buffer c % 2 while other waves may
+  // still multiply chunk c - 1 out of the other one; the barrier after the
+  // store then also orders the next reuse, so one barrier per chunk suffices
+  __shared__ double as[2][kChunk][kTile + 1];  // padded: the gradient's A is written along t
+  __shared__ double bs[2][kChunk][kTile];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   // the Hessian is symmetric (x~[r][j] x~[r][k] and x~[r][k] x~[r][j] are the
   // same product, summed in the same order), so its launch covers only the
@@ -163,16 +167,16 @@ __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt,
       }
     }
   };
-  auto store = [&]() {
+  auto store = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < kStage; ++q) {
       const int idx = tid + 256 * q;
       if constexpr (HESSIAN) {
-        as[idx / kTile][idx % kTile] = ra[q];
+        as[buf][idx / kTile][idx % kTile] = ra[q];
       } else {
-        as[idx % kChunk][idx / kChunk] = ra[q];
+        as[buf][idx % kChunk][idx / kChunk] = ra[q];
       }
-      bs[idx / kTile][idx % kTile] = rb[q];
+      bs[buf][idx / kTile][idx % kTile] = rb[q];
     }
   };
   // thread (ty, tx) owns rows i0 + ty + 16 a and columns j0 + tx + 16 b: the
@@ -183,8 +187,9 @@ __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt,
 #pragma unroll
     for (int b = 0; b < kPer; ++b) acc[a][b] = 0.0;
   load(0);
-  for (int64_t t0 = 0; t0 < len_t; t0 += kChunk) {
-    store();
+  int buf = 0;
+  for (int64_t t0 = 0; t0 < len_t; t0 += kChunk, buf ^= 1) {
+    store(buf);
     __syncthreads();
     // the next chunk's loads are in flight during this chunk's products
     if (t0 + kChunk < len_t) load(t0 + kChunk);
@@ -192,15 +197,14 @@ __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt,
     for (int tt = 0; tt < nt; ++tt) {
       double av[kPer], bv[kPer];
 #pragma unroll
-      for (int a = 0; a < kPer; ++a) av[a] = as[tt][ty + 16 * a];
+      for (int a = 0; a < kPer; ++a) av[a] = as[buf][tt][ty + 16 * a];
 #pragma unroll
-      for (int b = 0; b < kPer; ++b) bv[b] = bs[tt][tx + 16 * b];
+      for (int b = 0; b < kPer; ++b) bv[b] = bs[buf][tt][tx + 16 * b];
 #pragma unroll
       for (int a = 0; a < kPer; ++a)
 #pragma unroll
         for (int b = 0; b < kPer; ++b) acc[a][b] = __builtin_fma(av[a], bv[b], acc[a][b]);
     }
-    __syncthreads();
   }
 #pragma unroll
   for (int a = 0; a < kPer; ++a) {
