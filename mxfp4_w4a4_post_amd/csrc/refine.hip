@@ -108,16 +108,20 @@ __global__ __launch_bounds__(256) void transform_kernel(const void* __restrict__
 }
 
 // C[i][j] = sum over t (ascending) of A(t, i) * B(t, j) in fp64, one 128 x 128
-// output tile per workgroup, each thread 8 x 8 outputs (two fp64 LDS reads per
-// eight fused multiply-adds), t staged 16 at a time through LDS, the next
-// chunk loaded into registers while the current one is multiplied. Each term
-// is added by one fused multiply-add, in t order, so every output equals the
-// plain sequential sum of fused steps. The two instances:
+// output tile per workgroup, on the fp64 matrix cores: each wave owns a 64 x 64
+// quarter as 4 x 4 blocks of v_mfma_f64_16x16x4f64, which adds four products
+// per output as fused multiply-adds in k order (checked bit for bit against
+// the sequential chain, subnormals, signed zeros, overflow and NaN included),
+// so chaining it over ascending t gives every output exactly the plain
+// sequential sum of fused steps. t is staged 16 at a time through LDS (two
+// buffers), the next chunk loaded into registers while the current one is
+// multiplied; t past the end reads zeros, which leave a sum started at +0
+// unchanged (it can never be -0). The two instances:
 //   Hessian: A = B = the fp32 transformed rows [R, K]:  H[j][k] = sum_r x~[r][j] x~[r][k];
 //   gradient: A = E^T (E [N, K] fp64), B = H:          G[n][j] = sum_k E[n][k] H[k][j].
 constexpr int kTile = 128, kChunk = 16;
-constexpr int kPer = kTile / 16;                // outputs per thread along each side
 constexpr int kStage = kChunk * kTile / 256;    // staged values per thread and matrix
+typedef double v4d __attribute__((ext_vector_type(4)));
 
 template <bool HESSIAN>
 __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt, const double* __restrict__ e,
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt,
   // store then also orders the next reuse, so one barrier per chunk suffices
   __shared__ double as[2][kChunk][kTile + 1];  // padded: the gradient's A is written along t
   __shared__ double bs[2][kChunk][kTile];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tid = threadIdx.x;
   // the Hessian is symmetric (x~[r][j] x~[r][k] and x~[r][k] x~[r][j] are the
   // same product, summed in the same order), so its launch covers only the
   // tiles with row tile <= column tile, one per workgroup of a 1-D grid, and
@@ -179,13 +183,18 @@ __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt,
       bs[buf][idx / kTile][idx % kTile] = rb[q];
     }
   };
-  // thread (ty, tx) owns rows i0 + ty + 16 a and columns j0 + tx + 16 b: the
-  // 16 threads of a row group read 16 consecutive doubles of each LDS row
-  double acc[kPer][kPer];
+  // wave w owns rows i0 + 64 (w / 2) + [0, 64) and columns j0 + 64 (w % 2) +
+  // [0, 64); block (mi, nj) is 16 x 16. Operand lane l holds row / column
+  // l % 16 of its block at t offset l / 16; output lane l holds rows
+  // 4 v + l / 16 (v = 0 .. 3) of column l % 16.
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wi = 64 * (wave >> 1), wj = 64 * (wave & 1);
+  const int lr = lane & 15, lk = lane >> 4;
+  v4d acc[4][4];
 #pragma unroll
-  for (int a = 0; a < kPer; ++a)
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int b = 0; b < kPer; ++b) acc[a][b] = 0.0;
+    for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = v4d{0.0, 0.0, 0.0, 0.0};
   load(0);
   int buf = 0;
   for (int64_t t0 = 0; t0 < len_t; t0 += kChunk, buf ^= 1) {
@@ -194,39 +203,44 @@ __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ xt,
     // the next chunk's loads are in flight during this chunk's products
     if (t0 + kChunk < len_t) load(t0 + kChunk);
     const int nt = (int)(len_t - t0 < kChunk ? len_t - t0 : kChunk);
-    for (int tt = 0; tt < nt; ++tt) {
-      double av[kPer], bv[kPer];
+    for (int s4 = 0; s4 < nt; s4 += 4) {
+      double af[4], bf[4];
 #pragma unroll
-      for (int a = 0; a < kPer; ++a) av[a] = as[buf][tt][ty + 16 * a];
+      for (int mi = 0; mi < 4; ++mi) af[mi] = as[buf][s4 + lk][wi + 16 * mi + lr];
 #pragma unroll
-      for (int b = 0; b < kPer; ++b) bv[b] = bs[buf][tt][tx + 16 * b];
+      for (int nj = 0; nj < 4; ++nj) bf[nj] = bs[buf][s4 + lk][wj + 16 * nj + lr];
 #pragma unroll
-      for (int a = 0; a < kPer; ++a)
+      for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int b = 0; b < kPer; ++b) acc[a][b] = __builtin_fma(av[a], bv[b], acc[a][b]);
+        for (int nj = 0; nj < 4; ++nj)
+          acc[mi][nj] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[mi], bf[nj], acc[mi][nj], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int a = 0; a < kPer; ++a) {
-    const int64_t i = i0 + ty + 16 * a;
-    if (i >= rows_i) continue;
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int b = 0; b < kPer; ++b) {
-      const int64_t j = j0 + tx + 16 * b;
-      if (j < cols_j) out[i * cols_j + j] = acc[a][b];
-    }
-  }
-  if (HESSIAN && i0 != j0) {
-#pragma unroll
-    for (int a = 0; a < kPer; ++a) {
-      const int64_t i = i0 + ty + 16 * a;
+    for (int v = 0; v < 4; ++v) {
+      const int64_t i = i0 + wi + 16 * mi + 4 * v + lk;
       if (i >= rows_i) continue;
 #pragma unroll
-      for (int b = 0; b < kPer; ++b) {
-        const int64_t j = j0 + tx + 16 * b;
-        if (j < cols_j) out[j * rows_i + i] = acc[a][b];
+      for (int nj = 0; nj < 4; ++nj) {
+        const int64_t j = j0 + wj + 16 * nj + lr;
+        if (j < cols_j) out[i * cols_j + j] = acc[mi][nj][v];
       }
     }
+  if (HESSIAN && i0 != j0) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t i = i0 + wi + 16 * mi + 4 * v + lk;
+        if (i >= rows_i) continue;
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj) {
+          const int64_t j = j0 + wj + 16 * nj + lr;
+          if (j < cols_j) out[j * rows_i + i] = acc[mi][nj][v];
+        }
+      }
   }
 }
 
