@@ -912,6 +912,42 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   else static_cast<float*>(y)[m * ldy + n] = s;
 }
 
+// The same sums for 4 consecutive outputs of a row per thread (N % 4 == 0,
+// y and ldy aligned for 4-element stores): the split loads go out 8 at a time
+// before any is added, then are summed in split order from 0, as above, so
+// the results are the same bits; the one-element kernel waits for each
+// split's load in turn.
+__global__ __launch_bounds__(256) void splitk_reduce4_kernel(const float* __restrict__ part, int splits, int64_t M,
+                                                             int64_t N, void* __restrict__ y, int64_t ldy, bool bf16) {
+  const int64_t MN = M * N;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;
+  float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int k0 = 0; k0 < splits; k0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < splits) v[j] = *reinterpret_cast<const float4*>(part + (int64_t)(k0 + j) * MN + i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < splits) {
+        s.x += v[j].x;
+        s.y += v[j].y;
+        s.z += v[j].z;
+        s.w += v[j].w;
+      }
+  }
+  const int64_t m = i / N, n = i - m * N;
+  if (bf16) {
+    uint2 w;
+    w.x = f32_to_bf16_rne(s.x) | (f32_to_bf16_rne(s.y) << 16);
+    w.y = f32_to_bf16_rne(s.z) | (f32_to_bf16_rne(s.w) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + m * ldy + n) = w;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(y) + m * ldy + n) = s;
+  }
+}
+
 #ifndef CFGM
 #define CFGM 128, 256, 2, 2
 #endif
@@ -1065,8 +1101,14 @@ hipError_t launch_gemm(const GemmArgs& g_in, const GemmPlan& p, hipStream_t stre
   }
   if (e != hipSuccess || g.splits <= 1) return e;
   const int64_t n = g.M * g.N;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, g.partial,
-                     g.splits, g.M, g.N, g.y, g.ldy, g.y_bf16);
+  if (g.vec_partial && g.vec_y) {
+    const int64_t threads = n / 4;
+    hipLaunchKernelGGL(splitk_reduce4_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       g.partial, g.splits, g.M, g.N, g.y, g.ldy, g.y_bf16);
+  } else {
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, g.partial,
+                       g.splits, g.M, g.N, g.y, g.ldy, g.y_bf16);
+  }
   return hipGetLastError();
 }
 
