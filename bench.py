@@ -311,9 +311,10 @@ def refine_main(args, torch, binding, inputs, dev):
         "hessian_ms_per_step": round(ms_h, 4), "refine_ms_per_step": round(ms_r, 4),
         "weight_rows_per_s": round(sum(L["N"] for L in layers) / (ms * 1e-3), 1),
         "moves_per_row_mean": round(float(fl.mean()), 2), "rows_at_cap_pct": round(100.0 * float((fl >= REFINE_CAP).mean()), 2),
-        "roofline": {"bound": "alu", "achieved": round(g_tf, 3), "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
+        "roofline": {"bound": "mfma", "achieved": round(g_tf, 3), "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(g_tf / PEAK_FP64_TFLOPS, 4), "traffic": None,
-                     "kernel": "macaq_flip_refine (flops: the gradient G = E H, 2 N K^2 in fp64, per call)"},
+                     "kernel": "macaq_flip_refine (flops: the gradient G = E H, 2 N K^2 in fp64 on the fp64 matrix "
+                               "cores, per call; the call also runs the moves)"},
         "timing": "HIP events on the launch stream around %d eager steps; each step restores the round-to-nearest "
                   "codes (a device copy) before refining" % steps,
     }
