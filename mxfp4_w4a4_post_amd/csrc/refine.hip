@@ -23,14 +23,9 @@ namespace {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Value of E2M1 magnitude code c (0 .. 7): 0, .5, 1, 1.5, 2, 3, 4, 6 (exact).
-__device__ __forceinline__ double e2m1_mag(int c) {
-  return c < 4 ? 0.5 * c : ldexp((c & 1) ? 1.5 : 1.0, (c >> 1) - 1);
-}
 // Signed index m in -7 .. 7 of a 4-bit code (the -0 code 8 is index 0) and back.
 __device__ __forceinline__ int code_index(uint32_t c) { return (c & 8) ? -(int)(c & 7) : (int)(c & 7); }
 __device__ __forceinline__ uint32_t index_code(int m) { return m < 0 ? (8u | (uint32_t)(-m)) : (uint32_t)m; }
-__device__ __forceinline__ double index_value(int m) { return m < 0 ? -e2m1_mag(-m) : e2m1_mag(m); }
 
 // Rows through the multiplier and the block-Hadamard, one lane per 32-element
 // chunk exactly as the quantizer does it (workgroup = 32 rows x 256 elements).
@@ -94,11 +89,21 @@ __global__ __launch_bounds__(256) void transform_kernel(const void* __restrict__
     const uint4 cw = *reinterpret_cast<const uint4*>(codes + tiled_code_offset(row, k0, kpad));
     const int sc = scales[tiled_scale_offset(row, k0, kpad)];
     const uint32_t cb[4] = {cw.x, cw.y, cw.z, cw.w};
-    double* o = out64 + row * K + k0;
+    // dequantized code, branch-free: magnitude code m < 2 is m / 2, else
+    // (1 or 1.5) * 2^(m / 2 - 1); times 2^(scale - 127); every factor is exact
+    double2* o = reinterpret_cast<double2*>(out64 + row * K + k0);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t nib = (cb[i >> 3] >> (4 * (i & 7))) & 0xF;
-      o[i] = (double)v[i] - ldexp(index_value(code_index(nib)), sc - 127);
+    for (int i = 0; i < 32; i += 2) {
+      double q[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t nib = (cb[(i + h) >> 3] >> (4 * ((i + h) & 7))) & 0xF;
+        const int m = (int)(nib & 7);
+        const double mant = m < 2 ? 0.5 * (double)m : ((m & 1) ? 1.5 : 1.0);
+        const double mag = ldexp(mant, (m < 2 ? 0 : (m >> 1) - 1) + sc - 127);
+        q[h] = (double)v[i + h] - (((nib & 8) && m != 0) ? -mag : mag);  // the -0 code is +0
+      }
+      o[i >> 1] = make_double2(q[0], q[1]);
     }
   } else {
     float4* o = reinterpret_cast<float4*>(out32 + row * K + k0);
