@@ -42,6 +42,26 @@ def test_hessian_bit_exact(dev, R, K, b):
     assert np.array_equal(H_g.cpu().numpy().view(np.uint64), H_o.view(np.uint64))
 
 
+@pytest.mark.parametrize("R,K,b,factor", [(129, 1024, 0, 1e4), (70, 2048, 32, 3e3)])
+def test_hessian_bit_exact_wide_range(dev, R, K, b, factor):
+    """Channels spanning four decades and a ragged row count, so the fp64
+    sums cancel and round at very different magnitudes: the matrix-core
+    Hessian must still equal the oracle's sequential fused sums bit for bit."""
+    log("hessian wide range R=%d K=%d b=%d factor=%g" % (R, K, b, factor))
+    rng = np.random.default_rng(R * K)
+    x = rng.standard_normal((R, K)).astype(np.float32)
+    x *= np.exp(rng.uniform(0.0, np.log(factor), K)).astype(np.float32)
+    x[:, ::7] *= -1.0
+    xt = inputs.to_bf16(x)
+    xb = bits(xt)
+    s = oracle.calibrate(xb)
+    a, _ = oracle.multipliers(s, b)
+    H_o = oracle.hessian(xb, a if b else None, b)
+    H_g = binding.hessian(xt.to(dev), torch.from_numpy(a).to(dev) if b else None, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(H_g.cpu().numpy().view(np.uint64), H_o.view(np.uint64))
+
+
 def _refine_case(dev, N, K, b, cap, f32=False, seed=0, R=96, H_np=None):
     rng = np.random.default_rng(seed)
     x = _rows(R, K, seed + 1)
