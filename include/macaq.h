@@ -94,6 +94,15 @@ const char* macaq_status_string(macaq_status s);
 const char* macaq_last_error(void);
 
 /*
+ * Test hook for the device check that every enqueuing call makes: with arch
+ * non-NULL, the check takes that architecture name (e.g. "gfx942") instead
+ * of querying the HIP runtime, so the MACAQ_EUNSUPPORTED path can be
+ * exercised on any host; NULL restores the real query. Process-wide; not for
+ * use while other threads call the library.
+ */
+void macaq_debug_override_arch(const char* arch);
+
+/*
  * Per-channel scale from calibration activations (the "calibrated
  * per-channel scale" of the paper card's title and Abstract):
  *   s[k] = RN32(sqrt(max_r |xcal[r, k]|)), or 1 when that maximum is 0.
@@ -114,27 +123,50 @@ macaq_status macaq_calibrate_pow(const void* xcal, int64_t R, int64_t K, int64_t
                                  macaq_stream_t stream);
 
 /*
- * Folded multipliers for one layer: a[k] = RN32(c_b / s[k]) for the
- * activations and r[k] = RN32(c_b * s[k]) for the weights, c_b =
- * RN32(1/sqrt(b)) (1 when b = 0). s, a, r: device fp32 [K]; a or r may be
- * NULL to skip it. b in {0, 32, 64, 128}.
+ * Folded multipliers for one layer. "MACaQ: Fast, Model Agnostic Calibrated
+ * Quantization ..." (paper card, Abstract) scales the activations per channel
+ * and absorbs the inverse into the same layer's weights; with D = diag(1/s)
+ * and the orthonormal H = S_b / sqrt(b) (both readings), the activations take
+ * a[k] = RN32(c_b / s[k]) and the weights r[k] = RN32(c_b * s[k]), c_b =
+ * RN32(1/sqrt(b)) (1 when b = 0), so that (r .* w) . (a .* x) = w . x before
+ * rounding.
+ *
+ * Host-only and pure: s, a, r are host fp32 [K]; a or r may be NULL to skip
+ * it; IEEE single-precision divide and multiply, no device, no stream, no
+ * state. b in {0, 32, 64, 128}. Every s[k] must be positive and finite
+ * (MACAQ_EINVAL otherwise, with nothing written).
  */
-macaq_status macaq_make_multipliers(const float* s, int64_t K, int32_t b, float* a, float* r,
-                                    macaq_stream_t stream);
+macaq_status macaq_make_multipliers(const float* s, int64_t K, int32_t b, float* a, float* r);
+
+/*
+ * The same multipliers computed on the device, for a scale s that already
+ * lives there (macaq_calibrate's output): s, a, r are device fp32 [K], the
+ * work is enqueued on `stream`, and the results are bit-identical to
+ * macaq_make_multipliers (correctly rounded divide and multiply). s[k] must
+ * be positive and finite (not checked: it lives on the device).
+ */
+macaq_status macaq_make_multipliers_device(const float* s, int64_t K, int32_t b, float* a, float* r,
+                                           macaq_stream_t stream);
 
 /*
  * Offline half (paper card, Abstract: inverse transforms absorbed into the
  * weights; round-to-nearest MXFP4): W' = MXFP4(rows of S_b (r .* W[n, :])).
  * W: device [N, ldw] of w_dtype (bf16 or fp32), row n = output channel n.
- * r: device fp32 [K] from macaq_make_multipliers, or NULL with b = 0 for
- * plain MXFP4 weights. w_codes / w_scales: device, MACAQ_GEMM_LAYOUT,
- * macaq_packed_codes_bytes(N, K) / macaq_packed_scales_bytes(N, K) bytes.
+ * r: device fp32 [K] (macaq_make_multipliers, copied to the device, or
+ * macaq_make_multipliers_device), or NULL with b = 0 for plain MXFP4
+ * weights. w_codes / w_scales: device, in `layout`:
+ *   MACAQ_ROW_MAJOR:   [N, K/2] codes and [N, K/32] scales (N*K/2 and
+ *                      N*K/32 bytes; an interchange form);
+ *   MACAQ_GEMM_LAYOUT: macaq_packed_codes_bytes(N, K) /
+ *                      macaq_packed_scales_bytes(N, K) bytes, padding zero:
+ *                      what macaq_linear, macaq_gemm and the grouped and MoE
+ *                      calls read.
  * Requires K % 32 == 0, K % b == 0, ldw >= K; W, w_codes and w_scales 16-byte
  * aligned and rows of W a multiple of 16 bytes.
  */
 macaq_status macaq_prepare_weights(const void* W, macaq_dtype w_dtype, int64_t N, int64_t K, int64_t ldw,
-                                   const float* r, int32_t b, uint8_t* w_codes, uint8_t* w_scales,
-                                   macaq_stream_t stream);
+                                   const float* r, int32_t b, macaq_layout layout, uint8_t* w_codes,
+                                   uint8_t* w_scales, macaq_stream_t stream);
 
 /*
  * Online activation transform on its own (paper card, Abstract: per-channel
@@ -184,10 +216,13 @@ macaq_status macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t
 size_t macaq_linear_grouped_workspace_size(int64_t T, int32_t E, int64_t K, int64_t N);
 
 /*
- * The layer for E experts of a mixture-of-experts block (the pages apply
- * MACaQ unchanged to MoE models; each expert's linear layer has its own D and
- * absorbed weights): rows [offsets[e], offsets[e+1]) of X belong to expert e
- * and go through a[e, :] and W'_e.
+ * The layer for E experts of a mixture-of-experts block. "MACaQ - Huawei
+ * open-sources a 4-bit quantizer for GGUF, vLLM and Diffusers" (What it is)
+ * lists MoE models among those one recipe covers, and its How it works
+ * section handles every linear layer on its own; so each expert's linear
+ * layer is a MACaQ layer with its own D and absorbed weights: rows
+ * [offsets[e], offsets[e+1]) of X belong to expert e and go through a[e, :]
+ * and W'_e.
  * X: device bf16 [T, K] (contiguous, expert-major); offsets: device int32
  * [E+1], non-decreasing, offsets[0] = 0, offsets[E] = T (not checked on the
  * host: it lives on the device); a: device fp32 [E, K] or NULL with b = 0;

@@ -35,8 +35,11 @@ _SIGNATURES = {
     "macaq_last_error": (ctypes.c_char_p, []),
     "macaq_calibrate": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
     "macaq_calibrate_pow": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp]),
-    "macaq_make_multipliers": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
-    "macaq_prepare_weights": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp]),
+    "macaq_debug_override_arch": (None, [ctypes.c_char_p]),
+    "macaq_make_multipliers": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp]),
+    "macaq_make_multipliers_device": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
+    "macaq_prepare_weights": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, ctypes.c_int, _vp, _vp,
+                                             _vp]),
     "macaq_quant_act": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, ctypes.c_int, _vp, _vp, _vp]),
     "macaq_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
     "macaq_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64, _vp, ctypes.c_int, _i64,
@@ -86,14 +89,20 @@ def library_path() -> str:
 
 
 def load_library():
-    """Load libmacaq.so; build it first only when no built library exists."""
+    """Load libmacaq.so. It is (re)built first when it is missing or was built
+    from other sources than those in csrc/ and include/ now (the digest that
+    build.py records beside it), so the library that runs is always the one
+    the sources describe."""
     global _lib
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(_LIB_PATH):
-            from . import build as _build
+        from . import build as _build
+        if not _build.is_current():
+            print("macaq: libmacaq.so is missing or older than its sources; building it", flush=True)
             _build.build()
+            if not _build.is_current():
+                raise RuntimeError("macaq: the built library does not match its sources")
         lib = ctypes.CDLL(_LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             f = getattr(lib, name)
@@ -101,6 +110,12 @@ def load_library():
             f.argtypes = args
         _lib = lib
         return lib
+
+
+def override_arch(arch: str | None):
+    """Make the library's device check see `arch` instead of the device
+    (None restores the real query): the test hook of macaq.h."""
+    load_library().macaq_debug_override_arch(None if arch is None else arch.encode())
 
 
 def _status_string(status: int) -> str:
@@ -153,12 +168,29 @@ def calibrate(xcal: torch.Tensor, quarters: int = 2) -> torch.Tensor:
 
 
 def make_multipliers(s: torch.Tensor, b: int):
-    """(a, r): activation multiplier c_b / s and weight multiplier c_b * s."""
+    """(a, r): activation multiplier c_b / s and weight multiplier c_b * s of
+    a device scale s (macaq_make_multipliers_device, on s's stream)."""
     _need_cuda(s)
     s = s.contiguous()
     a = torch.empty_like(s)
     r = torch.empty_like(s)
-    _check(load_library().macaq_make_multipliers(_ptr(s), s.numel(), b, _ptr(a), _ptr(r), _stream(s)),
+    _check(load_library().macaq_make_multipliers_device(_ptr(s), s.numel(), b, _ptr(a), _ptr(r), _stream(s)),
+           "macaq_make_multipliers_device")
+    return a, r
+
+
+def make_multipliers_host(s, b: int):
+    """(a, r) of a host scale s (numpy fp32 or a CPU tensor) through the
+    library's host-only macaq_make_multipliers; returns numpy fp32 arrays."""
+    import numpy as np
+    if isinstance(s, torch.Tensor):
+        if s.is_cuda:
+            raise ValueError("macaq: make_multipliers_host takes a host scale")
+        s = s.numpy()
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    a = np.empty_like(s)
+    r = np.empty_like(s)
+    _check(load_library().macaq_make_multipliers(s.ctypes.data, s.size, b, a.ctypes.data, r.ctypes.data),
            "macaq_make_multipliers")
     return a, r
 
@@ -171,16 +203,28 @@ def packed_scales_bytes(rows: int, K: int) -> int:
     return int(load_library().macaq_packed_scales_bytes(rows, K))
 
 
-def prepare_weights(w: torch.Tensor, r: torch.Tensor | None, b: int, out: Packed | None = None) -> Packed:
-    """W' = MXFP4(W D^-1 H^T) in the GEMM layout."""
+def prepare_weights(w: torch.Tensor, r: torch.Tensor | None, b: int, out: Packed | None = None,
+                    layout: str = "gemm"):
+    """W' = MXFP4(W D^-1 H^T). layout "gemm" (default): a Packed operand in
+    the GEMM layout; layout "row": (codes [N, K/2], scales [N, K/32])."""
     _need_cuda(w, r)
     assert w.dim() == 2 and w.stride(1) == 1
     N, K = w.shape
+    if layout == "row":
+        codes = torch.empty(N, K // 2, dtype=torch.uint8, device=w.device)
+        scales = torch.empty(N, K // 32, dtype=torch.uint8, device=w.device)
+        _check(load_library().macaq_prepare_weights(_ptr(w), _dtype_code(w.dtype), N, K, w.stride(0), _ptr(r), b,
+                                                    MACAQ_ROW_MAJOR, _ptr(codes), _ptr(scales), _stream(w)),
+               "macaq_prepare_weights")
+        return codes, scales
+    if layout != "gemm":
+        raise ValueError("layout is 'row' or 'gemm'")
     if out is None:
         out = Packed(torch.empty(packed_codes_bytes(N, K), dtype=torch.uint8, device=w.device),
                      torch.empty(packed_scales_bytes(N, K), dtype=torch.uint8, device=w.device), N, K)
     _check(load_library().macaq_prepare_weights(_ptr(w), _dtype_code(w.dtype), N, K, w.stride(0), _ptr(r), b,
-                                                _ptr(out.codes), _ptr(out.scales), _stream(w)), "macaq_prepare_weights")
+                                                MACAQ_GEMM_LAYOUT, _ptr(out.codes), _ptr(out.scales), _stream(w)),
+           "macaq_prepare_weights")
     return out
 
 

@@ -7,6 +7,7 @@ packed-fp32 instructions.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -16,6 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmacaq.so")
+# digest of the sources and flags the library was built from, written after it
+DIGEST = LIB + ".digest"
 SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "moe.hip", "refine.hip"]
 
 HIPCC_FLAGS = [
@@ -31,8 +34,31 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
+def source_digest() -> str:
+    """sha256 (16 hex digits) of every file in csrc/, the public header and
+    the compiler flags."""
+    h = hashlib.sha256()
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)) + [os.path.join(INCLUDE, "macaq.h")]
+    for path in files:
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(HIPCC_FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
+def is_current() -> bool:
+    """True when libmacaq.so exists and was built from the current sources."""
+    if not (os.path.exists(LIB) and os.path.exists(DIGEST)):
+        return False
+    with open(DIGEST) as f:
+        return f.read().strip() == source_digest()
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source into libmacaq.so (always recompiles)."""
+    """Compile every source into libmacaq.so (always recompiles) and record
+    the sources' digest beside it."""
+    digest = source_digest()
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-o", tmp] + srcs
@@ -47,6 +73,9 @@ def build(verbose: bool = False) -> str:
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
+    with open(DIGEST + ".tmp", "w") as f:
+        f.write(digest + "\n")
+    os.replace(DIGEST + ".tmp", DIGEST)
     return LIB
 
 

@@ -34,12 +34,26 @@ macaq_status hip_fail(hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool valid_block(int32_t b) { return b == 0 || b == 32 || b == 64 || b == 128; }
 
+// c_b = RN32(1/sqrt(b)) (1 without a Hadamard): 1/b is exact in fp32 for a
+// power of two and sqrtf rounds once.
+float multiplier_cb(int32_t b) { return b > 0 ? std::sqrt(1.0f / (float)b) : 1.0f; }
+
 // gfx950 check of the current device, cached per device id.
 constexpr int kMaxDevices = 64;
 int g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
 std::mutex g_arch_mu;
+// Architecture name that replaces the device query when set (a test hook).
+char g_arch_override[64];
+bool g_arch_overridden = false;
 
 macaq_status check_device() {
+  {
+    std::lock_guard<std::mutex> lk(g_arch_mu);
+    if (g_arch_overridden) {
+      if (std::strncmp(g_arch_override, "gfx950", 6) == 0) return MACAQ_OK;
+      return fail(MACAQ_EUNSUPPORTED, "device is %s, not gfx950", g_arch_override);
+    }
+  }
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(MACAQ_EUNSUPPORTED, "no usable HIP device: %s", hipGetErrorString(e));
@@ -264,30 +278,61 @@ macaq_status macaq_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx
   return macaq_calibrate_pow(xcal, R, K, ldx, 2, s, stream);
 }
 
-macaq_status macaq_make_multipliers(const float* s, int64_t K, int32_t b, float* a, float* r, macaq_stream_t stream) {
-  if (!s || (!a && !r)) return fail(MACAQ_EINVAL, "macaq_make_multipliers: NULL pointer");
-  if (K < 1) return fail(MACAQ_EINVAL, "macaq_make_multipliers: K < 1");
-  if (!valid_block(b)) return fail(MACAQ_EINVAL, "macaq_make_multipliers: block %d not in {0, 32, 64, 128}", b);
+void macaq_debug_override_arch(const char* arch) {
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  g_arch_overridden = arch != nullptr;
+  if (arch) {
+    std::strncpy(g_arch_override, arch, sizeof g_arch_override - 1);
+    g_arch_override[sizeof g_arch_override - 1] = 0;
+  }
+}
+
+macaq_status macaq_make_multipliers(const float* s, int64_t K, int32_t b, float* a, float* r) {
+  const char* who = "macaq_make_multipliers";
+  if (!s || (!a && !r)) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (K < 1) return fail(MACAQ_EINVAL, "%s: K < 1", who);
+  if (!valid_block(b)) return fail(MACAQ_EINVAL, "%s: block %d not in {0, 32, 64, 128}", who, b);
   if (!aligned(s, 4) || (a && !aligned(a, 4)) || (r && !aligned(r, 4)))
-    return fail(MACAQ_EALIGN, "macaq_make_multipliers: misaligned pointer");
+    return fail(MACAQ_EALIGN, "%s: misaligned pointer", who);
+  for (int64_t k = 0; k < K; ++k)
+    if (!(s[k] > 0.0f) || !std::isfinite(s[k]))
+      return fail(MACAQ_EINVAL, "%s: s[%lld] = %g is not positive and finite", who, (long long)k, (double)s[k]);
+  const float cb = multiplier_cb(b);
+  // IEEE single precision: each quotient and product is rounded once
+  // (this file is compiled without contraction)
+  for (int64_t k = 0; k < K; ++k) {
+    if (a) a[k] = cb / s[k];
+    if (r) r[k] = cb * s[k];
+  }
+  return MACAQ_OK;
+}
+
+macaq_status macaq_make_multipliers_device(const float* s, int64_t K, int32_t b, float* a, float* r,
+                                           macaq_stream_t stream) {
+  const char* who = "macaq_make_multipliers_device";
+  if (!s || (!a && !r)) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (K < 1) return fail(MACAQ_EINVAL, "%s: K < 1", who);
+  if (!valid_block(b)) return fail(MACAQ_EINVAL, "%s: block %d not in {0, 32, 64, 128}", who, b);
+  if (!aligned(s, 4) || (a && !aligned(a, 4)) || (r && !aligned(r, 4)))
+    return fail(MACAQ_EALIGN, "%s: misaligned pointer", who);
   macaq_status st = check_device();
   if (st != MACAQ_OK) return st;
-  // c_b = RN32(1/sqrt(b)): 1/b is exact in fp32 and sqrtf rounds once.
-  const float cb = b > 0 ? std::sqrt(1.0f / (float)b) : 1.0f;
-  hipError_t e = launch_multipliers(s, K, cb, a, r, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_make_multipliers launch");
+  hipError_t e = launch_multipliers(s, K, multiplier_cb(b), a, r, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_make_multipliers_device launch");
 }
 
 macaq_status macaq_prepare_weights(const void* W, macaq_dtype w_dtype, int64_t N, int64_t K, int64_t ldw,
-                                   const float* r, int32_t b, uint8_t* w_codes, uint8_t* w_scales,
-                                   macaq_stream_t stream) {
+                                   const float* r, int32_t b, macaq_layout layout, uint8_t* w_codes,
+                                   uint8_t* w_scales, macaq_stream_t stream) {
   const char* who = "macaq_prepare_weights";
   if (w_dtype != MACAQ_BF16 && w_dtype != MACAQ_F32) return fail(MACAQ_EINVAL, "%s: bad weight dtype", who);
   macaq_status st = check_quant_shape(N, K, ldw, b, who);
   if (st != MACAQ_OK) return st;
+  if (layout != MACAQ_ROW_MAJOR && layout != MACAQ_GEMM_LAYOUT) return fail(MACAQ_EINVAL, "%s: bad layout", who);
   if (N == 0) return MACAQ_OK;
   if (!W || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
-  if (!operand_fits(N, K)) return fail(MACAQ_EINVAL, "%s: packed weights over 2 GiB", who);
+  if (layout == MACAQ_GEMM_LAYOUT && !operand_fits(N, K))
+    return fail(MACAQ_EINVAL, "%s: packed weights over 2 GiB", who);
   const size_t esz = w_dtype == MACAQ_F32 ? 4 : 2;
   if (!aligned(W, 16) || (ldw * (int64_t)esz) % 16 != 0 || !aligned(w_codes, 16) || !aligned(w_scales, 16) ||
       (r && !aligned(r, 16)))
@@ -303,7 +348,7 @@ macaq_status macaq_prepare_weights(const void* W, macaq_dtype w_dtype, int64_t N
   q.mult = r;
   q.codes = w_codes;
   q.scales = w_scales;
-  q.tiled = true;
+  q.tiled = layout == MACAQ_GEMM_LAYOUT;
   q.kpad = pad_k(K);
   hipError_t e = launch_quant_rows(q, b, w_dtype == MACAQ_F32, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_prepare_weights launch");

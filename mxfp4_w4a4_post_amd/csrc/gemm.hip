@@ -852,6 +852,375 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::O
   gemm_tiles<C, false, MODE>(g, tiles * g.splits, smem);
 }
 
+// ---------------------------------------------------------------------------
+// Wide tiles for large prefill shapes: 256 activation rows x 256 weight rows
+// per workgroup of 4 waves. Wave w owns weight rows [64w, 64w + 64) of the
+// tile and all 256 activation rows (8 x 2 fragments of 32 x 32, 256 fp32
+// accumulators per lane). One 256-element step moves 34 KiB of activations
+// and 34 KiB of weights for 33.5 MFLOP, two thirds of the bytes per flop of
+// the 128 x 256 tile. The activation block goes from memory straight into LDS
+// (buffer loads with the LDS flag, so no registers stage it) into one of four
+// stages, each wave loading two of its eight row groups; the weights of a
+// wave go into the registers its MFMAs read, two steps ahead, as in Pipe.
+// Steps run on across tiles: the last steps of a tile already load the first
+// steps of the workgroup's next tile, so only the epilogue separates them.
+//
+// Per step s (J = s % 4, stage J holds step s) and half step h:
+//   h < 3: read the fragments of (s, h+1) from stage J;
+//   h = 3: wait until this wave's loads of stage J+1 (step s+1) are done,
+//          barrier (every wave's are), read the fragments and scales of
+//          (s+1, 0) from stage J+1, then load step s+3 into stage J+3 = J-1
+//          (last read during step s-1, before the barrier);
+//   then the 16 MFMAs of (s, h), and the weight registers of half h are
+//   refilled with step s+2 (the scale dwords after h = 3).
+// The wait counts loads in issue order: after the loads of stage J+1 (issued
+// in half 3 of step s-2) come at least the 10 loads of stage J+2 (half 3 of
+// step s-1) and the 6 weight loads of halves 0-2 of step s, each half fenced
+// from the next, so vmcnt(16) covers stage J+1. Loads past a tile's range
+// or of rows past the operand go through an empty buffer resource (zeros, no
+// memory traffic) so that every step issues the same loads and the count
+// holds.
+// ---------------------------------------------------------------------------
+struct WideCfg {
+  static constexpr int BM = 256, BN = 256, FM = 8, FN = 2, WN = 64;
+  static constexpr int A_CODES = FM * kCodeBlock;    // 32 KiB
+  static constexpr int A_SCALES = FM * kScaleBlock;  // 2 KiB
+  // a stage holds the scales first, then the codes: every read of a stage
+  // is within 64 KiB of its start (one base address, immediate offsets)
+  static constexpr int CODES_AT = A_SCALES;
+  static constexpr int STAGE = A_CODES + A_SCALES;
+  static constexpr int EPI = epi_region(WN);         // bf16 epilogue staging, per wave
+  static constexpr int GROUP_M = 8;                  // m-tiles that share n-tiles in the walk
+  static constexpr int kStageWait = 16;              // vmcnt that covers the next stage (above)
+};
+static_assert(4 * WideCfg::STAGE + 4 * WideCfg::EPI <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+
+// Four LDS stages as distinct objects, so the compiler tells the loads into
+// one stage from the reads of another and waits only for what a read needs.
+__shared__ __attribute__((aligned(1024))) uint8_t wide_st0[WideCfg::STAGE];
+__shared__ __attribute__((aligned(1024))) uint8_t wide_st1[WideCfg::STAGE];
+__shared__ __attribute__((aligned(1024))) uint8_t wide_st2[WideCfg::STAGE];
+__shared__ __attribute__((aligned(1024))) uint8_t wide_st3[WideCfg::STAGE];
+__shared__ __attribute__((aligned(16))) uint8_t wide_epi[4 * WideCfg::EPI];
+
+template <int S>
+__device__ __forceinline__ uint8_t* wide_stage() {
+  if constexpr (S == 0) return wide_st0;
+  else if constexpr (S == 1) return wide_st1;
+  else if constexpr (S == 2) return wide_st2;
+  else return wide_st3;
+}
+
+typedef __attribute__((address_space(3))) void* LdsPtr;
+
+// 16 (or 4) bytes per lane from the buffer into LDS at lds + 16 * lane (4 *
+// lane); lds is uniform over the wave.
+__device__ __forceinline__ void dma16(Rsrc r, uint8_t* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, (int)voff, __builtin_amdgcn_readfirstlane(soff), 0, 0);
+}
+__device__ __forceinline__ void dma4(Rsrc r, uint8_t* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 4, (int)voff, __builtin_amdgcn_readfirstlane(soff), 0, 0);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8); the counters not named keep their maximum.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4); }
+constexpr int kWaitAll = 0;
+
+template <int MODE>
+struct Wide {
+  Acc<WideCfg> acc;
+  WStage<WideCfg> w[2];
+  AFrag<WideCfg> af[2];
+  uint32_t asc[WideCfg::FM], asc_next[WideCfg::FM];
+  // The tile's operands as buffers that start at its first row group, so a
+  // row group past the operand's end falls outside the buffer (loads of
+  // zeros, no memory traffic).
+  Rsrc ra, ras, rw, rws;
+  // This wave's lane offsets into them: activation row groups 2w, 2w+1 by
+  // quarter h of the k-block (codes) and their scales; weight row groups
+  // 2w, 2w+1 (codes: the quarter is an instruction offset) and scales.
+  uint32_t va[2][NH], vas[2], vw[2], vws[2];
+  int wave, lane;
+  int n;          // k-blocks per tile (a multiple of 4)
+
+  __device__ __forceinline__ void set_tile(const GemmArgs& g, int64_t m0, int64_t n0) {
+    const int64_t KB = n;
+    const int64_t a0 = (m0 / kGroupRows) * KB, w0 = (n0 / kGroupRows) * KB;
+    ra = make_rsrc(g.a_codes + a0 * kCodeBlock, tiled_codes_bytes(g.M, g.K) - a0 * kCodeBlock);
+    ras = make_rsrc(g.a_scales + a0 * kScaleBlock, tiled_scales_bytes(g.M, g.K) - a0 * kScaleBlock);
+    rw = make_rsrc(g.b_codes + w0 * kCodeBlock, tiled_codes_bytes(g.N, g.K) - w0 * kCodeBlock);
+    rws = make_rsrc(g.b_scales + w0 * kScaleBlock, tiled_scales_bytes(g.N, g.K) - w0 * kScaleBlock);
+  }
+
+  __device__ __forceinline__ void set_lanes() {
+    const uint32_t KB = (uint32_t)n;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t grp = (uint32_t)(2 * wave + i) * KB;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) va[i][h] = grp * kCodeBlock + h * kCodeHalf + lane * 16;
+      vas[i] = grp * kScaleBlock + lane * 4;
+      vw[i] = grp * kCodeBlock + lane * 16;
+      vws[i] = grp * kScaleBlock + lane * 4;
+    }
+  }
+
+  // The activation block of k-block kt into stage S (past the tile: zeros
+  // through an empty buffer, so every step issues the same loads).
+  template <int S>
+  __device__ __forceinline__ void load_stage(int kt) {
+    uint8_t* st = wide_stage<S>();
+    const bool live = kt < n;
+    const Rsrc rc = live ? ra : make_rsrc(nullptr, 0), rs = live ? ras : make_rsrc(nullptr, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        dma16(rc, st + WideCfg::CODES_AT + (2 * wave + i) * kCodeBlock + h * kCodeHalf, va[i][h], kt * kCodeBlock);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma4(rs, st + (2 * wave + i) * kScaleBlock, vas[i], kt * kScaleBlock);
+  }
+
+  // Quarter H of this wave's weights of k-block kt into slot st, or the
+  // scale dwords.
+  template <int H>
+  __device__ __forceinline__ void load_w_half(WStage<WideCfg>& st, int kt) {
+    const Rsrc r = kt < n ? rw : make_rsrc(nullptr, 0);
+#pragma unroll
+    for (int j = 0; j < WideCfg::FN; ++j) st.c[j][H] = load16(r, vw[j], kt * kCodeBlock + H * kCodeHalf);
+  }
+  __device__ __forceinline__ void load_w_scales(WStage<WideCfg>& st, int kt) {
+    const Rsrc r = kt < n ? rws : make_rsrc(nullptr, 0);
+#pragma unroll
+    for (int j = 0; j < WideCfg::FN; ++j) st.s[j] = load4(r, vws[j], kt * kScaleBlock);
+  }
+  __device__ __forceinline__ void load_w(WStage<WideCfg>& st, int kt) {
+    load_w_half<0>(st, kt);
+    load_w_half<1>(st, kt);
+    load_w_half<2>(st, kt);
+    load_w_half<3>(st, kt);
+    load_w_scales(st, kt);
+  }
+
+  template <int S>
+  __device__ __forceinline__ void read_frag(AFrag<WideCfg>& f, int h) {
+    const uint8_t* st = wide_stage<S>();
+#pragma unroll
+    for (int i = 0; i < WideCfg::FM; ++i)
+      f.c[i] = *reinterpret_cast<const v4i*>(st + WideCfg::CODES_AT + i * kCodeBlock + h * kCodeHalf + lane * 16);
+  }
+  template <int S>
+  __device__ __forceinline__ void read_scales(uint32_t (&s)[WideCfg::FM]) {
+    const uint8_t* st = wide_stage<S>();
+#pragma unroll
+    for (int i = 0; i < WideCfg::FM; ++i) s[i] = *reinterpret_cast<const uint32_t*>(st + i * kScaleBlock + lane * 4);
+  }
+
+  template <int H, int WS, int FS>
+  __device__ __forceinline__ void mfma_half() {
+#pragma unroll
+    for (int i = 0; i < WideCfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < WideCfg::FN; ++j)
+        acc.v[i][j] = mfma(w[WS].c[j][H], af[FS].c[i], acc.v[i][j], (int)w[WS].s[j], (int)asc[i], H);
+  }
+
+  // Half H of step s (J = s % 4).
+  template <int J, int H>
+  __device__ __forceinline__ void half(int s) {
+    constexpr int WS = J % 2, FS = H & 1;
+    constexpr int N_MFMA = WideCfg::FM * WideCfg::FN;
+    if constexpr (H < NH - 1) {
+      read_frag<J>(af[FS ^ 1], H + 1);
+    } else {
+      // stage J+1 complete in every wave, and every read of stage J+3 done
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(WideCfg::kStageWait));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frag<(J + 1) % 4>(af[FS ^ 1], 0);
+      read_scales<(J + 1) % 4>(asc_next);
+      load_stage<(J + 3) % 4>(s + 3);
+    }
+    mfma_half<H, WS, FS>();
+    load_w_half<H>(w[WS], s + 2);
+    if constexpr (H == NH - 1) load_w_scales(w[WS], s + 2);
+    constexpr int NR = (H < NH - 1) ? WideCfg::FM : 2 * WideCfg::FM;
+    constexpr int NV = WideCfg::FN + ((H == NH - 1) ? WideCfg::FN + 10 : 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NR, 0);
+    interleave<0, N_MFMA, 0, 0, NV>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  template <int J>
+  __device__ __forceinline__ void step(int s) {
+    half<J, 0>(s);
+    half<J, 1>(s);
+    half<J, 2>(s);
+    half<J, 3>(s);
+#pragma unroll
+    for (int i = 0; i < WideCfg::FM; ++i) asc[i] = asc_next[i];
+  }
+
+  // Stages 0-2 of the current tile (issued before the previous tile's
+  // output: they hold no registers; the weights follow the output, in
+  // prologue_start).
+  __device__ __forceinline__ void prologue_loads() {
+    load_stage<0>(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage<1>(1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage<2>(2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Weight steps 0 and 1, then stage 0 visible to every wave, its first
+  // fragments read, accumulators cleared. After stage 0 come stages 1 and 2,
+  // possibly the previous tile's output stores, and weight steps 0 and 1
+  // (10 loads each): vmcnt(40) covers stage 0.
+  __device__ __forceinline__ void prologue_start() {
+    load_w(w[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(w[1], 1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(40));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frag<0>(af[0], 0);
+    read_scales<0>(asc);
+#pragma unroll
+    for (int i = 0; i < WideCfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < WideCfg::FN; ++j) acc.v[i][j] = {};
+  }
+
+  // The tile's output, wave w's 256 rows x 64 columns, through buffer
+  // stores into a resource that spans rows [m0, M) from column n0w, so rows
+  // past M fall outside it; a column run past N takes an offset past every
+  // buffer. Needs N % 8 == 0 (bf16: 16-byte runs) or N % 4 == 0 (fp32: 4
+  // consecutive outputs per lane), ldy and Y aligned to match (the launcher
+  // checks). Fenced per 32-row fragment so the compiler keeps only one
+  // fragment's values in flight.
+  __device__ __forceinline__ void epilogue(const GemmArgs& g, int64_t m0, int64_t n0w) {
+    const int64_t m_lim = g.M - m0;
+    const int n_lim = (int)(g.N - n0w < WideCfg::WN ? g.N - n0w : WideCfg::WN);
+    if (n_lim <= 0) return;
+    constexpr int ES = MODE == kOutBf16Staged ? 2 : 4;
+    const Rsrc yr = make_rsrc(static_cast<uint8_t*>(g.y) + (m0 * g.ldy + n0w) * ES, ((m_lim - 1) * g.ldy + n_lim) * ES);
+    const int ld = (int)g.ldy * ES;  // bytes per row (< 2^31: Y's rows are within 2 GiB of the tile)
+    // the lane index is recomputed here (mbcnt) where the compiler cannot
+    // hoist it, so the lane's offsets are not held in registers across the
+    // main loop
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    if constexpr (MODE == kOutBf16Staged) {
+      constexpr int PITCH = epi_pitch(WideCfg::WN);
+      uint8_t* region = wide_epi + wave * WideCfg::EPI;
+      const int rr = ln >> 3, cc = (ln & 7) * 8;  // a pass covers rows rr of 8, 16 bytes at column cc
+      const uint32_t vo = cc < n_lim ? (uint32_t)(rr * ld + cc * 2) : kOob;
+#pragma unroll
+      for (int i = 0; i < WideCfg::FM; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int jn = 0; jn < WideCfg::FN; ++jn)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v16f& a = acc.v[i][jn];
+            const int n = jn * 32 + 8 * q + 4 * (ln >> 5);
+            uint2 wv;
+            wv.x = f32_to_bf16_rne(a[4 * q]) | (f32_to_bf16_rne(a[4 * q + 1]) << 16);
+            wv.y = f32_to_bf16_rne(a[4 * q + 2]) | (f32_to_bf16_rne(a[4 * q + 3]) << 16);
+            lds_at<uint2>(region, (ln & 31) * PITCH + n * 2) = wv;
+          }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const v4i v = lds_at<v4i>(region, (8 * p + rr) * PITCH + cc * 2);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
+                                                 yr, (int)vo, __builtin_amdgcn_readfirstlane((32 * i + 8 * p) * ld),
+                                                 0);
+        }
+      }
+    } else {
+      const int r = ln & 31, c4 = 4 * (ln >> 5);
+#pragma unroll
+      for (int i = 0; i < WideCfg::FM; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int jn = 0; jn < WideCfg::FN; ++jn)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v16f& a = acc.v[i][jn];
+            const int n = jn * 32 + 8 * q + c4;
+            const uint32_t vo = n < n_lim ? (uint32_t)(r * ld + n * 4) : kOob;
+            const v4f v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
+                                                   yr, (int)vo, __builtin_amdgcn_readfirstlane(32 * i * ld), 0);
+          }
+      }
+    }
+  }
+
+  // Tile t of the walk: groups of GROUP_M m-tiles share n-tiles, and each
+  // XCD takes a contiguous run of the walk.
+  __device__ __forceinline__ void tile_origin(const GemmArgs& g, uint32_t t, uint32_t tiles, int64_t& m0,
+                                              int64_t& n0) const {
+    const uint32_t x = t % kNumXcd, q = tiles / kNumXcd, r = tiles % kNumXcd;
+    const uint32_t u = x * q + (x < r ? x : r) + t / kNumXcd;
+    const uint32_t mt = (uint32_t)((g.M + WideCfg::BM - 1) / WideCfg::BM);
+    const uint32_t nt = (uint32_t)((g.N + WideCfg::BN - 1) / WideCfg::BN);
+    const uint32_t group = u / (WideCfg::GROUP_M * nt);
+    const uint32_t first_m = group * WideCfg::GROUP_M;
+    const uint32_t gsize = (mt - first_m) < WideCfg::GROUP_M ? (mt - first_m) : WideCfg::GROUP_M;
+    const uint32_t in_group = u - group * WideCfg::GROUP_M * nt;
+    m0 = (int64_t)(first_m + in_group % gsize) * WideCfg::BM;
+    n0 = (int64_t)(in_group / gsize) * WideCfg::BN;
+  }
+
+  __device__ __forceinline__ void run(const GemmArgs& g) {
+    lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t tiles =
+        (uint32_t)(((g.M + WideCfg::BM - 1) / WideCfg::BM) * ((g.N + WideCfg::BN - 1) / WideCfg::BN));
+    n = (int)(pad_k(g.K) / kBlockK);
+    set_lanes();
+    uint32_t t = blockIdx.x;
+    int64_t m0, n0;
+    tile_origin(g, t, tiles, m0, n0);
+    set_tile(g, m0, n0);
+    prologue_loads();
+    prologue_start();
+    for (;;) {
+      for (int s0 = 0; s0 < n; s0 += 4) {
+        step<0>(s0);
+        step<1>(s0 + 1);
+        step<2>(s0 + 2);
+        step<3>(s0 + 3);
+      }
+      // the next tile's first loads go out before this tile's output
+      const uint32_t tn = t + gridDim.x;
+      const int64_t pm0 = m0, pn0 = n0;
+      if (tn < tiles) {
+        tile_origin(g, tn, tiles, m0, n0);
+        set_tile(g, m0, n0);
+        prologue_loads();
+      }
+      epilogue(g, pm0, pn0 + wave * WideCfg::WN);
+      if (tn >= tiles) break;
+      t = tn;
+      prologue_start();
+    }
+    // loads past the last tile write zeros into LDS: let them land before
+    // the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+  }
+};
+
+template <int MODE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_wide_kernel(GemmArgs g) {
+  Wide<MODE> p;
+  p.run(g);
+}
+
 // Grouped: the tile map (built by build_tile_map_kernel) lists, per m-tile,
 // the expert and the first row; unused entries are skipped.
 template <class C, int MODE>
@@ -948,26 +1317,11 @@ __global__ __launch_bounds__(256) void splitk_reduce4_kernel(const float* __rest
   }
 }
 
-#ifndef CFGM
-#define CFGM 128, 256, 2, 2
-#endif
-using CfgM = TileCfg<CFGM>;  // prefill
-#ifndef CFGS64
-#define CFGS64 64, 128, 4, 2, true, 2
-#endif
-#ifndef CFGS32
-#define CFGS32 32, 128, 4, 2, true, 2
-#endif
-using CfgS64 = TileCfg<CFGS64>;  // decode, M <= 64
-using CfgS32 = TileCfg<CFGS32>;  // decode, M <= 32
-#ifndef CFGG
-#define CFGG 128, 256, 2, 2, true, 1, true
-#endif
-using CfgG = TileCfg<CFGG>;  // grouped (MoE experts), bf16 / fp32 output
-#ifndef CFGGS
-#define CFGGS 64, 256, 2, 2, true, 2
-#endif
-using CfgGS = TileCfg<CFGGS>;  // grouped with the SwiGLU epilogue (MoE gate/up)
+using CfgM = TileCfg<128, 256, 2, 2>;  // prefill
+using CfgS64 = TileCfg<64, 128, 4, 2, true, 2>;  // decode, M <= 64
+using CfgS32 = TileCfg<32, 128, 4, 2, true, 2>;  // decode, M <= 32
+using CfgG = TileCfg<128, 256, 2, 2, true, 1, true>;  // grouped (MoE experts), bf16 / fp32 output
+using CfgGS = TileCfg<64, 256, 2, 2, true, 2>;  // grouped with the SwiGLU epilogue (MoE gate/up)
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
@@ -1026,6 +1380,24 @@ hipError_t launch_grouped_cfg(const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The wide kernel's output stores need whole 16-byte runs of a row (bf16
+// with N % 8 == 0, fp32 with N % 4 == 0, row starts aligned to them) and
+// address Y through a 32-bit buffer range.
+bool wide_output_ok(const GemmArgs& g) {
+  const int64_t es = g.y_bf16 ? 2 : 4;
+  if (g.M * g.ldy * es >= (int64_t(1) << 31)) return false;
+  return g.y_bf16 ? (g.vec16_y && g.N % 8 == 0) : (g.vec_y && g.N % 4 == 0);
+}
+
+hipError_t launch_wide(const GemmArgs& g, hipStream_t stream) {
+  const int64_t tiles = ((g.M + WideCfg::BM - 1) / WideCfg::BM) * ((g.N + WideCfg::BN - 1) / WideCfg::BN);
+  if (tiles > 0x7FFFFFFF || g.splits != 1 || !wide_output_ok(g)) return hipErrorInvalidValue;
+  const dim3 gd((unsigned)(tiles < kNumCu ? tiles : kNumCu)), bd(NT);
+  if (g.y_bf16) hipLaunchKernelGGL(gemm_wide_kernel<kOutBf16Staged>, gd, bd, 0, stream, g);
+  else hipLaunchKernelGGL(gemm_wide_kernel<kOutF32>, gd, bd, 0, stream, g);
+  return hipGetLastError();
+}
+
 // Vector stores of 4 outputs need 4-element alignment of every row start.
 void set_vec_flags(GemmArgs& g) {
   const size_t es = g.y_bf16 ? 2 : 4;
@@ -1043,8 +1415,15 @@ constexpr double kUnitStartBytes = 64.0 * 1024.0;
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   GemmPlan p{};
   int64_t resident;
+  const int64_t wide_tiles = ((M + WideCfg::BM - 1) / WideCfg::BM) * ((N + WideCfg::BN - 1) / WideCfg::BN);
   if (M <= 32) { p.cfg = 3; p.bm = CfgS32::BM; p.bn = CfgS32::BN; resident = (int64_t)kNumCu * CfgS32::OCC; }
   else if (M <= 64) { p.cfg = 2; p.bm = CfgS64::BM; p.bn = CfgS64::BN; resident = (int64_t)kNumCu * CfgS64::OCC; }
+  else if (wide_tiles >= kNumCu && (pad_k(K) / kBlockK) % 4 == 0) {
+    p.cfg = 4;
+    p.bm = WideCfg::BM;
+    p.bn = WideCfg::BN;
+    resident = kNumCu;
+  }
   else { p.cfg = 1; p.bm = CfgM::BM; p.bn = CfgM::BN; resident = (int64_t)kNumCu * CfgM::OCC; }
   const int64_t nt = (N + p.bn - 1) / p.bn;
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * nt;
@@ -1095,6 +1474,7 @@ hipError_t launch_gemm(const GemmArgs& g_in, const GemmPlan& p, hipStream_t stre
   set_vec_flags(g);
   hipError_t e;
   switch (p.cfg) {
+    case 4: e = wide_output_ok(g) ? launch_wide(g, stream) : launch_cfg<CfgM>(g, stream); break;
     case 1: e = launch_cfg<CfgM>(g, stream); break;
     case 2: e = launch_cfg<CfgS64>(g, stream); break;
     default: e = launch_cfg<CfgS32>(g, stream); break;

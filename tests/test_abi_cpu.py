@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 25, names
+    assert len(names) == 27, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding._SIGNATURES), "binding signatures out of sync with the header"
@@ -66,11 +66,16 @@ def test_quant_act_rejects(lib):
 
 
 def test_prepare_weights_rejects(lib):
-    f = lib.macaq_prepare_weights
-    assert f(FAKE, 7, 8, 64, 64, None, 32, FAKE, FAKE, None) == EINVAL  # dtype
-    assert f(FAKE, 1, 8, 64, 66, None, 32, FAKE, FAKE, None) == EALIGN  # fp32 rows not 16-byte multiples
-    assert f(FAKE, 0, 8, 64, 64, None, 32, None, FAKE, None) == EINVAL
-    assert f(FAKE, 0, 0, 64, 64, None, 32, FAKE, FAKE, None) == OK
+    def f(W, dt, N, K, ldw, r, b, codes, scales, layout=1):
+        return lib.macaq_prepare_weights(W, dt, N, K, ldw, r, b, layout, codes, scales, None)
+
+    assert f(FAKE, 7, 8, 64, 64, None, 32, FAKE, FAKE) == EINVAL  # dtype
+    assert f(FAKE, 1, 8, 64, 66, None, 32, FAKE, FAKE) == EALIGN  # fp32 rows not 16-byte multiples
+    assert f(FAKE, 0, 8, 64, 64, None, 32, None, FAKE) == EINVAL
+    assert f(FAKE, 0, 8, 64, 64, None, 32, FAKE, FAKE, layout=5) == EINVAL  # bad layout
+    assert f(FAKE, 0, 1 << 24, 1 << 10, 1 << 10, None, 32, FAKE, FAKE) == EINVAL  # GEMM layout over 2 GiB
+    assert f(FAKE, 0, 0, 64, 64, None, 32, FAKE, FAKE) == OK
+    assert f(FAKE, 0, 0, 64, 64, None, 32, FAKE, FAKE, layout=0) == OK
 
 
 def test_linear_rejects(lib):
@@ -111,13 +116,110 @@ def test_calibrate_and_multipliers_reject(lib):
     assert lib.macaq_calibrate(FAKE, 0, 8, 8, FAKE, None) == EINVAL
     assert lib.macaq_calibrate(FAKE, 4, 8, 4, FAKE, None) == EINVAL
     assert lib.macaq_calibrate(FAKE + 1, 4, 8, 8, FAKE, None) == EALIGN
-    assert lib.macaq_make_multipliers(FAKE, 8, 48, FAKE, FAKE, None) == EINVAL
-    assert lib.macaq_make_multipliers(FAKE, 8, 32, None, None, None) == EINVAL
-    assert lib.macaq_make_multipliers(FAKE, 0, 32, FAKE, None, None) == EINVAL
+    d = lib.macaq_make_multipliers_device
+    assert d(FAKE, 8, 48, FAKE, FAKE, None) == EINVAL
+    assert d(FAKE, 8, 32, None, None, None) == EINVAL
+    assert d(FAKE, 0, 32, FAKE, None, None) == EINVAL
+    assert d(FAKE + 2, 8, 32, FAKE, None, None) == EALIGN
+
+
+def _f32(a):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a, a.ctypes.data
+
+
+def test_make_multipliers_host_matches_oracle(lib, orc):
+    """The host-only macaq_make_multipliers (no device, no stream) against
+    the oracle, bit for bit, for every Hadamard block, on scales that span
+    the fp32 range (subnormal to near overflow) and values whose quotient
+    and product round at a tie-adjacent point."""
+    import numpy as np
+    rng = np.random.default_rng(11)
+    s = np.concatenate([
+        np.float32(2.0) ** rng.integers(-149, 127, size=300).astype(np.float32),
+        (rng.random(300) * 100 + 1e-3).astype(np.float32),
+        np.array([1.0, 3.0, np.float32(np.sqrt(2.0)), 1e-40, 3.4e38, 0.1], np.float32),
+    ]).astype(np.float32)
+    for b in (0, 32, 64, 128):
+        a_o, r_o = orc.multipliers(s, b)
+        s_, sp = _f32(s)
+        a = np.full_like(s, np.nan)
+        r = np.full_like(s, np.nan)
+        assert lib.macaq_make_multipliers(sp, s.size, b, a.ctypes.data, r.ctypes.data) == OK
+        assert np.array_equal(a.view(np.uint32), a_o.view(np.uint32)), b
+        assert np.array_equal(r.view(np.uint32), r_o.view(np.uint32)), b
+        # either output may be skipped
+        a2 = np.zeros_like(s)
+        assert lib.macaq_make_multipliers(sp, s.size, b, a2.ctypes.data, None) == OK
+        assert np.array_equal(a2.view(np.uint32), a_o.view(np.uint32))
+
+
+def test_make_multipliers_host_rejects(lib):
+    """Bad arguments and non-positive or non-finite scales: a status, and
+    nothing written."""
+    import numpy as np
+    s, sp = _f32([1.0, 2.0, 0.0, 4.0])
+    a = np.full(4, 7.0, np.float32)
+    assert lib.macaq_make_multipliers(sp, 4, 32, a.ctypes.data, None) == EINVAL  # s[2] == 0
+    assert "s[2]" in _last(lib)
+    for bad in (-1.0, np.inf, np.nan):
+        s2, sp2 = _f32([1.0, bad])
+        assert lib.macaq_make_multipliers(sp2, 2, 32, a.ctypes.data, None) == EINVAL
+    assert np.all(a == 7.0)
+    assert lib.macaq_make_multipliers(sp, 4, 48, a.ctypes.data, None) == EINVAL  # block
+    assert lib.macaq_make_multipliers(sp, 0, 32, a.ctypes.data, None) == EINVAL  # K
+    assert lib.macaq_make_multipliers(None, 4, 32, a.ctypes.data, None) == EINVAL
+    assert lib.macaq_make_multipliers(sp, 4, 32, None, None) == EINVAL
+    assert lib.macaq_make_multipliers(sp + 2, 2, 32, a.ctypes.data, None) == EALIGN
+    assert np.all(a == 7.0)
+
+
+def test_binding_host_multipliers(orc):
+    import numpy as np
+    s = np.array([0.5, 2.0, 9.0, 1e-3], np.float32)
+    a, r = binding.make_multipliers_host(s, 64)
+    a_o, r_o = orc.multipliers(s, 64)
+    assert np.array_equal(a, a_o) and np.array_equal(r, r_o)
+
+
+def test_unsupported_device_reported_before_any_work(lib):
+    """With the device check told it runs on another architecture, every
+    enqueuing call returns MACAQ_EUNSUPPORTED after its argument checks, and
+    the caller's output stays untouched (host buffers stand in for device
+    memory: nothing may be written or launched)."""
+    import numpy as np
+    y = np.full(4 * 16, 3.0, np.float32)
+    codes = np.full(4 * 64 // 2, 0xAB, np.uint8)
+    scales = np.full(4 * 64 // 32, 0xCD, np.uint8)
+    x = np.zeros((4, 64), np.uint16)
+    ws = np.zeros(1 << 16, np.uint8)
+    wsp = (ws.ctypes.data + 255) // 256 * 256
+    binding.override_arch("gfx942")
+    try:
+        st = lib.macaq_quant_act(x.ctypes.data, 4, 64, 64, None, 32, 0, codes.ctypes.data, scales.ctypes.data, None)
+        assert st == EUNSUPPORTED and "gfx942" in _last(lib)
+        st = lib.macaq_prepare_weights(x.ctypes.data, 0, 4, 64, 64, None, 32, 0, codes.ctypes.data,
+                                       scales.ctypes.data, None)
+        assert st == EUNSUPPORTED
+        st = lib.macaq_linear(x.ctypes.data, 4, 64, 64, None, 32, FAKE, FAKE, 16, y.ctypes.data, 1, 16, wsp,
+                              len(ws) - 256, None)
+        assert st == EUNSUPPORTED
+        assert lib.macaq_make_multipliers_device(FAKE, 8, 32, FAKE, FAKE, None) == EUNSUPPORTED
+        # argument errors still win over the device check
+        assert lib.macaq_linear(x.ctypes.data, 4, 64, 64, None, 32, FAKE, FAKE, 0, y.ctypes.data, 1, 16, wsp,
+                                len(ws) - 256, None) == EINVAL
+        # the host-only call needs no device
+        s, sp = _f32([1.0, 2.0])
+        a = np.zeros(2, np.float32)
+        assert lib.macaq_make_multipliers(sp, 2, 32, a.ctypes.data, None) == OK
+    finally:
+        binding.override_arch(None)
+    assert np.all(y == 3.0) and np.all(codes == 0xAB) and np.all(scales == 0xCD)
 
 
 def test_packed_sizes(lib):
-    """GEMM layout: rows padded to 64, K to 128; codes K/2 and scales K/32 bytes a row."""
+    """GEMM layout: rows padded to 32, K to 256; codes K/2 and scales K/32 bytes a row."""
     for rows, K in [(1, 32), (16, 256), (65, 96), (2048, 4096), (8192, 28672)]:
         RP, KP = -(-rows // 32) * 32, -(-K // 256) * 256
         assert lib.macaq_packed_codes_bytes(rows, K) == RP * KP // 2

@@ -16,8 +16,8 @@ import torch
 
 import oracle
 from mxfp4_w4a4_post_amd import binding, inputs
-from parity_util import (REL_L2_TOL, assert_bf16_close, assert_quant_equal, bits, log, np_u8, packed_to_row_major,
-                         rel_l2, row_major_to_gemm_layout)
+from parity_util import (REL_L2_TOL, accumulation_bound, assert_bf16_bracket, assert_elementwise, assert_quant_equal,
+                         bits, log, np_u8, packed_to_row_major, rel_l2, row_major_to_gemm_layout, tile_sample)
 
 pytestmark = pytest.mark.gpu
 
@@ -192,10 +192,49 @@ def test_gemm_random_codes(dev, M, N, K):
     pa, pw = packed(ac, as_), packed(wc, ws)
     y = binding.linear_plain_gemm(pa, pw, out_dtype=torch.float32)
     y_o = oracle.gemm_codes(ac, as_, wc, ws)
+    bound = accumulation_bound(oracle, ac, as_, wc, ws, K)
+    assert_elementwise(y.cpu().numpy(), y_o, bound, "gemm fp32 %d %d %d" % (M, N, K))
     err = rel_l2(y.cpu().numpy(), y_o)
     assert err <= REL_L2_TOL, err
     y16 = binding.linear_plain_gemm(pa, pw, out_dtype=torch.bfloat16)
-    assert_bf16_close(y16, y.cpu().numpy().astype(np.float64), "gemm bf16 %d %d %d" % (M, N, K))
+    assert_bf16_bracket(y16, y_o, bound, "gemm bf16 %d %d %d" % (M, N, K))
+
+
+# Shapes with at least 256 tiles of 256 x 256 (and K a multiple of 1024):
+# the wide-tile kernel, with ragged last m- and n-tiles (N a multiple of 8).
+WIDE_SHAPES = [(4100, 4104, 1024), (4096, 4096, 2048), (2048, 14336, 4096), (3000, 6152, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", WIDE_SHAPES)
+def test_gemm_wide_tiles_random_codes(dev, M, N, K):
+    """The wide-tile GEMM on random codes: every output row of a sample that
+    holds a row of every 256-row tile (and the last row), all columns, each
+    within its accumulation bound, in fp32 and bf16."""
+    log("gemm wide M=%d N=%d K=%d" % (M, N, K))
+    rng = np.random.default_rng(M + 3 * N + 7 * K)
+    ac = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    as_ = rng.integers(118, 136, size=(M, K // 32), dtype=np.uint8)
+    wc = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    ws = rng.integers(118, 136, size=(N, K // 32), dtype=np.uint8)
+
+    def packed(c, sc):
+        tc, ts = row_major_to_gemm_layout(c, sc)
+        return binding.Packed(torch.from_numpy(tc).to(dev), torch.from_numpy(ts).to(dev), c.shape[0], 2 * c.shape[1])
+
+    pa, pw = packed(ac, as_), packed(wc, ws)
+    y = binding.linear_plain_gemm(pa, pw, out_dtype=torch.float32)
+    y16 = binding.linear_plain_gemm(pa, pw, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = tile_sample(M, 256, rng, extra=(0,))
+    y_o = oracle.gemm_codes(ac[rows], as_[rows], wc, ws)
+    bound = accumulation_bound(oracle, ac[rows], as_[rows], wc, ws, K)
+    got = y.cpu().numpy()[rows]
+    assert_elementwise(got, y_o, bound, "gemm wide fp32")
+    assert rel_l2(got, y_o) <= REL_L2_TOL
+    assert_bf16_bracket(y16.cpu()[torch.from_numpy(rows)], y_o, bound, "gemm wide bf16")
+    # the same call again is bit-identical
+    y2 = binding.linear_plain_gemm(pa, pw, out_dtype=torch.float32)
+    assert torch.equal(y, y2)
 
 
 # ---------------------------------------------------------------------------
@@ -221,13 +260,16 @@ def check_linear(case, dev, rows=None, cols=None, b=None):
     wc_o, ws_o = oracle.prepare_weights(wb, r_o, b)
     assert_quant_equal(wc_g[cols], ws_g[cols], wc_o, ws_o, oracle.transform_rows(wb, r_o, b),
                        case.name + " W'")
-    y_o = oracle.linear(xb, a_o, b, wc_o, ws_o)
+    ac_o, as_o = oracle.quant_rows(xb, a_o, b)
+    y_o = oracle.gemm_codes(ac_o, as_o, wc_o, ws_o)
+    bound = accumulation_bound(oracle, ac_o, as_o, wc_o, ws_o, case.K)
     got = y_g.cpu().numpy()[np.ix_(rows, cols)]
+    assert_elementwise(got, y_o, bound, case.name + " fp32")
     err = rel_l2(got, y_o)
     log("%s rel-L2 %.3g on %dx%d outputs" % (case.name, err, len(rows), len(cols)))
     assert err <= REL_L2_TOL, err
-    assert_bf16_close(y_g16.cpu()[torch.from_numpy(rows)][:, torch.from_numpy(cols)],
-                      got.astype(np.float64), case.name + " bf16")
+    assert_bf16_bracket(y_g16.cpu()[torch.from_numpy(rows)][:, torch.from_numpy(cols)], y_o, bound,
+                        case.name + " bf16")
     return y_g
 
 
@@ -284,12 +326,12 @@ def test_linear_strided_and_empty(dev):
 
 @pytest.mark.parametrize("shape", [0, 1, 2])
 def test_linear_prefill_8b(dev, shape):
+    """The whole layer on the GPU; the oracle on a row of every 128-row tile
+    (and the first and last rows) by every column."""
     case = cached_case(2, shape)
     log("linear %s" % case.name)
     rng = np.random.default_rng(100 + shape)
-    rows = np.sort(rng.choice(case.M, 24, replace=False))
-    cols = np.sort(rng.choice(case.N, 384, replace=False))
-    check_linear(case, dev, rows, cols)
+    check_linear(case, dev, tile_sample(case.M, 128, rng, extra=(0,)), None)
 
 
 @pytest.mark.parametrize("shape", [0, 1])
@@ -305,11 +347,14 @@ def test_linear_decode_32b(dev, M, shape):
 
 @pytest.mark.parametrize("shape,b", [(0, 32), (1, 32), (0, 64), (1, 64), (0, 128), (1, 128)])
 def test_linear_prefill_large(dev, shape, b):
+    """The whole layer on the GPU as the benchmark runs it; the oracle on a
+    row of every 256-row tile by every column (so every output tile is
+    checked), each output within its accumulation bound."""
     case = case_with_block(5, shape, b)
     log("linear %s" % case.name)
     rng = np.random.default_rng(300 + shape + b)
-    rows = np.sort(rng.choice(case.M, 12, replace=False))
-    cols = np.sort(rng.choice(case.N, 256, replace=False))
+    rows = tile_sample(case.M, 256, rng, extra=(0,)) if b == 32 else np.sort(rng.choice(case.M, 12, replace=False))
+    cols = None if b == 32 else np.sort(rng.choice(case.N, 512, replace=False))
     check_linear(case, dev, rows, cols, b=b)
 
 
