@@ -872,15 +872,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::O
 //          (s+1, 0) from stage J+1, then load step s+3 into stage J+3 = J-1
 //          (last read during step s-1, before the barrier);
 //   then the 16 MFMAs of (s, h), and the weight registers of half h are
-//   refilled with step s+2 (the scale dwords after h = 3).
-// The wait counts loads in issue order: after the loads of stage J+1 (issued
-// in half 3 of step s-2) come at least the 10 loads of stage J+2 (half 3 of
-// step s-1) and the 6 weight loads of halves 0-2 of step s, each half fenced
-// from the next, so vmcnt(16) covers stage J+1. Loads past a tile's range
-// or of rows past the operand go through an empty buffer resource (zeros, no
-// memory traffic) so that every step issues the same loads and the count
-// holds.
-// ---------------------------------------------------------------------------
+//   refilled with step s+2 (in half 0 also the weight scale dwords of step
+//   s+2, into one of four slots, so no MFMA of step s waits for them).
+// The stage wait counts loads in issue order: after the loads of stage J+1
+// (issued in half 3 of step s-2) come the 20 loads of step s-1 (10 weight,
+// 10 of stage J+2) and the 8 weight loads of halves 0-2 of step s, each half
+// fenced from the next, so vmcnt(28) covers stage J+1 and leaves the weights
+// of steps s+1 and s+2 in flight (in the first two steps of a tile that
+// follows an output, that output's stores sit between them too and are
+// waited for as well). Loads past a tile's range
+// or of rows past the operand go through an empty buffer resource (zeros,
+// no memory traffic) so that every step issues the same loads and the
+// counts hold.
 struct WideCfg {
   static constexpr int BM = 256, BN = 256, FM = 8, FN = 2, WN = 64;
   static constexpr int A_CODES = FM * kCodeBlock;    // 32 KiB
@@ -889,11 +892,10 @@ struct WideCfg {
   // is within 64 KiB of its start (one base address, immediate offsets)
   static constexpr int CODES_AT = A_SCALES;
   static constexpr int STAGE = A_CODES + A_SCALES;
-  static constexpr int EPI = epi_region(WN);         // bf16 epilogue staging, per wave
   static constexpr int GROUP_M = 8;                  // m-tiles that share n-tiles in the walk
-  static constexpr int kStageWait = 16;              // vmcnt that covers the next stage (above)
+  static constexpr int kStageWait = 28;              // vmcnt that covers the next stage (above)
 };
-static_assert(4 * WideCfg::STAGE + 4 * WideCfg::EPI <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+static_assert(4 * WideCfg::STAGE <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 
 // Four LDS stages as distinct objects, so the compiler tells the loads into
 // one stage from the reads of another and waits only for what a read needs.
@@ -901,7 +903,6 @@ __shared__ __attribute__((aligned(1024))) uint8_t wide_st0[WideCfg::STAGE];
 __shared__ __attribute__((aligned(1024))) uint8_t wide_st1[WideCfg::STAGE];
 __shared__ __attribute__((aligned(1024))) uint8_t wide_st2[WideCfg::STAGE];
 __shared__ __attribute__((aligned(1024))) uint8_t wide_st3[WideCfg::STAGE];
-__shared__ __attribute__((aligned(16))) uint8_t wide_epi[4 * WideCfg::EPI];
 
 template <int S>
 __device__ __forceinline__ uint8_t* wide_stage() {
@@ -930,8 +931,9 @@ constexpr int kWaitAll = 0;
 template <int MODE>
 struct Wide {
   Acc<WideCfg> acc;
-  WStage<WideCfg> w[2];
-  AFrag<WideCfg> af[2];
+  WStage<WideCfg> w[2];             // weight codes of steps s, s+1 (slot s % 2)
+  uint32_t wsc[4][WideCfg::FN];     // weight scale dwords of steps s .. s+2 (slot s % 4)
+  AFrag<WideCfg> af;  // activation fragments of the current half step, refilled one by one
   uint32_t asc[WideCfg::FM], asc_next[WideCfg::FM];
   // The tile's operands as buffers that start at its first row group, so a
   // row group past the operand's end falls outside the buffer (loads of
@@ -990,17 +992,17 @@ struct Wide {
 #pragma unroll
     for (int j = 0; j < WideCfg::FN; ++j) st.c[j][H] = load16(r, vw[j], kt * kCodeBlock + H * kCodeHalf);
   }
-  __device__ __forceinline__ void load_w_scales(WStage<WideCfg>& st, int kt) {
+  __device__ __forceinline__ void load_w_scales(uint32_t (&sc)[WideCfg::FN], int kt) {
     const Rsrc r = kt < n ? rws : make_rsrc(nullptr, 0);
 #pragma unroll
-    for (int j = 0; j < WideCfg::FN; ++j) st.s[j] = load4(r, vws[j], kt * kScaleBlock);
+    for (int j = 0; j < WideCfg::FN; ++j) sc[j] = load4(r, vws[j], kt * kScaleBlock);
   }
-  __device__ __forceinline__ void load_w(WStage<WideCfg>& st, int kt) {
+  __device__ __forceinline__ void load_w(WStage<WideCfg>& st, uint32_t (&sc)[WideCfg::FN], int kt) {
+    load_w_scales(sc, kt);
     load_w_half<0>(st, kt);
     load_w_half<1>(st, kt);
     load_w_half<2>(st, kt);
     load_w_half<3>(st, kt);
-    load_w_scales(st, kt);
   }
 
   template <int S>
@@ -1017,38 +1019,37 @@ struct Wide {
     for (int i = 0; i < WideCfg::FM; ++i) s[i] = *reinterpret_cast<const uint32_t*>(st + i * kScaleBlock + lane * 4);
   }
 
-  template <int H, int WS, int FS>
-  __device__ __forceinline__ void mfma_half() {
-#pragma unroll
-    for (int i = 0; i < WideCfg::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < WideCfg::FN; ++j)
-        acc.v[i][j] = mfma(w[WS].c[j][H], af[FS].c[i], acc.v[i][j], (int)w[WS].s[j], (int)asc[i], H);
-  }
-
-  // Half H of step s (J = s % 4).
+  // Half H of step s (J = s % 4): fragment i feeds its two MFMAs, then is
+  // refilled at once with fragment i of the next half step (read about 14
+  // MFMAs ahead of its use), so one set of fragment registers serves.
   template <int J, int H>
   __device__ __forceinline__ void half(int s) {
-    constexpr int WS = J % 2, FS = H & 1;
+    constexpr int WS = J % 2;
     constexpr int N_MFMA = WideCfg::FM * WideCfg::FN;
-    if constexpr (H < NH - 1) {
-      read_frag<J>(af[FS ^ 1], H + 1);
-    } else {
+    // the next half step: (s, H+1) from stage J, or (s+1, 0) from stage J+1
+    constexpr int NS = H < NH - 1 ? J : (J + 1) % 4;
+    constexpr int NHH = H < NH - 1 ? H + 1 : 0;
+    if constexpr (H == NH - 1) {
       // stage J+1 complete in every wave, and every read of stage J+3 done
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(WideCfg::kStageWait));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      read_frag<(J + 1) % 4>(af[FS ^ 1], 0);
-      read_scales<(J + 1) % 4>(asc_next);
+      read_scales<NS>(asc_next);
       load_stage<(J + 3) % 4>(s + 3);
     }
-    mfma_half<H, WS, FS>();
+    const uint8_t* nst = wide_stage<NS>() + WideCfg::CODES_AT + NHH * kCodeHalf + lane * 16;
+#pragma unroll
+    for (int i = 0; i < WideCfg::FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < WideCfg::FN; ++j)
+        acc.v[i][j] = mfma(w[WS].c[j][H], af.c[i], acc.v[i][j], (int)wsc[J][j], (int)asc[i], H);
+      af.c[i] = *reinterpret_cast<const v4i*>(nst + i * kCodeBlock);
+    }
+    if constexpr (H == 0) load_w_scales(wsc[(J + 2) % 4], s + 2);
     load_w_half<H>(w[WS], s + 2);
-    if constexpr (H == NH - 1) load_w_scales(w[WS], s + 2);
-    constexpr int NR = (H < NH - 1) ? WideCfg::FM : 2 * WideCfg::FM;
-    constexpr int NV = WideCfg::FN + ((H == NH - 1) ? WideCfg::FN + 10 : 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NR, 0);
-    interleave<0, N_MFMA, 0, 0, NV>();
+    constexpr int NV = WideCfg::FN + ((H == 0) ? WideCfg::FN : 0) + ((H == NH - 1) ? 10 : 0);
+    if constexpr (H == NH - 1) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, WideCfg::FM, 0);
+    interleave<0, N_MFMA, WideCfg::FM, 0, NV>();
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -1075,23 +1076,27 @@ struct Wide {
   }
 
   // Weight steps 0 and 1, then stage 0 visible to every wave, its first
-  // fragments read, accumulators cleared. After stage 0 come stages 1 and 2,
-  // possibly the previous tile's output stores, and weight steps 0 and 1
-  // (10 loads each): vmcnt(40) covers stage 0.
+  // fragments read, accumulators cleared. After stage 0 come stages 1 and 2
+  // and weight steps 0 and 1 (10 loads each), with the previous tile's
+  // output stores (at least 32, see epilogue) between them after a tile:
+  // vmcnt(40), or the counter's maximum of 63 then.
+  template <bool AFTER_OUTPUT>
   __device__ __forceinline__ void prologue_start() {
-    load_w(w[0], 0);
+    load_w(w[0], wsc[0], 0);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(w[1], 1);
+    load_w(w[1], wsc[1], 1);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(40));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(AFTER_OUTPUT ? 63 : 40));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_frag<0>(af[0], 0);
+    read_frag<0>(af, 0);
     read_scales<0>(asc);
+    if constexpr (!AFTER_OUTPUT) {  // after an output, the epilogue has cleared them
 #pragma unroll
-    for (int i = 0; i < WideCfg::FM; ++i)
+      for (int i = 0; i < WideCfg::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < WideCfg::FN; ++j) acc.v[i][j] = {};
+        for (int j = 0; j < WideCfg::FN; ++j) acc.v[i][j] = {};
+    }
   }
 
   // The tile's output, wave w's 256 rows x 64 columns, through buffer
@@ -1104,40 +1109,55 @@ struct Wide {
   __device__ __forceinline__ void epilogue(const GemmArgs& g, int64_t m0, int64_t n0w) {
     const int64_t m_lim = g.M - m0;
     const int n_lim = (int)(g.N - n0w < WideCfg::WN ? g.N - n0w : WideCfg::WN);
-    if (n_lim <= 0) return;
     constexpr int ES = MODE == kOutBf16Staged ? 2 : 4;
-    const Rsrc yr = make_rsrc(static_cast<uint8_t*>(g.y) + (m0 * g.ldy + n0w) * ES, ((m_lim - 1) * g.ldy + n_lim) * ES);
-    const int ld = (int)g.ldy * ES;  // bytes per row (< 2^31: Y's rows are within 2 GiB of the tile)
+    // a wave whose columns are all past N still issues its stores (into an
+    // empty buffer), so every wave issues the same number of them
+    const Rsrc yr = n_lim > 0 ? make_rsrc(static_cast<uint8_t*>(g.y) + (m0 * g.ldy + n0w) * ES,
+                                          ((m_lim - 1) * g.ldy + n_lim) * ES)
+                              : make_rsrc(nullptr, 0);
+    // bytes per row (< 2^31: Y is within a 2 GiB buffer range), uniform
+    const int ld = __builtin_amdgcn_readfirstlane((int)g.ldy * ES);
     // the lane index is recomputed here (mbcnt) where the compiler cannot
     // hoist it, so the lane's offsets are not held in registers across the
     // main loop
     int ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
     if constexpr (MODE == kOutBf16Staged) {
-      constexpr int PITCH = epi_pitch(WideCfg::WN);
-      uint8_t* region = wide_epi + wave * WideCfg::EPI;
-      const int rr = ln >> 3, cc = (ln & 7) * 8;  // a pass covers rows rr of 8, 16 bytes at column cc
-      const uint32_t vo = cc < n_lim ? (uint32_t)(rr * ld + cc * 2) : kOob;
+      // Lane l < 32 holds row l, columns 8q .. 8q+3 of each 32-column
+      // fragment, lane l+32 columns 8q+4 .. 8q+7: one permlane32 swap per
+      // dword of a q pair gives lane l columns 16p .. 16p+7 and lane l+32
+      // columns 16p+8 .. 16p+15, so each lane stores 16 contiguous bytes.
+      const int r = ln & 31, half = ln >> 5;
+      const uint32_t vrow = (uint32_t)(r * ld + half * 16);
 #pragma unroll
       for (int i = 0; i < WideCfg::FM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
+        // keep the row's accumulators in their AGPRs until here, so the
+        // conversion copies out one row at a time
 #pragma unroll
-        for (int jn = 0; jn < WideCfg::FN; ++jn)
+        for (int jn = 0; jn < WideCfg::FN; ++jn) asm volatile("" : "+a"(acc.v[i][jn]));
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const v16f& a = acc.v[i][jn];
-            const int n = jn * 32 + 8 * q + 4 * (ln >> 5);
-            uint2 wv;
-            wv.x = f32_to_bf16_rne(a[4 * q]) | (f32_to_bf16_rne(a[4 * q + 1]) << 16);
-            wv.y = f32_to_bf16_rne(a[4 * q + 2]) | (f32_to_bf16_rne(a[4 * q + 3]) << 16);
-            lds_at<uint2>(region, (ln & 31) * PITCH + n * 2) = wv;
+        for (int jn = 0; jn < WideCfg::FN; ++jn) {
+          const v16f& a = acc.v[i][jn];
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            uint32_t lo[2], hi[2];  // q = 2p and q = 2p + 1, two dwords each
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+              lo[d] = f32_to_bf16_rne(a[8 * p + 2 * d]) | (f32_to_bf16_rne(a[8 * p + 2 * d + 1]) << 16);
+              hi[d] = f32_to_bf16_rne(a[8 * p + 4 + 2 * d]) | (f32_to_bf16_rne(a[8 * p + 4 + 2 * d + 1]) << 16);
+              const auto sw = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
+              lo[d] = sw[0];
+              hi[d] = sw[1];
+            }
+            const int col = jn * 32 + 16 * p + 8 * half;  // this lane's first column
+            const uint32_t vo = col < n_lim ? vrow : kOob;
+            const __attribute__((ext_vector_type(4))) unsigned v = {lo[0], lo[1], hi[0], hi[1]};
+            __builtin_amdgcn_raw_buffer_store_b128(v, yr, (int)vo,
+                                                   __builtin_amdgcn_readfirstlane(32 * i * ld + (jn * 32 + 16 * p) * 2),
+                                                   0);
           }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const v4i v = lds_at<v4i>(region, (8 * p + rr) * PITCH + cc * 2);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
-                                                 yr, (int)vo, __builtin_amdgcn_readfirstlane((32 * i + 8 * p) * ld),
-                                                 0);
+          acc.v[i][jn] = {};  // ready for the next tile
         }
       }
     } else {
@@ -1156,6 +1176,8 @@ struct Wide {
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
                                                    yr, (int)vo, __builtin_amdgcn_readfirstlane(32 * i * ld), 0);
           }
+#pragma unroll
+        for (int jn = 0; jn < WideCfg::FN; ++jn) acc.v[i][jn] = {};  // ready for the next tile
       }
     }
   }
@@ -1188,7 +1210,7 @@ struct Wide {
     tile_origin(g, t, tiles, m0, n0);
     set_tile(g, m0, n0);
     prologue_loads();
-    prologue_start();
+    prologue_start<false>();
     for (;;) {
       for (int s0 = 0; s0 < n; s0 += 4) {
         step<0>(s0);
@@ -1196,7 +1218,11 @@ struct Wide {
         step<2>(s0 + 2);
         step<3>(s0 + 3);
       }
-      // the next tile's first loads go out before this tile's output
+      // every load still in flight is a zero load past the tile (the last
+      // real ones fed its last steps): let them land, so that none holds a
+      // register the output reuses; then the next tile's first activation
+      // blocks go out before this tile's output
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
       const uint32_t tn = t + gridDim.x;
       const int64_t pm0 = m0, pn0 = n0;
       if (tn < tiles) {
@@ -1207,7 +1233,7 @@ struct Wide {
       epilogue(g, pm0, pn0 + wave * WideCfg::WN);
       if (tn >= tiles) break;
       t = tn;
-      prologue_start();
+      prologue_start<true>();
     }
     // loads past the last tile write zeros into LDS: let them land before
     // the workgroup's LDS is released
