@@ -199,6 +199,25 @@ macaq_status macaq_linear(const void* X, int64_t M, int64_t K, int64_t ldx, cons
                           macaq_stream_t stream);
 
 /*
+ * macaq_linear for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same computation and kernels, with the
+ * quantized activations and split-K partial sums in a scratch array the
+ * library owns, 128 MiB on each GPU it runs on, held until the process ends
+ * (its address is looked up on the first call on a device). Arguments as
+ * macaq_linear without the workspace. A call whose scratch need,
+ * macaq_linear_workspace_size(M, K, N), exceeds 128 MiB returns
+ * MACAQ_EWORKSPACE before anything is enqueued. Every call on one GPU uses
+ * the same scratch: calls that may overlap on one GPU (different streams
+ * without ordering between them) race and give wrong results; calls on one
+ * stream are ordered and safe. Nothing in the scratch needs clearing
+ * between calls.
+ */
+macaq_status macaq_linear_noalloc(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
+                                  const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, void* Y,
+                                  macaq_dtype y_dtype, int64_t ldy, macaq_stream_t stream);
+
+/*
  * The GEMM alone on operands already in MXFP4 (the contraction step of
  * macaq_linear; also the baseline for the cost of the activation transform):
  * Y[m, n] = sum_k dq(A[m, k]) dq(W'[n, k]).

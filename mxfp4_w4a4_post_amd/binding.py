@@ -44,6 +44,8 @@ _SIGNATURES = {
     "macaq_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
     "macaq_linear": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64, _vp, ctypes.c_int, _i64,
                                     _vp, _sz, _vp]),
+    "macaq_linear_noalloc": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64, _vp, ctypes.c_int,
+                                            _i64, _vp]),
     "macaq_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
     "macaq_gemm": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, ctypes.c_int, _i64, _vp, _sz, _vp]),
     "macaq_linear_grouped_workspace_size": (_sz, [_i64, _i32, _i64, _i64]),
@@ -282,6 +284,22 @@ def linear(x: torch.Tensor, a: torch.Tensor | None, b: int, w: Packed, out_dtype
                                        _ptr(y), _dtype_code(y.dtype), y.stride(0), _ptr(ws), ws.numel(), _stream(x)),
            "macaq_linear")
     return y
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def linear_noalloc(x: torch.Tensor, a: torch.Tensor | None, b: int, w: Packed, out: torch.Tensor) -> torch.Tensor:
+    """linear() through macaq_linear_noalloc: no workspace, the library's own
+    scratch (128 MiB per GPU); out [M, N] (bf16 or fp32) must be given."""
+    _need_cuda(x, a, w.codes, w.scales, out)
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    assert K == w.K, "activation K %d does not match the weights' %d" % (K, w.K)
+    _check(load_library().macaq_linear_noalloc(_ptr(x), M, K, x.stride(0), _ptr(a), b, _ptr(w.codes), _ptr(w.scales),
+                                               w.rows, _ptr(out), _dtype_code(out.dtype), out.stride(0), _stream(x)),
+           "macaq_linear_noalloc")
+    return out
 
 
 def linear_plain_gemm(a: Packed, w: Packed, out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,

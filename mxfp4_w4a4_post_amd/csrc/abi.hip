@@ -93,6 +93,32 @@ LinearWs linear_ws(int64_t M, int64_t K, size_t extra_bytes) {
   return w;
 }
 
+// Scratch of macaq_linear_noalloc: the quantized activations and split-K
+// partial sums of one call, in device memory the library owns (one copy per
+// GPU, held until the process ends). Host code never uses the array's name
+// as an address: each device's address comes from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+uint8_t* g_scratch_at[kMaxDevices];  // per device, set on its first no-allocation call
+std::mutex g_scratch_mu;
+
+macaq_status scratch_address(uint8_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MACAQ_EUNSUPPORTED, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_at[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MACAQ_EHIP, "hipGetSymbolAddress(scratch) gave no address");
+    g_scratch_at[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_at[dev];
+  return MACAQ_OK;
+}
+
 // Flip-Refinement keeps a row's state in the registers of one workgroup (at most 1024 threads).
 constexpr int64_t kMaxRefineK = 32768;
 
@@ -447,29 +473,33 @@ macaq_status macaq_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t
                      reinterpret_cast<hipStream_t>(stream), who);
 }
 
-macaq_status macaq_linear(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
-                          const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, void* Y, macaq_dtype y_dtype,
-                          int64_t ldy, void* workspace, size_t workspace_bytes, macaq_stream_t stream) {
-  const char* who = "macaq_linear";
+// Argument checks of macaq_linear and its no-allocation variant (workspace
+// aside); MACAQ_OK with *empty set when there is nothing to do.
+static macaq_status linear_check(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
+                                 const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, const void* Y,
+                                 macaq_dtype y_dtype, int64_t ldy, const char* who, bool* empty) {
+  *empty = false;
   macaq_status st = check_quant_shape(M, K, ldx, b, who);
   if (st != MACAQ_OK) return st;
   if (N < 1) return fail(MACAQ_EINVAL, "%s: N < 1", who);
-  if (M == 0) return MACAQ_OK;
+  if (M == 0) {
+    *empty = true;
+    return MACAQ_OK;
+  }
   if (!X || !w_codes || !w_scales) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
   if (!operand_fits(M, K) || !operand_fits(N, K)) return fail(MACAQ_EINVAL, "%s: packed operand over 2 GiB", who);
   st = check_out(Y, y_dtype, N, ldy, who);
   if (st != MACAQ_OK) return st;
   if (!aligned(X, 16) || ldx % 8 != 0 || (a && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 16))
     return fail(MACAQ_EALIGN, "%s: X, a, w_codes, w_scales must be 16-byte aligned and ldx a multiple of 8", who);
-  if (M == 0) return MACAQ_OK;
-  const GemmPlan p = plan_gemm(M, N, K);
-  const LinearWs w = linear_ws(M, K, p.partial_bytes);
-  if (!workspace || workspace_bytes < w.total || !aligned(workspace, kWsAlign))
-    return fail(MACAQ_EWORKSPACE, "%s: need %zu workspace bytes, 256-byte aligned", who, w.total);
-  st = check_device();
-  if (st != MACAQ_OK) return st;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return MACAQ_OK;
+}
+
+// Quantize, then the GEMM, with the layout of linear_ws in `ws`.
+static macaq_status linear_enqueue(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
+                                   const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, void* Y,
+                                   macaq_dtype y_dtype, int64_t ldy, uint8_t* ws, const LinearWs& w, hipStream_t s,
+                                   const char* who) {
   QuantArgs q{};
   q.x = X;
   q.M = M;
@@ -481,9 +511,47 @@ macaq_status macaq_linear(const void* X, int64_t M, int64_t K, int64_t ldx, cons
   q.tiled = true;
   q.kpad = pad_k(K);
   hipError_t e = launch_quant_rows(q, b, false, s);
-  if (e != hipSuccess) return hip_fail(e, "macaq_linear quantize launch");
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return gemm_common(q.codes, q.scales, M, K, w_codes, w_scales, N, Y, y_dtype, ldy,
                      reinterpret_cast<float*>(ws + w.extra_off), s, who);
+}
+
+macaq_status macaq_linear(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
+                          const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, void* Y, macaq_dtype y_dtype,
+                          int64_t ldy, void* workspace, size_t workspace_bytes, macaq_stream_t stream) {
+  const char* who = "macaq_linear";
+  bool empty;
+  macaq_status st = linear_check(X, M, K, ldx, a, b, w_codes, w_scales, N, Y, y_dtype, ldy, who, &empty);
+  if (st != MACAQ_OK || empty) return st;
+  const LinearWs w = linear_ws(M, K, plan_gemm(M, N, K).partial_bytes);
+  if (!workspace || workspace_bytes < w.total || !aligned(workspace, kWsAlign))
+    return fail(MACAQ_EWORKSPACE, "%s: need %zu workspace bytes, 256-byte aligned", who, w.total);
+  st = check_device();
+  if (st != MACAQ_OK) return st;
+  return linear_enqueue(X, M, K, ldx, a, b, w_codes, w_scales, N, Y, y_dtype, ldy, static_cast<uint8_t*>(workspace),
+                        w, reinterpret_cast<hipStream_t>(stream), who);
+}
+
+macaq_status macaq_linear_noalloc(const void* X, int64_t M, int64_t K, int64_t ldx, const float* a, int32_t b,
+                                  const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, void* Y,
+                                  macaq_dtype y_dtype, int64_t ldy, macaq_stream_t stream) {
+  const char* who = "macaq_linear_noalloc";
+  bool empty;
+  macaq_status st = linear_check(X, M, K, ldx, a, b, w_codes, w_scales, N, Y, y_dtype, ldy, who, &empty);
+  if (st != MACAQ_OK || empty) return st;
+  const LinearWs w = linear_ws(M, K, plan_gemm(M, N, K).partial_bytes);
+  if (w.total > kScratchBytes)
+    return fail(MACAQ_EWORKSPACE,
+                "%s: M = %lld, K = %lld, N = %lld need %zu bytes of scratch; the library's fixed scratch holds %zu "
+                "(use macaq_linear with a workspace)",
+                who, (long long)M, (long long)K, (long long)N, w.total, kScratchBytes);
+  st = check_device();
+  if (st != MACAQ_OK) return st;
+  uint8_t* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MACAQ_OK) return st;
+  return linear_enqueue(X, M, K, ldx, a, b, w_codes, w_scales, N, Y, y_dtype, ldy, ws, w,
+                        reinterpret_cast<hipStream_t>(stream), who);
 }
 
 size_t macaq_linear_grouped_workspace_size(int64_t T, int32_t E, int64_t K, int64_t N) {
