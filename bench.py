@@ -1,16 +1,19 @@
 """Benchmark of the MACaQ online W4A4 linear layer on one MI355X.
 
-Default workload (the headline): the prefill 8B-shaped layer set, M = 2048
-tokens through (K, N) = (4096, 4096), (4096, 14336), (14336, 4096), Hadamard
-block 32. One step = macaq_linear on each of the three layers (activation
-scale + block-Hadamard + MXFP4 quantize + scaled-FP4 GEMM), bf16 in and out.
-Weights are prepared beforehand (offline). Other workloads (--workload):
-decode-32b (M = 1, 8, 32, 64 through 5120x25600 and 25600x5120), moe-128e
+Default workload (the headline): the large prefill layer pair, M = 8192
+tokens through (K, N) = (8192, 28672) and (28672, 8192), Hadamard block 32
+(blocks 64 and 128 reported alongside as a sweep). One step = macaq_linear
+on each layer (activation scale + block-Hadamard + MXFP4 quantize +
+scaled-FP4 GEMM), bf16 in and out. Weights are prepared beforehand
+(offline). Other workloads (--workload): prefill-8b (M = 2048 through
+4096x4096, 4096x14336, 14336x4096), decode-32b (M = 1, 8, 32, 64 through
+5120x25600 and 25600x5120), moe-128e
 (grouped gate/up and down projections of 4096 tokens routed top-8 over 128
 experts), moe-block (the same 4096 tokens through the whole MoE block:
 routing, gathered gate/up with the SwiGLU epilogue that quantizes the down
 input, down, weighted top-8 combine), prefill-large (M = 8192 through
-8192x28672 and 28672x8192, Hadamard block from --block), refine-8b (offline
+8192x28672 and 28672x8192, Hadamard block from --block; the default),
+refine-8b (offline
 Flip-Refinement of the prefill layers' weights: Hessian of 512 transformed
 calibration rows, up to 64 greedy code moves per weight row), quant-error
 (relative output error of the layer against the exact bf16 product for the
@@ -64,7 +67,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="prefill-8b", choices=sorted(WORKLOADS))
+    p.add_argument("--workload", default="prefill-large", choices=sorted(WORKLOADS))
     p.add_argument("--block", type=int, default=None, help="Hadamard block (default: the workload's first)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -73,6 +76,10 @@ def parse():
     p.add_argument("--gemm-only", default=None, metavar="MxNxK",
                    help="only run the GEMM (macaq_gemm) on random MXFP4 operands of this shape --profile-steps "
                         "times (for counter collection) and exit")
+    p.add_argument("--results", default=None, metavar="FILE",
+                   help="also append the JSON line to FILE (one line per run)")
+    p.add_argument("--no-block-sweep", action="store_true",
+                   help="prefill-large: skip the Hadamard blocks 64 and 128 reported beside the headline block")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="if > 0: only copy a MIB-MiB device buffer 3 times (the known-size reference for the "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -555,6 +562,31 @@ def step_distribution(torch, step, reps, warmup):
     return pick(0.1), pick(0.5), pick(0.9)
 
 
+def overhead_pairs(torch, step, step_plain, reps, warmup):
+    """The fused and the plain step (one HIP graph per operand copy each)
+    replayed alternately, fused then plain, each replay bracketed by its own
+    HIP events: per pair the ratio fused / plain. Returns the ratios' (p10,
+    median, p90) and the medians of both step times, in ms."""
+    gf = [capture(torch, lambda c=c: step(c)) for c in range(ROTATE)]
+    gp = [capture(torch, lambda c=c: step_plain(c)) for c in range(ROTATE)]
+    for i in range(warmup):
+        gf[i % ROTATE].replay()
+        gp[i % ROTATE].replay()
+    pairs = []
+    for i in range(reps):
+        with Timer(torch) as tf:
+            gf[i % ROTATE].replay()
+        with Timer(torch) as tp:
+            gp[i % ROTATE].replay()
+        pairs.append((tf, tp))
+    torch.cuda.synchronize()
+    f = [a.ms() for a, _ in pairs]
+    p = [b.ms() for _, b in pairs]
+    ratios = sorted(x / y for x, y in zip(f, p))
+    pick = lambda v, q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+    return (pick(ratios, 0.1), pick(ratios, 0.5), pick(ratios, 0.9)), pick(sorted(f), 0.5), pick(sorted(p), 0.5)
+
+
 def cpu_baseline(entries, target_s, moe):
     """The oracle (C, fp64 GEMM over codes, as it stands) on a bounded sample
     of the step's rows: rows of every dense layer, or the first experts."""
@@ -776,6 +808,7 @@ def main():
         "hbm_gbs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
         "plain_mxfp4_ms_per_step": round(ms_plain, 5),
         "transform_overhead_pct": round(100 * (ms / ms_plain - 1), 2),
+        "transform_overhead_method": "timed steps of the fused and the plain path, one graph replay each",
         "wall_s_timed": round(wall, 4),
         "timing": "the timed steps in one HIP graph (operand copies cycled, %d copies), HIP events on the launch "
                   "stream" % ROTATE,
@@ -804,10 +837,21 @@ def main():
         out["kernels_ms_per_step"] = {"calls": len(entries), "quant": round(q, 5), "gemm": round(g, 5),
                                       "quant_plain": round(qp, 5), "gemm_plain": round(gp, 5)}
         out["overhead_split_ms"] = {"quantize": round(q - qp, 5), "gemm_on_transformed_codes": round(g - gp, 5)}
-        # the same fused step one step at a time (median and spread), and with
-        # fp32 output (the precision the parity tests compare)
-        p10, p50, p90 = step_distribution(torch, step, max(args.steps, 50), args.warmup)
-        out["step_ms_p10_median_p90"] = [round(p10, 5), round(p50, 5), round(p90, 5)]
+        # the overhead from interleaved single steps: fused, plain, fused,
+        # plain ... (at least 50 pairs), the median of the per-pair ratios
+        # with its spread; it replaces the two-replay figure above
+        reps = max(args.steps, 50)
+        (r10, r50, r90), f50, p50 = overhead_pairs(torch, step, lambda c: step(c, True), reps, args.warmup)
+        out["transform_overhead_pct"] = round(100 * (r50 - 1), 2)
+        out["transform_overhead_p10_p90_pct"] = [round(100 * (r10 - 1), 2), round(100 * (r90 - 1), 2)]
+        out["transform_overhead_method"] = ("median of %d per-pair ratios fused/plain, the two steps replayed "
+                                            "alternately (one graph per operand copy each), HIP events around "
+                                            "each replay" % reps)
+        out["transform_overhead_two_replays_pct"] = round(100 * (ms / ms_plain - 1), 2)
+        out["transform_overhead_kernel_sum_pct"] = round(100 * ((q + g) / (qp + gp) - 1), 2)
+        out["step_ms_median_fused_plain"] = [round(f50, 5), round(p50, 5)]
+        # the same fused step with fp32 output (the precision the parity
+        # tests compare)
         ms32, _ = timed_steps(torch, lambda c: [e.fused_f32(c) for e in entries], args.steps, args.warmup)
         out["fp32_out"] = {"ms_per_step": round(ms32, 5), "tflops": round(flops / (ms32 * 1e-3) / 1e12, 2)}
         gemm_ms = g
@@ -820,12 +864,42 @@ def main():
                                "kernel_source_digest": digest}
         else:
             tf = flops / (gemm_ms * 1e-3) / 1e12
+            kname = ("gemm_wide_kernel (256 x 256 tiles, scaled-FP4 MFMA)" if wl == 5 else
+                     "scaled-FP4 MFMA GEMM (gemm_wide_kernel for 4096 x 14336, gemm_kernel 128 x 256 for the "
+                     "4096-wide layers)")
             out["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP4_TFLOPS,
                                "unit": "TFLOP/s", "frac": round(tf / PEAK_FP4_TFLOPS, 4),
                                "traffic": load_traffic(spec["name"], digest),
-                               "kernel": "gemm_kernel (scaled-FP4 MFMA)",
+                               "kernel": kname,
                                "avg_launch_us": round(1e3 * gemm_ms / len(entries), 3),
                                "kernel_source_digest": digest}
+        if wl == 5 and not args.no_block_sweep:
+            # the other Hadamard blocks of the large prefill workload: the
+            # same layers and plain path, fused step with b = 64 and 128
+            # (the headline's device buffers are released first; the oracle
+            # baseline needs only their host-side cases)
+            import types
+            entries = [types.SimpleNamespace(oracle_case=e.oracle_case) for e in entries]
+            torch.cuda.empty_cache()
+            sweep = {}
+            for bb in [v for v in spec["blocks"] if v != b]:
+                eb, _ = dense_entries(torch, binding, inputs, wl, bb, dev)
+
+                def step_b(c, plain=False, eb=eb):
+                    for e in eb:
+                        (e.plain if plain else e.fused)(c)
+
+                msb, _ = timed_steps(torch, step_b, args.steps, args.warmup)
+                (b10, b50, b90), _, _ = overhead_pairs(torch, step_b, lambda c: step_b(c, True), reps, args.warmup)
+                tfb = flops / (msb * 1e-3) / 1e12
+                sweep["b=%d" % bb] = {"ms_per_step": round(msb, 5), "tflops": round(tfb, 2),
+                                      "pct_mxfp4_peak": round(100 * tfb / PEAK_FP4_TFLOPS, 2),
+                                      "transform_overhead_pct": round(100 * (b50 - 1), 2),
+                                      "transform_overhead_p10_p90_pct": [round(100 * (b10 - 1), 2),
+                                                                         round(100 * (b90 - 1), 2)]}
+                del eb
+                torch.cuda.empty_cache()
+            out["block_sweep"] = sweep
     else:
         calls = [timed_steps(torch, e.fused, 10, 2)[0] for e in entries]
         gb = nbytes / (sum(calls) * 1e-3) / 1e9
@@ -837,7 +911,11 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(entries, args.cpu_seconds, "block" if wl == MOE_BLOCK else moe)
         out["cpu_baseline"]["cpu_model"] = host_cpu_model()
-    print(json.dumps(out), flush=True)
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.results:
+        with open(args.results, "a") as f:
+            f.write(line + "\n")
 
 
 if __name__ == "__main__":
