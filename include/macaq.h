@@ -69,18 +69,25 @@ extern "C" {
 /* Same type as HIP's hipStream_t. */
 typedef struct ihipStream_t* macaq_stream_t;
 
-typedef enum {
+/* Status, element type and layout are plain 32-bit integers with the named
+   values below, so that any value a caller passes is defined behaviour: an
+   unknown dtype or layout is rejected with MACAQ_EINVAL, an unknown status
+   has the text "unknown status". */
+typedef int32_t macaq_status;
+enum {
   MACAQ_OK = 0,
   MACAQ_EINVAL = 1,       /* null pointer, bad size, block or leading dimension */
   MACAQ_EALIGN = 2,       /* pointer or leading dimension not aligned as documented */
   MACAQ_EWORKSPACE = 3,   /* workspace smaller than the *_workspace_size result */
   MACAQ_EUNSUPPORTED = 4, /* current device is not gfx950 */
   MACAQ_EHIP = 5          /* a HIP runtime call failed; see macaq_last_error() */
-} macaq_status;
+};
 
-typedef enum { MACAQ_BF16 = 0, MACAQ_F32 = 1 } macaq_dtype;
+typedef int32_t macaq_dtype;
+enum { MACAQ_BF16 = 0, MACAQ_F32 = 1 };
 
-typedef enum { MACAQ_ROW_MAJOR = 0, MACAQ_GEMM_LAYOUT = 1 } macaq_layout;
+typedef int32_t macaq_layout;
+enum { MACAQ_ROW_MAJOR = 0, MACAQ_GEMM_LAYOUT = 1 };
 
 /* Bytes of the codes / scales of a rows x K operand in MACAQ_GEMM_LAYOUT
    (0 for an empty operand). */
@@ -101,6 +108,18 @@ const char* macaq_last_error(void);
  * use while other threads call the library.
  */
 void macaq_debug_override_arch(const char* arch);
+
+/*
+ * Stress hook for the persistent GEMM launches (macaq_linear, macaq_gemm,
+ * the grouped layer and the MoE calls): with n > 0 each such launch uses at
+ * most n workgroups, so every workgroup walks more tiles, in another order
+ * and another interleaving with the rest; n <= 0 restores the planned grid.
+ * Each output tile is still computed whole by one workgroup in a fixed
+ * order, so results must stay bit-identical: a difference exposes a race
+ * between consecutive tiles of one workgroup. Process-wide, read at each
+ * launch; slower, not for production.
+ */
+void macaq_debug_limit_workgroups(int32_t n);
 
 /*
  * Per-channel scale from calibration activations (the "calibrated

@@ -36,6 +36,7 @@ _SIGNATURES = {
     "macaq_calibrate": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
     "macaq_calibrate_pow": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp]),
     "macaq_debug_override_arch": (None, [ctypes.c_char_p]),
+    "macaq_debug_limit_workgroups": (None, [_i32]),
     "macaq_make_multipliers": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp]),
     "macaq_make_multipliers_device": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
     "macaq_prepare_weights": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, ctypes.c_int, _vp, _vp,
@@ -100,6 +101,17 @@ def load_library():
         if _lib is not None:
             return _lib
         from . import build as _build
+        alt = os.environ.get("MACAQ_LIBRARY")
+        if alt:
+            # another build of the same sources (the sanitized host build of
+            # the CPU tests); loaded as it is
+            lib = ctypes.CDLL(alt)
+            for name, (res, args) in _SIGNATURES.items():
+                f = getattr(lib, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = lib
+            return lib
         if not _build.is_current():
             print("macaq: libmacaq.so is missing or older than its sources; building it", flush=True)
             _build.build()
@@ -118,6 +130,12 @@ def override_arch(arch: str | None):
     """Make the library's device check see `arch` instead of the device
     (None restores the real query): the test hook of macaq.h."""
     load_library().macaq_debug_override_arch(None if arch is None else arch.encode())
+
+
+def limit_workgroups(n: int):
+    """Cap every persistent GEMM launch at n workgroups (n <= 0: the planned
+    grid): the stress hook of macaq.h, for tests; results must not change."""
+    load_library().macaq_debug_limit_workgroups(int(n))
 
 
 def _status_string(status: int) -> str:

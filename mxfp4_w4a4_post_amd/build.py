@@ -81,3 +81,45 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+
+
+# Host code under AddressSanitizer and UndefinedBehaviorSanitizer (each flag
+# applies to the host pass only; device code is built as usual).
+SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g",
+]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime, to preload into a
+    process that loads the sanitized library."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found (%r)" % path)
+    return path
+
+
+def build_sanitized(out: str, jobs: int = 5) -> str:
+    """The same sources as libmacaq.so, host code sanitized, linked to `out`
+    (the objects go beside it). For the CPU tests of the host code: nothing
+    in it is launched."""
+    from concurrent.futures import ThreadPoolExecutor
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"] + SANITIZE_FLAGS + ["-I", INCLUDE, "-I", CSRC]
+
+    def compile_one(src):
+        obj = os.path.join(os.path.dirname(out), os.path.splitext(src)[0] + ".san.o")
+        res = subprocess.run([hipcc()] + flags + ["-c", os.path.join(CSRC, src), "-o", obj],
+                             capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed on %s (%d):\n%s" % (src, res.returncode, res.stderr))
+        return obj
+
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    res = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + SANITIZE_FLAGS + ["-o", out] + objs,
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed (%d):\n%s" % (res.returncode, res.stderr))
+    return out

@@ -313,6 +313,8 @@ void macaq_debug_override_arch(const char* arch) {
   }
 }
 
+void macaq_debug_limit_workgroups(int32_t n) { macaq::set_workgroup_cap(n); }
+
 macaq_status macaq_make_multipliers(const float* s, int64_t K, int32_t b, float* a, float* r) {
   const char* who = "macaq_make_multipliers";
   if (!s || (!a && !r)) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);

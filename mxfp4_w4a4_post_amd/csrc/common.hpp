@@ -117,6 +117,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 // swiglu: the MoE gate/up GEMM with the SwiGLU epilogue (its own tile shape)
 GemmPlan plan_gemm_grouped(int64_t T, int E, int64_t N, int64_t K, bool swiglu = false);
 hipError_t launch_gemm(const GemmArgs& g, const GemmPlan& p, hipStream_t stream);
+// Upper bound on the workgroups of every persistent GEMM launch (0: the
+// planned grid); the stress hook of the tests.
+void set_workgroup_cap(int32_t n);
 hipError_t launch_gemm_grouped(const GemmArgs& g, const GemmPlan& p, hipStream_t stream);
 
 // Exclusive prefix sum of v over a workgroup of NTH threads (Hillis-Steele

@@ -25,6 +25,8 @@
 // LDS access of a wave is 64 consecutive 16-byte (or 4-byte) words.
 #include "mx_lane.hpp"
 
+#include <atomic>
+
 namespace macaq {
 namespace {
 
@@ -1343,6 +1345,18 @@ __global__ __launch_bounds__(256) void splitk_reduce4_kernel(const float* __rest
   }
 }
 
+// Persistent launches take at most g_workgroup_cap workgroups when it is
+// positive. Every persistent kernel strides its tiles by gridDim.x, and the
+// XCD renumbering is a bijection of the tiles for any grid, so a smaller
+// grid only changes which workgroup computes a tile and in what order.
+std::atomic<int32_t> g_workgroup_cap{0};
+
+int64_t persistent_grid(int64_t tiles, int64_t resident) {
+  int64_t grid = tiles < resident ? tiles : resident;
+  const int32_t cap = g_workgroup_cap.load(std::memory_order_relaxed);
+  return (cap > 0 && cap < grid) ? cap : grid;
+}
+
 using CfgM = TileCfg<128, 256, 2, 2>;  // prefill
 using CfgS64 = TileCfg<64, 128, 4, 2, true, 2>;  // decode, M <= 64
 using CfgS32 = TileCfg<32, 128, 4, 2, true, 2>;  // decode, M <= 32
@@ -1356,7 +1370,7 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t stream) {
   const int64_t total = mt * nt * g.splits;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int64_t resident = (int64_t)kNumCu * C::OCC;
-  const int64_t grid = total < resident ? total : resident;
+  const int64_t grid = persistent_grid(total, resident);
   const dim3 gd((unsigned)grid), bd(NT);
   if constexpr (C::DEFER) {
     if (g.splits == 1 && g.y_bf16 && g.vec16_y && g.N % 8 == 0 && g.ldy < kDeferMaxLd) {
@@ -1383,7 +1397,7 @@ hipError_t launch_grouped_cfg(const GemmArgs& g, hipStream_t stream) {
   const int64_t total = g.max_mtiles * nt;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int64_t resident = (int64_t)kNumCu * C::OCC;
-  const int64_t grid = total < resident ? total : resident;
+  const int64_t grid = persistent_grid(total, resident);
   const dim3 gd((unsigned)grid), bd(NT);
   if constexpr (SWIGLU) {
     switch (g.q_b) {
@@ -1418,7 +1432,7 @@ bool wide_output_ok(const GemmArgs& g) {
 hipError_t launch_wide(const GemmArgs& g, hipStream_t stream) {
   const int64_t tiles = ((g.M + WideCfg::BM - 1) / WideCfg::BM) * ((g.N + WideCfg::BN - 1) / WideCfg::BN);
   if (tiles > 0x7FFFFFFF || g.splits != 1 || !wide_output_ok(g)) return hipErrorInvalidValue;
-  const dim3 gd((unsigned)(tiles < kNumCu ? tiles : kNumCu)), bd(NT);
+  const dim3 gd((unsigned)persistent_grid(tiles, kNumCu)), bd(NT);
   if (g.y_bf16) hipLaunchKernelGGL(gemm_wide_kernel<kOutBf16Staged>, gd, bd, 0, stream, g);
   else hipLaunchKernelGGL(gemm_wide_kernel<kOutF32>, gd, bd, 0, stream, g);
   return hipGetLastError();
@@ -1433,6 +1447,8 @@ void set_vec_flags(GemmArgs& g) {
 }
 
 }  // namespace
+
+void set_workgroup_cap(int32_t n) { g_workgroup_cap.store(n > 0 ? n : 0, std::memory_order_relaxed); }
 
 // Bytes a CU would stream in the time a work unit spends starting its
 // pipeline (first loads in flight, nothing consumed yet).

@@ -98,9 +98,10 @@ def _ladder(t, X):
 
 
 def rn_bf16(v):
-    """Round fp64 values to the nearest bf16 (8 significant bits), ties to
-    even, directly (no intermediate fp32 rounding); normal range only."""
-    m, e = np.frexp(np.asarray(v, np.float64))
+    """Round fp64 values to fp32, then to the nearest bf16 (8 significant
+    bits, ties to even), as a device rounds its fp32 result and as the
+    oracle rounds an expert row; normal range only. Both steps are monotone."""
+    m, e = np.frexp(np.asarray(v, np.float64).astype(np.float32).astype(np.float64))
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
 

@@ -52,10 +52,9 @@ def test_rn_bf16_matches_torch(orc):
     import torch
     rng = np.random.default_rng(5)
     v = rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000))
-    # values exactly representable in fp32 round the same directly and via torch
-    v32 = v.astype(np.float32)
-    ref = torch.from_numpy(v32).to(torch.bfloat16).float().numpy().astype(np.float64)
-    assert np.array_equal(rn_bf16(v32.astype(np.float64)), ref)
+    # fp64 values round to fp32 first, then to bf16, as torch does in two steps
+    ref = torch.from_numpy(v).float().to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(rn_bf16(v), ref)
     # ties to even: 1 + 2^-8 lies between 1 and 1 + 2^-7
     assert rn_bf16(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8]))[0] == 1.0
     assert rn_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
