@@ -175,6 +175,15 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// (bf16(lo) | bf16(hi) << 16), each rounded to nearest even (one packed
+// conversion instruction on gfx950).
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -880,12 +889,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(C::OCC, C::O
 // (issued in half 3 of step s-2) come the 20 loads of step s-1 (10 weight,
 // 10 of stage J+2) and the 8 weight loads of halves 0-2 of step s, each half
 // fenced from the next, so vmcnt(28) covers stage J+1 and leaves the weights
-// of steps s+1 and s+2 in flight (in the first two steps of a tile that
-// follows an output, that output's stores sit between them too and are
-// waited for as well). Loads past a tile's range
-// or of rows past the operand go through an empty buffer resource (zeros,
-// no memory traffic) so that every step issues the same loads and the
-// counts hold.
+// of steps s+1 and s+2 in flight (more operations after the stage only make
+// the wait stricter). A tile's first two steps wait with the counter's
+// maximum instead: the previous tile's output stores sit between their
+// stages and the count, so they drain during those steps, and are waited
+// for from step 2 on. Loads past a tile's range or of rows past the operand
+// go through an empty buffer resource (zeros, no memory traffic) so that
+// every step issues the same loads and the counts hold.
 struct WideCfg {
   static constexpr int BM = 256, BN = 256, FM = 8, FN = 2, WN = 64;
   static constexpr int A_CODES = FM * kCodeBlock;    // 32 KiB
@@ -1024,7 +1034,7 @@ struct Wide {
   // Half H of step s (J = s % 4): fragment i feeds its two MFMAs, then is
   // refilled at once with fragment i of the next half step (read about 14
   // MFMAs ahead of its use), so one set of fragment registers serves.
-  template <int J, int H>
+  template <int J, int H, int WAIT, bool FIRST>
   __device__ __forceinline__ void half(int s) {
     constexpr int WS = J % 2;
     constexpr int N_MFMA = WideCfg::FM * WideCfg::FN;
@@ -1033,7 +1043,7 @@ struct Wide {
     constexpr int NHH = H < NH - 1 ? H + 1 : 0;
     if constexpr (H == NH - 1) {
       // stage J+1 complete in every wave, and every read of stage J+3 done
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(WideCfg::kStageWait));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(WAIT));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       read_scales<NS>(asc_next);
@@ -1044,7 +1054,8 @@ struct Wide {
     for (int i = 0; i < WideCfg::FM; ++i) {
 #pragma unroll
       for (int j = 0; j < WideCfg::FN; ++j)
-        acc.v[i][j] = mfma(w[WS].c[j][H], af.c[i], acc.v[i][j], (int)wsc[J][j], (int)asc[i], H);
+        acc.v[i][j] = mfma(w[WS].c[j][H], af.c[i], (FIRST && H == 0) ? v16f{} : acc.v[i][j], (int)wsc[J][j],
+                           (int)asc[i], H);
       af.c[i] = *reinterpret_cast<const v4i*>(nst + i * kCodeBlock);
     }
     if constexpr (H == 0) load_w_scales(wsc[(J + 2) % 4], s + 2);
@@ -1055,19 +1066,28 @@ struct Wide {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  template <int J>
+  template <int J, int WAIT = WideCfg::kStageWait, bool FIRST = false>
   __device__ __forceinline__ void step(int s) {
-    half<J, 0>(s);
-    half<J, 1>(s);
-    half<J, 2>(s);
-    half<J, 3>(s);
+    half<J, 0, WAIT, FIRST>(s);
+    half<J, 1, WAIT, FIRST>(s);
+    half<J, 2, WAIT, FIRST>(s);
+    half<J, 3, WAIT, FIRST>(s);
 #pragma unroll
     for (int i = 0; i < WideCfg::FM; ++i) asc[i] = asc_next[i];
   }
 
-  // Stages 0-2 of the current tile (issued before the previous tile's
-  // output: they hold no registers; the weights follow the output, in
-  // prologue_start).
+  // 32 stores into an empty buffer: before a workgroup's first tile they
+  // stand in for an output, so that every tile starts with the same count
+  // of operations between its stages.
+  __device__ __forceinline__ void empty_stores() {
+    const Rsrc nr = make_rsrc(nullptr, 0);
+    const __attribute__((ext_vector_type(4))) unsigned z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) __builtin_amdgcn_raw_buffer_store_b128(z, nr, 0, 16 * i, 0);
+  }
+
+  // Stages 0-2 of a tile (issued before the previous tile's output: they
+  // hold no registers).
   __device__ __forceinline__ void prologue_loads() {
     load_stage<0>(0);
     __builtin_amdgcn_sched_barrier(0);
@@ -1077,39 +1097,43 @@ struct Wide {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // Weight steps 0 and 1, then stage 0 visible to every wave, its first
-  // fragments read, accumulators cleared. After stage 0 come stages 1 and 2
-  // and weight steps 0 and 1 (10 loads each), with the previous tile's
-  // output stores (at least 32, see epilogue) between them after a tile:
-  // vmcnt(40), or the counter's maximum of 63 then.
-  template <bool AFTER_OUTPUT>
-  __device__ __forceinline__ void prologue_start() {
+  // Weight steps 0 and 1 of a tile, issued right after its stages 0-2 and
+  // before the previous tile's output, so that the first MFMAs, which wait
+  // for these registers, do not also wait for that output's stores (the
+  // counter is in order).
+  __device__ __forceinline__ void first_weights() {
     load_w(w[0], wsc[0], 0);
     __builtin_amdgcn_sched_barrier(0);
     load_w(w[1], wsc[1], 1);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(AFTER_OUTPUT ? 63 : 40));
+  }
+
+  // Stage 0 visible to every wave, its first fragments and scales read.
+  // After stage 0 come stages 1 and 2 and weight steps 0 and 1 (10 loads
+  // each) and at least 32 stores (the previous tile's output, or
+  // empty_stores): at least 72 operations, so the counter's maximum of 63
+  // covers stage 0. The accumulators need no clearing: the tile's first
+  // MFMAs take a zero input.
+  __device__ __forceinline__ void stage0_ready() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frag<0>(af, 0);
     read_scales<0>(asc);
-    if constexpr (!AFTER_OUTPUT) {  // after an output, the epilogue has cleared them
-#pragma unroll
-      for (int i = 0; i < WideCfg::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < WideCfg::FN; ++j) acc.v[i][j] = {};
-    }
   }
 
   // The tile's output, wave w's 256 rows x 64 columns, through buffer
-  // stores into a resource that spans rows [m0, M) from column n0w, so rows
-  // past M fall outside it; a column run past N takes an offset past every
-  // buffer. Needs N % 8 == 0 (bf16: 16-byte runs) or N % 4 == 0 (fp32: 4
-  // consecutive outputs per lane), ldy and Y aligned to match (the launcher
+  // stores into a resource that spans rows [m0, M) from column n0w. A lane's
+  // row and column are both in its VGPR offset (the scalar offset is 0), and
+  // a lane whose row is past M or whose column run is past N takes an offset
+  // past every buffer, so no store depends on whether the range check counts
+  // the scalar offset. Needs N % 8 == 0 (bf16: 16-byte runs) or N % 4 == 0 (fp32:
+  // 4 consecutive outputs per lane), ldy and Y aligned to match (the launcher
   // checks). Fenced per 32-row fragment so the compiler keeps only one
   // fragment's values in flight.
   __device__ __forceinline__ void epilogue(const GemmArgs& g, int64_t m0, int64_t n0w) {
     const int64_t m_lim = g.M - m0;
+    const int m_rows = (int)(m_lim < WideCfg::BM ? m_lim : WideCfg::BM);  // rows of the tile inside M
     const int n_lim = (int)(g.N - n0w < WideCfg::WN ? g.N - n0w : WideCfg::WN);
     constexpr int ES = MODE == kOutBf16Staged ? 2 : 4;
     // a wave whose columns are all past N still issues its stores (into an
@@ -1130,10 +1154,12 @@ struct Wide {
       // dword of a q pair gives lane l columns 16p .. 16p+7 and lane l+32
       // columns 16p+8 .. 16p+15, so each lane stores 16 contiguous bytes.
       const int r = ln & 31, half = ln >> 5;
-      const uint32_t vrow = (uint32_t)(r * ld + half * 16);
 #pragma unroll
       for (int i = 0; i < WideCfg::FM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
+        // (32i + r) * ld < M * ldy * 2 < 2^31 for a row inside M
+        const bool row_in = 32 * i + r < m_rows;
+        const uint32_t vrow = (uint32_t)(32 * i + r) * (uint32_t)ld + (uint32_t)(half * 16);
         // keep the row's accumulators in their AGPRs until here, so the
         // conversion copies out one row at a time
 #pragma unroll
@@ -1146,20 +1172,17 @@ struct Wide {
             uint32_t lo[2], hi[2];  // q = 2p and q = 2p + 1, two dwords each
 #pragma unroll
             for (int d = 0; d < 2; ++d) {
-              lo[d] = f32_to_bf16_rne(a[8 * p + 2 * d]) | (f32_to_bf16_rne(a[8 * p + 2 * d + 1]) << 16);
-              hi[d] = f32_to_bf16_rne(a[8 * p + 4 + 2 * d]) | (f32_to_bf16_rne(a[8 * p + 4 + 2 * d + 1]) << 16);
+              lo[d] = bf16x2_rne(a[8 * p + 2 * d], a[8 * p + 2 * d + 1]);
+              hi[d] = bf16x2_rne(a[8 * p + 4 + 2 * d], a[8 * p + 4 + 2 * d + 1]);
               const auto sw = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
               lo[d] = sw[0];
               hi[d] = sw[1];
             }
             const int col = jn * 32 + 16 * p + 8 * half;  // this lane's first column
-            const uint32_t vo = col < n_lim ? vrow : kOob;
+            const uint32_t vo = row_in && col < n_lim ? vrow + (uint32_t)((jn * 32 + 16 * p) * 2) : kOob;
             const __attribute__((ext_vector_type(4))) unsigned v = {lo[0], lo[1], hi[0], hi[1]};
-            __builtin_amdgcn_raw_buffer_store_b128(v, yr, (int)vo,
-                                                   __builtin_amdgcn_readfirstlane(32 * i * ld + (jn * 32 + 16 * p) * 2),
-                                                   0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, yr, (int)vo, 0, 0);
           }
-          acc.v[i][jn] = {};  // ready for the next tile
         }
       }
     } else {
@@ -1167,19 +1190,19 @@ struct Wide {
 #pragma unroll
       for (int i = 0; i < WideCfg::FM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
+        // (32i + r) * ld < M * ldy * 4 < 2^31 for a row inside M
+        const bool row_in = 32 * i + r < m_rows;
 #pragma unroll
         for (int jn = 0; jn < WideCfg::FN; ++jn)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const v16f& a = acc.v[i][jn];
             const int n = jn * 32 + 8 * q + c4;
-            const uint32_t vo = n < n_lim ? (uint32_t)(r * ld + n * 4) : kOob;
+            const uint32_t vo = row_in && n < n_lim ? (uint32_t)(32 * i + r) * (uint32_t)ld + (uint32_t)(n * 4) : kOob;
             const v4f v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
-                                                   yr, (int)vo, __builtin_amdgcn_readfirstlane(32 * i * ld), 0);
+                                                   yr, (int)vo, 0, 0);
           }
-#pragma unroll
-        for (int jn = 0; jn < WideCfg::FN; ++jn) acc.v[i][jn] = {};  // ready for the next tile
       }
     }
   }
@@ -1212,9 +1235,22 @@ struct Wide {
     tile_origin(g, t, tiles, m0, n0);
     set_tile(g, m0, n0);
     prologue_loads();
-    prologue_start<false>();
+    first_weights();
+    empty_stores();
+    __builtin_amdgcn_sched_barrier(0);
+    stage0_ready();
     for (;;) {
-      for (int s0 = 0; s0 < n; s0 += 4) {
+      // The first four steps are their own code, so the loop's waits are
+      // those of the steady state. In steps 0 and 1 the stage wait is 63:
+      // after stage 1 come stage 2, weight steps 0 and 1 (30), at least 32
+      // stores and 8 loads of step 0 (at least 70 operations); after stage 2
+      // come 20 + 32 + 20 (step 0) + 8 (at least 80). From step 2 on, the
+      // next stage was issued after the stores and the usual count holds.
+      step<0, 63, true>(0);
+      step<1, 63>(1);
+      step<2>(2);
+      step<3>(3);
+      for (int s0 = 4; s0 < n; s0 += 4) {
         step<0>(s0);
         step<1>(s0 + 1);
         step<2>(s0 + 2);
@@ -1223,7 +1259,7 @@ struct Wide {
       // every load still in flight is a zero load past the tile (the last
       // real ones fed its last steps): let them land, so that none holds a
       // register the output reuses; then the next tile's first activation
-      // blocks go out before this tile's output
+      // blocks and weight steps go out before this tile's output
       __builtin_amdgcn_s_waitcnt(kWaitAll);
       const uint32_t tn = t + gridDim.x;
       const int64_t pm0 = m0, pn0 = n0;
@@ -1231,11 +1267,12 @@ struct Wide {
         tile_origin(g, tn, tiles, m0, n0);
         set_tile(g, m0, n0);
         prologue_loads();
+        first_weights();
       }
       epilogue(g, pm0, pn0 + wave * WideCfg::WN);
       if (tn >= tiles) break;
       t = tn;
-      prologue_start<true>();
+      stage0_ready();
     }
     // loads past the last tile write zeros into LDS: let them land before
     // the workgroup's LDS is released
