@@ -14,6 +14,16 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// bf16(lo) | bf16(hi) << 16, each rounded to nearest even (NaN stays NaN):
+// one packed conversion instruction on gfx950.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // E2M1 element code of the MXFP4 format in the MFMA format selectors.
 constexpr int kFmtFp4 = 4;
 

@@ -175,20 +175,6 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-// (bf16(lo) | bf16(hi) << 16), each rounded to nearest even (one packed
-// conversion instruction on gfx950).
-__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
-  const f32x2_t v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 
 template <class C>
 struct Acc {
@@ -215,8 +201,8 @@ __device__ __forceinline__ void store_frags(const Acc<C>& acc, void* base, int64
         if (VEC && (FULL || n + 3 < n_lim)) {
           if constexpr (OUT == 1) {
             uint2 w;
-            w.x = f32_to_bf16_rne(a[4 * q]) | (f32_to_bf16_rne(a[4 * q + 1]) << 16);
-            w.y = f32_to_bf16_rne(a[4 * q + 2]) | (f32_to_bf16_rne(a[4 * q + 3]) << 16);
+            w.x = bf16x2_rne(a[4 * q], a[4 * q + 1]);
+            w.y = bf16x2_rne(a[4 * q + 2], a[4 * q + 3]);
             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + m * ld + n) = w;
           } else {
             *reinterpret_cast<float4*>(static_cast<float*>(base) + m * ld + n) =
@@ -226,7 +212,7 @@ __device__ __forceinline__ void store_frags(const Acc<C>& acc, void* base, int64
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             if (!FULL && n + e >= n_lim) continue;
-            if constexpr (OUT == 1) static_cast<uint16_t*>(base)[m * ld + n + e] = (uint16_t)f32_to_bf16_rne(a[4 * q + e]);
+            if constexpr (OUT == 1) static_cast<uint16_t*>(base)[m * ld + n + e] = (uint16_t)bf16x2_rne(a[4 * q + e], 0.0f);
             else static_cast<float*>(base)[m * ld + n + e] = a[4 * q + e];
           }
         }
@@ -266,8 +252,8 @@ __device__ __forceinline__ void store_bf16_staged(const Acc<C>& acc, uint16_t* y
         const v16f& a = acc.v[i][jn];
         const int n = jn * 32 + 8 * q + 4 * (lane >> 5);
         uint2 w;
-        w.x = f32_to_bf16_rne(a[4 * q]) | (f32_to_bf16_rne(a[4 * q + 1]) << 16);
-        w.y = f32_to_bf16_rne(a[4 * q + 2]) | (f32_to_bf16_rne(a[4 * q + 3]) << 16);
+        w.x = bf16x2_rne(a[4 * q], a[4 * q + 1]);
+        w.y = bf16x2_rne(a[4 * q + 2], a[4 * q + 3]);
         lds_at<uint2>(region, (lane & 31) * PITCH + n * 2) = w;
       }
 #pragma unroll
@@ -592,8 +578,8 @@ struct Pipe {
           const int m = i * 32 + (lane & 31);
           const int n = wave * C::WN + jn * 32 + 8 * q + 4 * (lane >> 5);
           uint2 w;
-          w.x = f32_to_bf16_rne(a[4 * q]) | (f32_to_bf16_rne(a[4 * q + 1]) << 16);
-          w.y = f32_to_bf16_rne(a[4 * q + 2]) | (f32_to_bf16_rne(a[4 * q + 3]) << 16);
+          w.x = bf16x2_rne(a[4 * q], a[4 * q + 1]);
+          w.y = bf16x2_rne(a[4 * q + 2], a[4 * q + 3]);
           lds_at<uint2>(smem, C::OUT_OFF + m * C::OUT_PITCH + n * 2) = w;
         }
     const int64_t m_lim = tc.m_end - tc.m0, n_lim = g.N - tc.n0;
@@ -1342,7 +1328,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   float s = 0.0f;
   for (int k = 0; k < splits; ++k) s += part[(int64_t)k * M * N + i];
   const int64_t m = i / N, n = i - m * N;
-  if (bf16) static_cast<uint16_t*>(y)[m * ldy + n] = (uint16_t)f32_to_bf16_rne(s);
+  if (bf16) static_cast<uint16_t*>(y)[m * ldy + n] = (uint16_t)bf16x2_rne(s, 0.0f);
   else static_cast<float*>(y)[m * ldy + n] = s;
 }
 
@@ -1374,8 +1360,8 @@ __global__ __launch_bounds__(256) void splitk_reduce4_kernel(const float* __rest
   const int64_t m = i / N, n = i - m * N;
   if (bf16) {
     uint2 w;
-    w.x = f32_to_bf16_rne(s.x) | (f32_to_bf16_rne(s.y) << 16);
-    w.y = f32_to_bf16_rne(s.z) | (f32_to_bf16_rne(s.w) << 16);
+    w.x = bf16x2_rne(s.x, s.y);
+    w.y = bf16x2_rne(s.z, s.w);
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + m * ldy + n) = w;
   } else {
     *reinterpret_cast<float4*>(static_cast<float*>(y) + m * ldy + n) = s;

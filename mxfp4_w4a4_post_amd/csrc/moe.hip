@@ -225,11 +225,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int3
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ uint32_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 
 // y[t, c .. c+7] = sum_j w[t, j] * rows[pos[t*k + j], c .. c+7]: one thread
 // per 8 outputs (one 16-byte load per expert row), one workgroup row per token.
@@ -259,14 +254,14 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __rest
     uint16_t* out = static_cast<uint16_t*>(y) + t * ldy + c;
     if constexpr (VEC) {
       uint4 v;
-      v.x = to_bf16(acc[0]) | (to_bf16(acc[1]) << 16);
-      v.y = to_bf16(acc[2]) | (to_bf16(acc[3]) << 16);
-      v.z = to_bf16(acc[4]) | (to_bf16(acc[5]) << 16);
-      v.w = to_bf16(acc[6]) | (to_bf16(acc[7]) << 16);
+      v.x = bf16x2_rne(acc[0], acc[1]);
+      v.y = bf16x2_rne(acc[2], acc[3]);
+      v.z = bf16x2_rne(acc[4], acc[5]);
+      v.w = bf16x2_rne(acc[6], acc[7]);
       *reinterpret_cast<uint4*>(out) = v;
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) out[i] = (uint16_t)to_bf16(acc[i]);
+      for (int i = 0; i < 8; ++i) out[i] = (uint16_t)bf16x2_rne(acc[i], 0.0f);
     }
   } else {
     float* out = static_cast<float*>(y) + t * ldy + c;
