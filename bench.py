@@ -105,6 +105,15 @@ class Timer:
         return self.s.elapsed_time(self.e)
 
 
+def emit(args, out):
+    """Print the result line, and append it to --results when given."""
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.results:
+        with open(args.results, "a") as f:
+            f.write(line + "\n")
+
+
 def source_digest(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -356,7 +365,7 @@ def refine_main(args, torch, binding, inputs, dev):
                                    kind="oracle",
                                    sample="Hessian of %d rows at K=%d (%.1f s) and the refinement of %d weight rows "
                                           "(%.1f s), single-threaded C" % (hrows, K, th, rows, tr))
-    print(json.dumps(out), flush=True)
+    emit(args, out)
 
 
 def quant_error_main(args, torch, binding, inputs, dev):
@@ -412,7 +421,7 @@ def quant_error_main(args, torch, binding, inputs, dev):
                                    cores=threads, kind="oracle",
                                    sample="%d rows of the prefill recipe's layer (quantize + fp64 GEMM over codes), "
                                           "%.1f s" % (rows, dt))
-    print(json.dumps(out), flush=True)
+    emit(args, out)
 
 
 def prepare_stream_main(args, torch, binding, inputs, dev):
@@ -498,7 +507,7 @@ def prepare_stream_main(args, torch, binding, inputs, dev):
         res["cpu_baseline"] = dict(value=round(wb.size * 2 / dt / 1e9, 4), unit="GB/s of bf16 weights", cores=1,
                                    kind="oracle", sample="256 rows of a 4096 x 4096 layer (calibrate, multipliers, "
                                                          "prepare), %.2f s" % dt)
-    print(json.dumps(res), flush=True)
+    emit(args, res)
 
 
 def capture(torch, fn):
@@ -911,11 +920,7 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(entries, args.cpu_seconds, "block" if wl == MOE_BLOCK else moe)
         out["cpu_baseline"]["cpu_model"] = host_cpu_model()
-    line = json.dumps(out)
-    print(line, flush=True)
-    if args.results:
-        with open(args.results, "a") as f:
-            f.write(line + "\n")
+    emit(args, out)
 
 
 if __name__ == "__main__":
