@@ -31,7 +31,12 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ off, in
 }
 
 // One lane per MX group: a workgroup covers one block of the GEMM layout (32
-// rows x 256 elements); lane (r, c) = (tid / 8, tid % 8) owns elements
+// rows x 256 elements). Consecutive workgroups take consecutive k-blocks of
+// the same 32 rows (a one-dimensional grid, k-block fastest), so neighbouring
+// workgroups read consecutive pieces of each row and write consecutive blocks
+// of the GEMM layout; with the row block fastest instead, the same kernel
+// reads and writes 16-57 KB apart and runs 8-24% slower on 8192-row inputs.
+// Lane (r, c) = (tid / 8, tid % 8) owns elements
 // [32c, 32c + 32) of row r of the block. Butterflies of span 1 .. 16 stay in
 // the lane; spans 32 and 64 (Hadamard blocks of 64 and 128) pair the lanes of
 // chunks c ^ 1 and c ^ 2 of the same row. Eight lanes of a row load 512
@@ -44,8 +49,10 @@ template <bool F32_IN, int B, bool SCALE, bool GROUPED, bool TILED>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
   const int tid = threadIdx.x;
   const int c = tid & 7;
-  const int64_t row = (int64_t)blockIdx.x * kGroupRows + (tid >> 3);
-  const int64_t k0 = (int64_t)blockIdx.y * kBlockK + c * 32;
+  const int64_t nkb = q.kpad / kBlockK;
+  const int64_t rb = (int64_t)blockIdx.x / nkb, kb = (int64_t)blockIdx.x - rb * nkb;
+  const int64_t row = rb * kGroupRows + (tid >> 3);
+  const int64_t k0 = kb * kBlockK + c * 32;
   const bool valid = row < q.M && k0 < q.K;
 
   // the row's raw values first, so their loads are in flight while the
@@ -72,14 +79,14 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
     const float* mrow = q.mult;
     staged = true;
     if constexpr (GROUPED) {
-      const int64_t r0 = (int64_t)blockIdx.x * kGroupRows;
+      const int64_t r0 = rb * kGroupRows;
       const int64_t r1 = (r0 + kGroupRows - 1 < q.M ? r0 + kGroupRows - 1 : q.M - 1);
       const int e0 = expert_of_row(q.offsets, q.E, r0 < q.M ? r0 : q.M - 1);
       staged = e0 == expert_of_row(q.offsets, q.E, r1);
       mrow += (int64_t)e0 * q.K;
     }
     if (staged) {
-      const int64_t kk = (int64_t)blockIdx.y * kBlockK + tid;
+      const int64_t kk = kb * kBlockK + tid;
       msh[tid] = kk < q.K ? mrow[kk] : 0.0f;
       __syncthreads();
     }
@@ -211,8 +218,8 @@ hipError_t launch_one(const QuantArgs& q, hipStream_t stream) {
   // tiled: cover the padded rows and K; row-major: just M x K
   const int64_t rows = TILED ? pad_rows(q.M) : q.M;
   const int64_t gx = (rows + kGroupRows - 1) / kGroupRows, gy = q.kpad / kBlockK;
-  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((quant_rows_kernel<F32_IN, B, SCALE, GROUPED, TILED>), dim3((unsigned)gx, (unsigned)gy),
+  if (gx * gy > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((quant_rows_kernel<F32_IN, B, SCALE, GROUPED, TILED>), dim3((unsigned)(gx * gy)),
                      dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
