@@ -55,41 +55,68 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
   const int64_t k0 = kb * kBlockK + c * 32;
   const bool valid = row < q.M && k0 < q.K;
 
-  // the row's raw values first, so their loads are in flight while the
-  // multipliers are staged
-  uint4 raw[F32_IN ? 8 : 4];
-  if (valid) {
-    int64_t src = row;
-    if (q.gather) {  // MoE rows read their token's activations
-      src = q.gather[row];
-      src = src < 0 ? 0 : (src >= q.src_rows ? q.src_rows - 1 : src);
-    }
-    const uint4* p = F32_IN ? reinterpret_cast<const uint4*>(static_cast<const float*>(q.x) + src * q.ldx + k0)
-                            : reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.x) + src * q.ldx + k0);
-#pragma unroll
-    for (int i = 0; i < (F32_IN ? 8 : 4); ++i) raw[i] = p[i];
+  // Load order matters: the vector-memory counter completes in issue order,
+  // so a wait for a load also waits for every load issued before it. The
+  // small loads that the block's barriers depend on (the MoE gather index
+  // and expert offsets, the multipliers) therefore go out before the rows'
+  // values, and the barriers wait for them only, not for the rows.
+  int64_t src = row < q.M ? row : q.M - 1;  // lanes past M read a row inside it
+  if (q.gather) {  // MoE rows read their token's activations
+    src = q.gather[src];
+    src = src < 0 ? 0 : (src >= q.src_rows ? q.src_rows - 1 : src);
   }
-
-  // the block's 256 multipliers are shared by its 32 rows: stage them in LDS
-  // once. MoE rows take their expert's multipliers; a block whose rows span
-  // two experts (rows are expert-major) has each lane read its own.
+  // The block's 256 multipliers are shared by its 32 rows: staged in LDS
+  // once. MoE rows take their expert's multipliers (the expert offsets are
+  // searched in LDS when they fit, else where they are); a block whose rows
+  // span two experts (rows are expert-major) has each lane read its own.
   __shared__ __attribute__((aligned(16))) float msh[kBlockK];
+  __shared__ int32_t offs[GROUPED ? kMaxExperts + 1 : 1];
   bool staged = false;
+  int e_lane = 0;  // grouped, not staged: this lane's expert
+  float mval = 0.0f;
   if constexpr (SCALE) {
     const float* mrow = q.mult;
     staged = true;
     if constexpr (GROUPED) {
       const int64_t r0 = rb * kGroupRows;
       const int64_t r1 = (r0 + kGroupRows - 1 < q.M ? r0 + kGroupRows - 1 : q.M - 1);
-      const int e0 = expert_of_row(q.offsets, q.E, r0 < q.M ? r0 : q.M - 1);
-      staged = e0 == expert_of_row(q.offsets, q.E, r1);
+      const int64_t rr = row < q.M ? row : q.M - 1;
+      int e0, e1;
+      if (q.E <= kMaxExperts) {  // uniform
+        for (int i = tid; i <= q.E; i += kThreads) offs[i] = q.offsets[i];
+        __syncthreads();
+        e0 = expert_of_row(offs, q.E, r0 < q.M ? r0 : q.M - 1);
+        e1 = expert_of_row(offs, q.E, r1);
+        if (e0 != e1) e_lane = expert_of_row(offs, q.E, rr);
+      } else {
+        e0 = expert_of_row(q.offsets, q.E, r0 < q.M ? r0 : q.M - 1);
+        e1 = expert_of_row(q.offsets, q.E, r1);
+        if (e0 != e1) e_lane = expert_of_row(q.offsets, q.E, rr);
+      }
+      staged = e0 == e1;
       mrow += (int64_t)e0 * q.K;
     }
     if (staged) {
       const int64_t kk = kb * kBlockK + tid;
-      msh[tid] = kk < q.K ? mrow[kk] : 0.0f;
-      __syncthreads();
+      mval = kk < q.K ? mrow[kk] : 0.0f;
     }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the rows' loads after these
+
+  // every lane loads (a lane past K reads elements 0 .. 31 of its row and,
+  // like a lane past M, takes zeros below), so the loads are branch-free and
+  // the waits above count exactly the loads issued after theirs
+  uint4 raw[F32_IN ? 8 : 4];
+  {
+    const int64_t kl = k0 < q.K ? k0 : 0;
+    const uint4* p = F32_IN ? reinterpret_cast<const uint4*>(static_cast<const float*>(q.x) + src * q.ldx + kl)
+                            : reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q.x) + src * q.ldx + kl);
+#pragma unroll
+    for (int i = 0; i < (F32_IN ? 8 : 4); ++i) raw[i] = p[i];
+  }
+  if (SCALE && staged) {
+    msh[tid] = mval;
+    __syncthreads();
   }
 
   float v[32];
@@ -117,18 +144,24 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
       }
     }
     if constexpr (SCALE) {
-      const float4* mp;
-      if (!staged)
-        mp = reinterpret_cast<const float4*>(q.mult + (GROUPED ? (int64_t)expert_of_row(q.offsets, q.E, row) * q.K : 0) + k0);
-      else
-        mp = reinterpret_cast<const float4*>(msh + c * 32);
+      // the multipliers from LDS or (a block across two experts) from memory:
+      // two paths, so each reads its own address space
+      float4 u[8];
+      if (staged) {
+        const float4* mp = reinterpret_cast<const float4*>(msh + c * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[i] = mp[i];
+      } else {
+        const float4* mp = reinterpret_cast<const float4*>(q.mult + (int64_t)e_lane * q.K + k0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[i] = mp[i];
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float4 u = mp[i];
-        v[4 * i] *= u.x;
-        v[4 * i + 1] *= u.y;
-        v[4 * i + 2] *= u.z;
-        v[4 * i + 3] *= u.w;
+        v[4 * i] *= u[i].x;
+        v[4 * i + 1] *= u[i].y;
+        v[4 * i + 2] *= u[i].z;
+        v[4 * i + 3] *= u[i].w;
       }
     }
   } else {
