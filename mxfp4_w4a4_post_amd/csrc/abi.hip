@@ -93,6 +93,15 @@ LinearWs linear_ws(int64_t M, int64_t K, size_t extra_bytes) {
   return w;
 }
 
+// The grouped layer's extra workspace: the tile map, then the expert of each
+// row.
+size_t grouped_map_bytes(int64_t max_mtiles) {
+  return round_up(((size_t)max_mtiles * 2 + 1) * sizeof(int32_t), kWsAlign);
+}
+size_t grouped_extra_bytes(int64_t T, int64_t max_mtiles) {
+  return grouped_map_bytes(max_mtiles) + (size_t)T * sizeof(int32_t);
+}
+
 // Scratch of macaq_linear_noalloc: the quantized activations and split-K
 // partial sums of one call, in device memory the library owns (one copy per
 // GPU, held until the process ends). Host code never uses the array's name
@@ -143,11 +152,12 @@ macaq_status check_out(const void* Y, macaq_dtype dt, int64_t N, int64_t ldy, co
   return MACAQ_OK;
 }
 
-// Workspace of the MoE calls, R = T*k rows: routing arrays and the routing
-// counts, the tile map of the grouped GEMMs, the gathered gate/up input, the
+// Workspace of the MoE calls, R = T*k rows: routing arrays (with the
+// expert of each row) and the routing counts, the tile map of the grouped GEMMs, the gathered gate/up input, the
 // down input and the bf16 expert rows.
 struct MoeWs {
-  size_t offsets, row_token, pos, counts, map, map2, agu_codes, agu_scales, dn_codes, dn_scales, rows, total;
+  size_t offsets, row_token, row_expert, pos, counts, map, map2, agu_codes, agu_scales, dn_codes, dn_scales, rows,
+      total;
   int64_t max_mtiles;
 };
 
@@ -167,6 +177,7 @@ MoeWs moe_ws(int64_t T, int32_t k, int32_t E, int64_t H, int64_t F) {
   };
   w.offsets = take((size_t)(E + 1) * 4);
   w.row_token = take((size_t)R * 4);
+  w.row_expert = take((size_t)R * 4);
   w.pos = take((size_t)R * 4);
   w.counts = take(route_counts_bytes(R, E));
   w.map = take(((size_t)w.max_mtiles * 2 + 1) * 4);
@@ -199,16 +210,22 @@ hipError_t moe_gate_up_launch(const void* X, int64_t T, int64_t H, int64_t ldx, 
                               const int32_t* offsets, int32_t E, const float* a_gu, int32_t b,
                               const uint8_t* wgu_codes, const uint8_t* wgu_scales, int64_t F, const float* a_dn,
                               uint8_t* dn_codes, uint8_t* dn_scales, uint8_t* ws, const MoeWs& w, int32_t* map,
-                              bool build_map, hipStream_t s) {
+                              bool routed_here, hipStream_t s) {
   const int64_t R = T * k;
+  // the expert of each row: written by the routing when it ran in this call,
+  // else from the offsets
+  int32_t* row_expert = reinterpret_cast<int32_t*>(ws + w.row_expert);
+  if (a_gu && !routed_here) {
+    const hipError_t e = launch_row_expert(offsets, E, R, row_expert, s);
+    if (e != hipSuccess) return e;
+  }
   QuantArgs q{};
   q.x = X;
   q.M = R;
   q.K = H;
   q.ldx = ldx;
   q.mult = a_gu;
-  q.offsets = a_gu ? offsets : nullptr;
-  q.E = E;
+  q.row_expert = a_gu ? row_expert : nullptr;
   q.codes = ws + w.agu_codes;
   q.scales = ws + w.agu_scales;
   q.tiled = true;
@@ -230,7 +247,7 @@ hipError_t moe_gate_up_launch(const void* X, int64_t T, int64_t H, int64_t ldx, 
   g.tile_map = map;
   g.E = E;
   g.max_mtiles = w.max_mtiles;
-  g.map_ready = !build_map;
+  g.map_ready = routed_here;
   g.swiglu = true;
   g.q_codes = dn_codes;
   g.q_scales = dn_scales;
@@ -560,7 +577,7 @@ size_t macaq_linear_grouped_workspace_size(int64_t T, int32_t E, int64_t K, int6
   if (T <= 0 || E < 1 || K <= 0 || N <= 0) return 0;
   const GemmPlan p = plan_gemm_grouped(T, E, N, K);
   const int64_t max_mtiles = (T + p.bm - 1) / p.bm + E;
-  return linear_ws(T, K, ((size_t)max_mtiles * 2 + 1) * sizeof(int32_t)).total;
+  return linear_ws(T, K, grouped_extra_bytes(T, max_mtiles)).total;
 }
 
 macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t E, int64_t T, int64_t K,
@@ -588,17 +605,21 @@ macaq_status macaq_linear_grouped(const void* X, const int32_t* offsets, int32_t
   if (st != MACAQ_OK) return st;
   const GemmPlan p = plan_gemm_grouped(T, E, N, K);
   const int64_t max_mtiles = (T + p.bm - 1) / p.bm + E;
-  const LinearWs w = linear_ws(T, K, ((size_t)max_mtiles * 2 + 1) * sizeof(int32_t));
+  const LinearWs w = linear_ws(T, K, grouped_extra_bytes(T, max_mtiles));
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t* row_expert = reinterpret_cast<int32_t*>(ws + w.extra_off + grouped_map_bytes(max_mtiles));
+  if (a) {
+    const hipError_t e = launch_row_expert(offsets, E, T, row_expert, s);
+    if (e != hipSuccess) return hip_fail(e, "macaq_linear_grouped row experts launch");
+  }
   QuantArgs q{};
   q.x = X;
   q.M = T;
   q.K = K;
   q.ldx = K;
   q.mult = a;
-  q.offsets = a ? offsets : nullptr;
-  q.E = E;
+  q.row_expert = a ? row_expert : nullptr;
   q.codes = ws + w.codes_off;
   q.scales = ws + w.scales_off;
   q.tiled = true;
@@ -652,7 +673,8 @@ macaq_status macaq_moe_route(const int32_t* ids, int64_t T, int32_t k, int32_t E
   macaq_status st = check_device();
   if (st != MACAQ_OK) return st;
   hipError_t e = launch_moe_route(ids, T, k, E, offsets, row_token, pos, static_cast<int32_t*>(workspace),
-                                  RouteMaps{{nullptr, nullptr}, {0, 0}, 0}, reinterpret_cast<hipStream_t>(stream));
+                                  RouteMaps{{nullptr, nullptr}, {0, 0}, 0}, nullptr,
+                                  reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_route launch");
 }
 
@@ -680,7 +702,7 @@ macaq_status macaq_moe_gate_up(const void* X, int64_t T, int64_t H, int64_t ldx,
   if (st != MACAQ_OK) return st;
   hipError_t e = moe_gate_up_launch(X, T, H, ldx, k, row_token, offsets, E, a_gu, b, wgu_codes, wgu_scales, F, a_dn,
                                     dn_codes, dn_scales, static_cast<uint8_t*>(workspace), w,
-                                    reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + w.map), true,
+                                    reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + w.map), false,
                                     reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_moe_gate_up launch");
 }
@@ -749,10 +771,11 @@ macaq_status macaq_moe_block(const void* X, int64_t T, int64_t H, int64_t ldx, c
   int32_t* map_dn = bm_dn == bm_gu ? map_gu : reinterpret_cast<int32_t*>(ws + w.map2);
   const RouteMaps maps{{map_gu, bm_dn == bm_gu ? nullptr : map_dn}, {bm_gu, bm_dn}, w.max_mtiles};
   hipError_t e =
-      launch_moe_route(ids, T, k, E, offsets, row_token, pos, reinterpret_cast<int32_t*>(ws + w.counts), maps, s);
+      launch_moe_route(ids, T, k, E, offsets, row_token, pos, reinterpret_cast<int32_t*>(ws + w.counts), maps,
+                       reinterpret_cast<int32_t*>(ws + w.row_expert), s);
   if (e != hipSuccess) return hip_fail(e, "macaq_moe_block routing launch");
   e = moe_gate_up_launch(X, T, H, ldx, k, row_token, offsets, E, a_gu, b, wgu_codes, wgu_scales, F, a_dn,
-                         ws + w.dn_codes, ws + w.dn_scales, ws, w, map_gu, false, s);
+                         ws + w.dn_codes, ws + w.dn_scales, ws, w, map_gu, true, s);
   if (e != hipSuccess) return hip_fail(e, "macaq_moe_block gate/up launch");
   e = moe_down_combine_launch(ws + w.dn_codes, ws + w.dn_scales, offsets, pos, w_route, T, k, E, wdn_codes,
                               wdn_scales, H, F, Y, y_dtype, ldy, ws, w, map_dn, false, s);

@@ -69,8 +69,7 @@ struct QuantArgs {
   const void* x;         // bf16 or fp32 rows [M, ldx]
   int64_t M, K, ldx;
   const float* mult;     // [K] or [E, K] (grouped); nullptr = no multiply
-  const int32_t* offsets;  // grouped only: [E+1], rows of expert e
-  int E;
+  const int32_t* row_expert;  // grouped only: [M], the expert of each row (its multipliers' row)
   uint8_t* codes;        // [M, K/2] row-major, or the GEMM layout
   uint8_t* scales;       // [M, K/32] row-major, or the GEMM layout
   bool tiled;            // write the GEMM layout (with its zero padding)
@@ -85,6 +84,9 @@ hipError_t launch_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx,
 hipError_t launch_multipliers(const float* s, int64_t K, float cb, float* a, float* r, hipStream_t stream);
 // x_is_f32: input rows are fp32 (weights) instead of bf16.
 hipError_t launch_quant_rows(const QuantArgs& q, int b, bool x_is_f32, hipStream_t stream);
+// out[r] = the expert of row r of an expert-major row set (the largest e < E
+// with off[e] <= r), for rows r in [0, rows).
+hipError_t launch_row_expert(const int32_t* off, int E, int64_t rows, int32_t* out, hipStream_t stream);
 
 struct GemmArgs {
   const uint8_t* a_codes;   // GEMM layout, M rows (T rows when grouped)
@@ -164,8 +166,10 @@ struct RouteMaps {
   int bm[2];
   int64_t max_mtiles;
 };
+// row_expert (optional, [T*k]): the expert of each row, E - 1 past the routed rows.
 hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
-                            int32_t* pos, int32_t* counts, const RouteMaps& maps, hipStream_t stream);
+                            int32_t* pos, int32_t* counts, const RouteMaps& maps, int32_t* row_expert,
+                            hipStream_t stream);
 hipError_t launch_moe_combine(const uint16_t* rows, int64_t H, const int32_t* pos, const float* w, int64_t T, int k,
                               void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
 

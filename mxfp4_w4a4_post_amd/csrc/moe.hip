@@ -128,7 +128,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int3
                                                                       int k, int E, const int32_t* __restrict__ counts,
                                                                       int G, int32_t* __restrict__ offsets,
                                                                       int32_t* __restrict__ row_token,
-                                                                      int32_t* __restrict__ pos, RouteMaps m) {
+                                                                      int32_t* __restrict__ pos, RouteMaps m,
+                                                                      int32_t* __restrict__ row_expert) {
   __shared__ int base[kMaxExperts];   // first row of this chunk's entries of e
   __shared__ int first[kMaxExperts];  // expert totals, then the sorted place of e's first entry
   __shared__ int offs[kMaxExperts];   // offsets[e]
@@ -216,11 +217,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int3
       const int row = base[key] + (4 * tid + s - first[key]);
       pos[i] = row;
       row_token[row] = (int32_t)((uint32_t)i / (uint32_t)k);
+      if (row_expert) row_expert[row] = key;
     } else if (key == E) {
       pos[i] = -1;
     }
   }
-  for (int64_t r = routed + (int64_t)g * kRouteThreads + tid; r < n; r += (int64_t)G * kRouteThreads) row_token[r] = 0;
+  // rows past the routed ones: token 0, and the expert a search of the
+  // offsets gives them (the last)
+  for (int64_t r = routed + (int64_t)g * kRouteThreads + tid; r < n; r += (int64_t)G * kRouteThreads) {
+    row_token[r] = 0;
+    if (row_expert) row_expert[r] = E - 1;
+  }
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -280,13 +287,14 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __rest
 int64_t moe_route_chunks(int64_t n) { return n > 0 ? (n + kRouteChunk - 1) / kRouteChunk : 1; }
 
 hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
-                            int32_t* pos, int32_t* counts, const RouteMaps& maps, hipStream_t stream) {
+                            int32_t* pos, int32_t* counts, const RouteMaps& maps, int32_t* row_expert,
+                            hipStream_t stream) {
   const int64_t n = T * k, G = moe_route_chunks(n);
   hipLaunchKernelGGL(route_count_kernel, dim3((unsigned)G), dim3(kRouteThreads), 0, stream, ids, n, E, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)G), dim3(kRouteThreads), 0, stream, ids, n, k, E, counts,
-                     (int)G, offsets, row_token, pos, maps);
+                     (int)G, offsets, row_token, pos, maps, row_expert);
   return hipGetLastError();
 }
 

@@ -57,20 +57,19 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
 
   // Load order matters: the vector-memory counter completes in issue order,
   // so a wait for a load also waits for every load issued before it. The
-  // small loads that the block's barriers depend on (the MoE gather index
-  // and expert offsets, the multipliers) therefore go out before the rows'
-  // values, and the barriers wait for them only, not for the rows.
+  // small loads that the block's barrier depends on (the MoE gather index,
+  // the row experts, the multipliers) therefore go out before the rows'
+  // values, and the barrier waits for them only, not for the rows.
   int64_t src = row < q.M ? row : q.M - 1;  // lanes past M read a row inside it
   if (q.gather) {  // MoE rows read their token's activations
     src = q.gather[src];
     src = src < 0 ? 0 : (src >= q.src_rows ? q.src_rows - 1 : src);
   }
   // The block's 256 multipliers are shared by its 32 rows: staged in LDS
-  // once. MoE rows take their expert's multipliers (the expert offsets are
-  // searched in LDS when they fit, else where they are); a block whose rows
-  // span two experts (rows are expert-major) has each lane read its own.
+  // once. Grouped rows take their expert's multipliers (the experts of the
+  // block's first and last rows are uniform loads; a block whose rows span
+  // two experts (rows are expert-major) has each lane read its own).
   __shared__ __attribute__((aligned(16))) float msh[kBlockK];
-  __shared__ int32_t offs[GROUPED ? kMaxExperts + 1 : 1];
   bool staged = false;
   int e_lane = 0;  // grouped, not staged: this lane's expert
   float mval = 0.0f;
@@ -80,20 +79,9 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
     if constexpr (GROUPED) {
       const int64_t r0 = rb * kGroupRows;
       const int64_t r1 = (r0 + kGroupRows - 1 < q.M ? r0 + kGroupRows - 1 : q.M - 1);
-      const int64_t rr = row < q.M ? row : q.M - 1;
-      int e0, e1;
-      if (q.E <= kMaxExperts) {  // uniform
-        for (int i = tid; i <= q.E; i += kThreads) offs[i] = q.offsets[i];
-        __syncthreads();
-        e0 = expert_of_row(offs, q.E, r0 < q.M ? r0 : q.M - 1);
-        e1 = expert_of_row(offs, q.E, r1);
-        if (e0 != e1) e_lane = expert_of_row(offs, q.E, rr);
-      } else {
-        e0 = expert_of_row(q.offsets, q.E, r0 < q.M ? r0 : q.M - 1);
-        e1 = expert_of_row(q.offsets, q.E, r1);
-        if (e0 != e1) e_lane = expert_of_row(q.offsets, q.E, rr);
-      }
-      staged = e0 == e1;
+      const int e0 = q.row_expert[r0 < q.M ? r0 : q.M - 1];
+      staged = e0 == q.row_expert[r1];
+      if (!staged) e_lane = q.row_expert[row < q.M ? row : q.M - 1];
       mrow += (int64_t)e0 * q.K;
     }
     if (staged) {
@@ -180,6 +168,22 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
   } else if (valid) {
     *reinterpret_cast<uint4*>(q.codes + row * (q.K >> 1) + (k0 >> 1)) = out;
     q.scales[row * (q.K >> 5) + (k0 >> 5)] = (uint8_t)sc;
+  }
+}
+
+// One thread per row: the expert offsets in LDS when they fit (one parallel
+// load per workgroup), then a binary search.
+__global__ __launch_bounds__(kThreads) void row_expert_kernel(const int32_t* __restrict__ off, int E, int64_t rows,
+                                                              int32_t* __restrict__ out) {
+  __shared__ int32_t offs[kMaxExperts + 1];
+  const int tid = threadIdx.x;
+  const int64_t r = (int64_t)blockIdx.x * kThreads + tid;
+  if (E <= kMaxExperts) {  // uniform
+    for (int i = tid; i <= E; i += kThreads) offs[i] = off[i];
+    __syncthreads();
+    if (r < rows) out[r] = expert_of_row(offs, E, r);
+  } else if (r < rows) {
+    out[r] = expert_of_row(off, E, r);
   }
 }
 
@@ -271,7 +275,7 @@ hipError_t launch_b(const QuantArgs& q, int b, hipStream_t stream) {
 template <bool TILED>
 hipError_t launch_layout(const QuantArgs& q, int b, bool x_is_f32, hipStream_t stream) {
   const bool scale = q.mult != nullptr;
-  const bool grouped = q.offsets != nullptr;
+  const bool grouped = q.row_expert != nullptr;
   if (x_is_f32) {
     if (grouped) return hipErrorInvalidValue;
     return scale ? launch_b<true, true, false, TILED>(q, b, stream) : launch_b<true, false, false, TILED>(q, b, stream);
@@ -286,6 +290,14 @@ hipError_t launch_layout(const QuantArgs& q, int b, bool x_is_f32, hipStream_t s
 hipError_t launch_quant_rows(const QuantArgs& q, int b, bool x_is_f32, hipStream_t stream) {
   if (q.M == 0) return hipSuccess;
   return q.tiled ? launch_layout<true>(q, b, x_is_f32, stream) : launch_layout<false>(q, b, x_is_f32, stream);
+}
+
+hipError_t launch_row_expert(const int32_t* off, int E, int64_t rows, int32_t* out, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t blocks = (rows + kThreads - 1) / kThreads;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(row_expert_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, off, E, rows, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_calibrate(const void* xcal, int64_t R, int64_t K, int64_t ldx, int quarters, float* s,
