@@ -257,6 +257,11 @@ def moe_block_entries(torch, binding, inputs, b, dev):
     e.gate_up = lambda c: binding.moe_gate_up(xs[c], k, tok, off, lfs[c].a_gu, b, lfs[c].wgu, lfs[c].a_dn, out=dn,
                                               workspace=work)
     e.down_combine = lambda c: binding.moe_down_combine(dn, off, pos, w, lfs[c].wdn, out=y, workspace=work)
+    # the same parts of the plain MXFP4 block (no multipliers, no Hadamard)
+    dnp = binding.moe_gate_up(xs[0], k, tok, off, lp.a_gu, 0, lp.wgu, lp.a_dn, workspace=work)
+    e.gate_up_plain = lambda c: binding.moe_gate_up(xs[c], k, tok, off, lps[c].a_gu, 0, lps[c].wgu, lps[c].a_dn,
+                                                    out=dnp, workspace=work)
+    e.down_combine_plain = lambda c: binding.moe_down_combine(dnp, off, pos, w, lps[c].wdn, out=y, workspace=work)
     e.parts_bytes = {"gate_up": 2 * R * H + E * 2 * F * H * 17 / 32 + R * F * 17 / 32,
                      "down_combine": R * F * 17 / 32 + E * H * F * 17 / 32 + 2 * R * H * 2 + 2 * T * H}
     e.oracle_case = (case, None)
@@ -816,17 +821,29 @@ def main():
         "tokens_per_s": round(tokens / (ms * 1e-3), 1),
         "hbm_gbs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
         "plain_mxfp4_ms_per_step": round(ms_plain, 5),
-        "transform_overhead_pct": round(100 * (ms / ms_plain - 1), 2),
-        "transform_overhead_method": "timed steps of the fused and the plain path, one graph replay each",
         "wall_s_timed": round(wall, 4),
         "timing": "the timed steps in one HIP graph (operand copies cycled, %d copies), HIP events on the launch "
                   "stream" % ROTATE,
     }
+    # the overhead from interleaved single steps: fused, plain, fused, plain
+    # ... (at least 50 pairs), the median of the per-pair ratios with its
+    # spread; it replaces the two-replay figure above
+    reps = max(args.steps, 50)
+    (r10, r50, r90), f50, p50 = overhead_pairs(torch, step, lambda c: step(c, True), reps, args.warmup)
+    out["transform_overhead_pct"] = round(100 * (r50 - 1), 2)
+    out["transform_overhead_p10_p90_pct"] = [round(100 * (r10 - 1), 2), round(100 * (r90 - 1), 2)]
+    out["transform_overhead_method"] = ("median of %d per-pair ratios fused/plain, the two steps replayed "
+                                        "alternately (one graph per operand copy each), HIP events around "
+                                        "each replay" % reps)
+    out["transform_overhead_two_replays_pct"] = round(100 * (ms / ms_plain - 1), 2)
+    out["step_ms_median_fused_plain"] = [round(f50, 5), round(p50, 5)]
     if wl == MOE_BLOCK:
         e = entries[0]
         parts = {k: timed_steps(torch, getattr(e, k), args.steps, args.warmup)[0]
-                 for k in ("route", "gate_up", "down_combine")}
+                 for k in ("route", "gate_up", "down_combine", "gate_up_plain", "down_combine_plain")}
         out["calls_ms_per_step"] = {k: round(v, 5) for k, v in parts.items()}
+        out["overhead_split_ms"] = {"gate_up": round(parts["gate_up"] - parts["gate_up_plain"], 5),
+                                    "down_combine": round(parts["down_combine"] - parts["down_combine_plain"], 5)}
         gb_step = nbytes / (ms * 1e-3) / 1e9
         gu_gb = e.parts_bytes["gate_up"] / (parts["gate_up"] * 1e-3) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": round(gb_step, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -846,19 +863,7 @@ def main():
         out["kernels_ms_per_step"] = {"calls": len(entries), "quant": round(q, 5), "gemm": round(g, 5),
                                       "quant_plain": round(qp, 5), "gemm_plain": round(gp, 5)}
         out["overhead_split_ms"] = {"quantize": round(q - qp, 5), "gemm_on_transformed_codes": round(g - gp, 5)}
-        # the overhead from interleaved single steps: fused, plain, fused,
-        # plain ... (at least 50 pairs), the median of the per-pair ratios
-        # with its spread; it replaces the two-replay figure above
-        reps = max(args.steps, 50)
-        (r10, r50, r90), f50, p50 = overhead_pairs(torch, step, lambda c: step(c, True), reps, args.warmup)
-        out["transform_overhead_pct"] = round(100 * (r50 - 1), 2)
-        out["transform_overhead_p10_p90_pct"] = [round(100 * (r10 - 1), 2), round(100 * (r90 - 1), 2)]
-        out["transform_overhead_method"] = ("median of %d per-pair ratios fused/plain, the two steps replayed "
-                                            "alternately (one graph per operand copy each), HIP events around "
-                                            "each replay" % reps)
-        out["transform_overhead_two_replays_pct"] = round(100 * (ms / ms_plain - 1), 2)
         out["transform_overhead_kernel_sum_pct"] = round(100 * ((q + g) / (qp + gp) - 1), 2)
-        out["step_ms_median_fused_plain"] = [round(f50, 5), round(p50, 5)]
         # the same fused step with fp32 output (the precision the parity
         # tests compare)
         ms32, _ = timed_steps(torch, lambda c: [e.fused_f32(c) for e in entries], args.steps, args.warmup)

@@ -718,9 +718,17 @@ struct Pipe {
   // The K loop; its last barrier leaves every LDS buffer idle. DEF: step s
   // also writes piece s of the pending output, and the pieces a short tile
   // did not reach follow the loop, fenced from the next staging by a barrier.
-  template <bool DEF = false>
+  // PEEL: the first iteration is its own code, so the loop keeps the steady
+  // state's waits (the compiler's waits at a loop top otherwise also cover
+  // the prologue's pending loads); nsteps is a positive multiple of U.
+  template <bool DEF = false, bool PEEL = false>
   __device__ __forceinline__ void loop() {
-    for (int64_t s0 = 0; s0 < nsteps; s0 += C::U) steps<0, DEF>(s0);
+    int64_t s0 = 0;
+    if constexpr (PEEL) {
+      steps<0, DEF>(0);
+      s0 = C::U;
+    }
+    for (; s0 < nsteps; s0 += C::U) steps<0, DEF>(s0);
     if constexpr (DEF) {
       if (nsteps < C::PIECES_W) {
         flush(nsteps);
@@ -811,7 +819,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& g, int64_t total, uin
   if constexpr (DEF) p.clear_pending();
   for (;;) {
     p.prologue_lds();
-    p.template loop<DEF>();
+    // (grouped kernels: the peeled copy spills registers)
+    p.template loop<DEF, !GROUPED>();
     TileRef nxt;
     int64_t tn = t + gridDim.x;
     while (tn < total && !tile_at<C, GROUPED>(g, xcd_remap(tn, total), nxt)) tn += gridDim.x;
