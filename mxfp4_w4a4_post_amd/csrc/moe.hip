@@ -137,13 +137,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int3
   __shared__ int buf[kRouteChunk];
   __shared__ int sh[4];
   const int tid = threadIdx.x, g = blockIdx.x;
-  // entries of e in earlier chunks and in all chunks
+  // entries of e in earlier chunks and in all chunks: the chunk counts are
+  // loaded 16 at a time (a clamped index, so the loads are unconditional and
+  // all in flight together) and summed in chunk order
   for (int e = tid; e < E; e += kRouteThreads) {
     int bef = 0, tot = 0;
-    for (int c = 0; c < G; ++c) {
-      const int v = counts[(int64_t)c * E + e];
-      tot += v;
-      bef += c < g ? v : 0;
+    for (int c0 = 0; c0 < G; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = counts[(int64_t)(c0 + j < G ? c0 + j : G - 1) * E + e];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int c = c0 + j;
+        const int x = c < G ? v[j] : 0;
+        tot += x;
+        bef += c < g ? x : 0;
+      }
     }
     base[e] = bef;
     first[e] = tot;
