@@ -254,16 +254,29 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __rest
   const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (c >= H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int32_t r = pos[t * k + j];
-    if (r < 0) continue;
-    const float wt = w[t * k + j];
-    const uint4 u = *reinterpret_cast<const uint4*>(rows + (int64_t)r * H + c);
-    const uint32_t q[4] = {u.x, u.y, u.z, u.w};
+  // the token's rows 8 at a time: every load issued before the first is
+  // used (a dropped entry reads row 0 and is skipped), then summed in j order
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    uint4 u[8];
+    bool use[8];
+    float wt[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = __builtin_fmaf(wt, bf16_lo(q[i]), acc[2 * i]);
-      acc[2 * i + 1] = __builtin_fmaf(wt, bf16_hi(q[i]), acc[2 * i + 1]);
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = j0 + jj < k ? j0 + jj : k - 1;
+      const int32_t r = pos[t * k + j];
+      use[jj] = j0 + jj < k && r >= 0;
+      wt[jj] = w[t * k + j];
+      u[jj] = *reinterpret_cast<const uint4*>(rows + (int64_t)(r >= 0 ? r : 0) * H + c);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all loads out before the first sum
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const uint32_t q[4] = {u[jj].x, u[jj].y, u[jj].z, u[jj].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = use[jj] ? __builtin_fmaf(wt[jj], bf16_lo(q[i]), acc[2 * i]) : acc[2 * i];
+        acc[2 * i + 1] = use[jj] ? __builtin_fmaf(wt[jj], bf16_hi(q[i]), acc[2 * i + 1]) : acc[2 * i + 1];
+      }
     }
   }
   if constexpr (BF16) {
