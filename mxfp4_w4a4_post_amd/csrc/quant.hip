@@ -44,9 +44,12 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ off, in
 // GEMM layout (rows r .. r+7 of one chunk), or a row's 128 code bytes in the
 // row-major layout.
 // TILED: write the GEMM layout, including its zero padding; otherwise
-// row-major [M, K/2] codes and [M, K/32] scales.
+// row-major [M, K/2] codes and [M, K/32] scales. The grouped GEMM-layout
+// variants (the MoE inputs) are held to 8 waves per SIMD (59 VGPRs, no
+// spills; left alone they take 68 and run at 7), which hides more of their
+// gathered rows' latency.
 template <bool F32_IN, int B, bool SCALE, bool GROUPED, bool TILED>
-__global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantArgs q) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GROUPED && TILED && !F32_IN ? 8 : 1))) void quant_rows_kernel(QuantArgs q) {
   const int tid = threadIdx.x;
   const int c = tid & 7;
   const int64_t nkb = q.kpad / kBlockK;
