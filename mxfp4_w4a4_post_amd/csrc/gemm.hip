@@ -819,8 +819,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& g, int64_t total, uin
   if constexpr (DEF) p.clear_pending();
   for (;;) {
     p.prologue_lds();
-    // (grouped kernels: the peeled copy spills registers)
-    p.template loop<DEF, !GROUPED>();
+    // (grouped kernels: the peeled copy spills registers, except with the
+    // deferred output)
+    p.template loop<DEF, !GROUPED || DEF>();
     TileRef nxt;
     int64_t tn = t + gridDim.x;
     while (tn < total && !tile_at<C, GROUPED>(g, xcd_remap(tn, total), nxt)) tn += gridDim.x;
