@@ -20,7 +20,9 @@ calibration rows, up to 64 greedy code moves per weight row), quant-error
 calibration variants s = max^(q/4) and Hadamard blocks b in {0, 32, 64, 128}
 on three activation recipes), prepare-stream (weights of 8 blocks of 8B-shaped
 linears prepared from pinned host memory back to pinned host memory with one
-layer resident, copies overlapped with preparation) and tiny.
+layer resident, copies overlapped with preparation), tiny, and peaks (the
+chip's measured ceilings: scaled-FP4 MFMA rate with constant and random
+operands, plain-read and copy bandwidth).
 
 Inputs are resident in HBM; the timed steps rotate through several copies of
 activations and weights so that no step finds its operands in the 256 MB
@@ -50,7 +52,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ROTATE = 4                  # operand copies cycled through by the timed steps
 ORACLE_THREADS_CAP = 16     # one GPU's share of the host CPU
 WORKLOADS = {"tiny": 1, "prefill-8b": 2, "decode-32b": 3, "moe-128e": 4, "prefill-large": 5, "moe-block": 6,
-             "refine-8b": 7, "quant-error": 8, "prepare-stream": 9}
+             "refine-8b": 7, "quant-error": 8, "prepare-stream": 9, "peaks": 10}
+PEAKS = 10  # the chip's measured ceilings: scaled-FP4 MFMA rate and plain-read / copy bandwidth
+MFMA_FLOPS = 2 * 32 * 32 * 64  # one scaled-FP4 MFMA 32x32x64
 PREPARE_STREAM = 9  # offline: a stack of 8B-shaped blocks prepared from pinned host memory, one layer resident
 STREAM_BLOCKS = 8
 BLOCK_SHAPES = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096), (4096, 14336)]
@@ -515,6 +519,85 @@ def prepare_stream_main(args, torch, binding, inputs, dev):
     emit(args, res)
 
 
+def peaks_main(args, torch, binding, dev):
+    """The ceilings the kernels are read against, measured on this device:
+    back-to-back scaled-FP4 MFMAs on register operands (one workgroup of 4
+    waves per CU, 8 independent accumulators per wave) with constant and with
+    random operand bytes, and plain reads of 70 MiB, 470 MiB and 2 GiB (each
+    thread 8 loads of 16 bytes in flight, inputs rotated past the 256 MB
+    last-level cache) at several grid sizes, and a device copy of 512 MiB;
+    the reads and the copy are timed over back-to-back launches, as a layer's
+    launches follow one another in a step."""
+    import statistics
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    nops = binding.MFMA_PROBE_OPERAND_BYTES
+    operands = {"constant": torch.full((nops,), 0x22, dtype=torch.uint8, device=dev),  # E2M1 1.0 in each nibble
+                "random": torch.randint(0, 256, (nops,), dtype=torch.uint8, device=dev, generator=gen)}
+    out = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    iters = 20000
+    flops = cus * 4 * iters * 8 * MFMA_FLOPS
+    mfma = {}
+    for name, ops in operands.items():
+        binding.mfma_probe(ops, cus, 200, out)
+        ts = []
+        for _ in range(5):
+            with Timer(torch) as t:
+                binding.mfma_probe(ops, cus, iters, out)
+            torch.cuda.synchronize()
+            ts.append(t.ms())
+        mfma[name] = round(flops / (statistics.median(ts) * 1e-3) / 1e12, 1)
+    reads = {}
+    iout = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+    for mib, copies in ((70, 8), (470, 2), (2048, 1)):
+        bufs = [torch.randint(0, 1 << 30, (mib << 18,), dtype=torch.int32, device=dev, generator=gen)
+                for _ in range(copies)]
+        row = {}
+        reps = 16
+        for wgs in (256, 512, 1024, 4096):
+            for i in range(copies):
+                binding.read_probe(bufs[i], wgs, iout)
+            ts = []
+            for _ in range(3):
+                with Timer(torch) as t:  # back-to-back launches, copies rotated
+                    for i in range(reps):
+                        binding.read_probe(bufs[i % copies], wgs, iout)
+                torch.cuda.synchronize()
+                ts.append(t.ms() / reps)
+            row[str(wgs)] = round((mib << 20) / (statistics.median(ts) * 1e-3) / 1e9, 1)
+        reads["%d MiB" % mib] = row
+        del bufs
+        torch.cuda.empty_cache()
+    src = [torch.randint(0, 1 << 30, (128 << 20,), dtype=torch.int32, device=dev, generator=gen) for _ in range(2)]
+    dst = [torch.empty_like(x) for x in src]
+    ts = []
+    for _ in range(3):
+        with Timer(torch) as t:
+            for i in range(8):
+                dst[i % 2].copy_(src[i % 2])
+        torch.cuda.synchronize()
+        ts.append(t.ms() / 8)
+    copy_gbs = round(2 * (512 << 20) / (statistics.median(ts) * 1e-3) / 1e9, 1)
+    best_read = max(v for row in reads.values() for v in row.values())
+    res = {
+        "metric": "measured ceilings: scaled-FP4 MFMA rate and HBM read bandwidth", "value": mfma["random"],
+        "unit": "TFLOP/s (scaled-FP4 MFMA, random operands)", "n_gpus": 1, "steps": 5, "warmup": 1,
+        "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4 (E2M1 x E2M1, fp32 accumulate)", "data": "synthetic (constant and seeded random bytes)",
+        "config": {"workload": "peaks: %d workgroups x 4 waves x %d rounds of 8 independent 32x32x64 scaled-FP4 "
+                               "MFMAs; plain reads of 70 MiB, 470 MiB, 2 GiB; device copy of 512 MiB" % (cus, iters),
+                   "compute_units": cus},
+        "mfma_fp4_tflops": dict(mfma, nominal=PEAK_FP4_TFLOPS),
+        "mfma_fraction_of_nominal": {k: round(v / PEAK_FP4_TFLOPS, 4) for k, v in mfma.items()},
+        "hbm_read_gbs_by_workgroups": reads, "copy_gbs_read_plus_write": copy_gbs,
+        "hbm_read_fraction_of_nominal": round(best_read / PEAK_HBM_GBS, 4),
+        "timing": "MFMA: HIP events around each launch (median of 5); reads and copy: HIP events around 16 (8) "
+                  "back-to-back launches with the buffers rotated, per launch (median of 3)",
+    }
+    emit(args, res)
+
+
 def capture(torch, fn):
     """A HIP graph of the kernels that fn enqueues on the current stream."""
     s = torch.cuda.Stream()
@@ -756,6 +839,9 @@ def main():
         return
     if wl == PREPARE_STREAM:
         prepare_stream_main(args, torch, binding, inputs, dev)
+        return
+    if wl == PEAKS:
+        peaks_main(args, torch, binding, dev)
         return
     spec = inputs.WORKLOAD_SPECS[4 if wl == MOE_BLOCK else wl]
     b = args.block if args.block is not None else spec["blocks"][0]

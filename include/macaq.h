@@ -122,6 +122,36 @@ void macaq_debug_override_arch(const char* arch);
 void macaq_debug_limit_workgroups(int32_t n);
 
 /*
+ * Measurement probes, not part of the layer: the ceilings that the GEMM and
+ * the bandwidth-bound kernels are compared with on the device at hand (the
+ * nominal peaks are the chip's published figures).
+ *
+ * macaq_debug_mfma_probe: `workgroups` workgroups of 256 threads (96 KiB of
+ * LDS each, so one per CU) each run `iters` rounds of 8 independent scaled
+ * FP4 MFMAs (32x32x64, E2M1 x E2M1, every scale 2^0) per wave on register
+ * operands, nothing else in the loop. Thread t reads its 6 operands of 16
+ * bytes once, from bytes [96 t, 96 t + 96) of `operands` (device, at least
+ * 24576 bytes, shared by every workgroup; random bytes make the matrix
+ * cores' inputs change from one MFMA to the next). out: device fp32
+ * [workgroups * 256], written (a sum of each thread's accumulators, so the
+ * work is kept). Work: workgroups * 4 * iters * 8 * 131072 flops.
+ *
+ * macaq_debug_read_probe: reads `bytes` of device memory at `src` with
+ * `workgroups` workgroups of 256 threads, each thread with 8 loads of 16
+ * bytes in flight along a grid-stride walk. out: device uint32
+ * [workgroups * 256], written (a fold of what each thread read).
+ *
+ * Both: MACAQ_EINVAL for NULL pointers, workgroups outside [1, 65536],
+ * iters < 1 or bytes < 16; MACAQ_EALIGN unless operands and src are 16-byte
+ * aligned and bytes is a multiple of 16; enqueued on `stream`, nothing
+ * allocated.
+ */
+macaq_status macaq_debug_mfma_probe(const void* operands, int32_t workgroups, int32_t iters, float* out,
+                                    macaq_stream_t stream);
+macaq_status macaq_debug_read_probe(const void* src, int64_t bytes, int32_t workgroups, uint32_t* out,
+                                    macaq_stream_t stream);
+
+/*
  * Per-channel scale from calibration activations (the "calibrated
  * per-channel scale" of the paper card's title and Abstract):
  *   s[k] = RN32(sqrt(max_r |xcal[r, k]|)), or 1 when that maximum is 0.

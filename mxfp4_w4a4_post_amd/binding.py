@@ -37,6 +37,8 @@ _SIGNATURES = {
     "macaq_calibrate_pow": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp]),
     "macaq_debug_override_arch": (None, [ctypes.c_char_p]),
     "macaq_debug_limit_workgroups": (None, [_i32]),
+    "macaq_debug_mfma_probe": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
+    "macaq_debug_read_probe": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp]),
     "macaq_make_multipliers": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp]),
     "macaq_make_multipliers_device": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
     "macaq_prepare_weights": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, ctypes.c_int, _vp, _vp,
@@ -136,6 +138,31 @@ def limit_workgroups(n: int):
     """Cap every persistent GEMM launch at n workgroups (n <= 0: the planned
     grid): the stress hook of macaq.h, for tests; results must not change."""
     load_library().macaq_debug_limit_workgroups(int(n))
+
+
+MFMA_PROBE_OPERAND_BYTES = 24576
+
+
+def mfma_probe(operands: torch.Tensor, workgroups: int, iters: int, out: torch.Tensor) -> torch.Tensor:
+    """Back-to-back scaled-FP4 MFMAs on register operands (the measurement
+    probe of macaq.h); operands: device uint8 of at least 24576 bytes, out:
+    device fp32 of workgroups * 256."""
+    _need_cuda(operands, out)
+    assert operands.numel() * operands.element_size() >= MFMA_PROBE_OPERAND_BYTES
+    assert out.dtype == torch.float32 and out.numel() >= workgroups * 256
+    _check(load_library().macaq_debug_mfma_probe(_ptr(operands), workgroups, iters, _ptr(out), _stream(out)),
+           "macaq_debug_mfma_probe")
+    return out
+
+
+def read_probe(src: torch.Tensor, workgroups: int, out: torch.Tensor) -> torch.Tensor:
+    """A plain read of src (device, contiguous) by the measurement probe of
+    macaq.h; out: device int32 of workgroups * 256."""
+    _need_cuda(src, out)
+    assert src.is_contiguous() and out.dtype == torch.int32 and out.numel() >= workgroups * 256
+    _check(load_library().macaq_debug_read_probe(_ptr(src), src.numel() * src.element_size(), workgroups, _ptr(out),
+                                                 _stream(src)), "macaq_debug_read_probe")
+    return out
 
 
 def _status_string(status: int) -> str:

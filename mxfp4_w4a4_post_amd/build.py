@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmacaq.so")
 # digest of the sources and flags the library was built from, written after it
 DIGEST = LIB + ".digest"
-SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "moe.hip", "refine.hip"]
+SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "moe.hip", "refine.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -332,6 +332,35 @@ void macaq_debug_override_arch(const char* arch) {
 
 void macaq_debug_limit_workgroups(int32_t n) { macaq::set_workgroup_cap(n); }
 
+macaq_status macaq_debug_mfma_probe(const void* operands, int32_t workgroups, int32_t iters, float* out,
+                                    macaq_stream_t stream) {
+  const char* who = "macaq_debug_mfma_probe";
+  if (!operands || !out) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (workgroups < 1 || workgroups > 65536 || iters < 1)
+    return fail(MACAQ_EINVAL, "%s: workgroups = %d not in [1, 65536] or iters = %d < 1", who, workgroups, iters);
+  if (!aligned(operands, 16) || !aligned(out, 4)) return fail(MACAQ_EALIGN, "%s: operands 16-byte aligned", who);
+  macaq_status st = check_device();
+  if (st != MACAQ_OK) return st;
+  const hipError_t e =
+      launch_mfma_probe(operands, workgroups, iters, out, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_debug_mfma_probe launch");
+}
+
+macaq_status macaq_debug_read_probe(const void* src, int64_t bytes, int32_t workgroups, uint32_t* out,
+                                    macaq_stream_t stream) {
+  const char* who = "macaq_debug_read_probe";
+  if (!src || !out) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);
+  if (bytes < 16 || workgroups < 1 || workgroups > 65536)
+    return fail(MACAQ_EINVAL, "%s: bytes = %lld < 16 or workgroups = %d not in [1, 65536]", who, (long long)bytes,
+                workgroups);
+  if (!aligned(src, 16) || bytes % 16 != 0 || !aligned(out, 4))
+    return fail(MACAQ_EALIGN, "%s: src 16-byte aligned and bytes a multiple of 16", who);
+  macaq_status st = check_device();
+  if (st != MACAQ_OK) return st;
+  const hipError_t e = launch_read_probe(src, bytes, workgroups, out, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MACAQ_OK : hip_fail(e, "macaq_debug_read_probe launch");
+}
+
 macaq_status macaq_make_multipliers(const float* s, int64_t K, int32_t b, float* a, float* r) {
   const char* who = "macaq_make_multipliers";
   if (!s || (!a && !r)) return fail(MACAQ_EINVAL, "%s: NULL pointer", who);

@@ -173,6 +173,12 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t
 hipError_t launch_moe_combine(const uint16_t* rows, int64_t H, const int32_t* pos, const float* w, int64_t T, int k,
                               void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
 
+// Measurement probes: back-to-back scaled-FP4 MFMAs on register operands
+// (ops: 24576 bytes, out: workgroups * 256 floats) and a plain read of
+// `bytes` at src (out: workgroups * 256 words).
+hipError_t launch_mfma_probe(const void* ops, int workgroups, int iters, float* out, hipStream_t stream);
+hipError_t launch_read_probe(const void* src, int64_t bytes, int workgroups, uint32_t* out, hipStream_t stream);
+
 // Flip-Refinement: the Hessian of transformed calibration rows (xt: R x K fp32
 // scratch) and the greedy code moves (E, G: N x K fp64 scratch, hdiag: K).
 hipError_t launch_hessian(const void* xcal, int64_t R, int64_t K, int64_t ldx, const float* a, int b, float* xt,

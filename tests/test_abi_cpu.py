@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 29, names
+    assert len(names) == 31, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding._SIGNATURES), "binding signatures out of sync with the header"
@@ -110,6 +110,21 @@ def test_gemm_and_grouped_reject(lib):
     assert g(FAKE, None, 2, 16, 64, None, 0, FAKE, FAKE, 8, FAKE, 0, FAKE, 0, None) == EINVAL
     assert g(FAKE, FAKE, 2, 16, 64, None, 0, FAKE, FAKE, 8, FAKE, 0, FAKE, 0, None) == EWORKSPACE
     assert g(FAKE, FAKE, 2, 0, 64, None, 0, FAKE, FAKE, 8, FAKE, 0, FAKE, 0, None) == OK
+
+
+def test_probes_reject(lib):
+    m = lib.macaq_debug_mfma_probe
+    assert m(None, 256, 10, FAKE, None) == EINVAL
+    assert m(FAKE, 0, 10, FAKE, None) == EINVAL
+    assert m(FAKE, 70000, 10, FAKE, None) == EINVAL
+    assert m(FAKE, 256, 0, FAKE, None) == EINVAL
+    assert m(FAKE + 4, 256, 10, FAKE, None) == EALIGN
+    r = lib.macaq_debug_read_probe
+    assert r(FAKE, 1 << 20, 256, None, None) == EINVAL
+    assert r(FAKE, 8, 256, FAKE, None) == EINVAL
+    assert r(FAKE, 1 << 20, 0, FAKE, None) == EINVAL
+    assert r(FAKE, (1 << 20) + 4, 256, FAKE, None) == EALIGN
+    assert r(FAKE + 8, 1 << 20, 256, FAKE, None) == EALIGN
 
 
 def test_calibrate_and_multipliers_reject(lib):
