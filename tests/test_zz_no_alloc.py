@@ -3,7 +3,9 @@ macaq_linear (caller's workspace) on the same inputs, through the C ABI.
 Both run the same kernels, so the outputs must be the same bits: two calls
 in a row, the second on a smaller input (the scratch keeps the first call's
 contents), then a decode shape whose split-K partial sums also live in the
-scratch. A size beyond the scratch is refused before anything is enqueued."""
+scratch, and the call captured in a HIP graph and replayed with other calls
+in between. A size beyond the scratch is refused before anything is
+enqueued."""
 import ctypes
 
 import numpy as np
@@ -56,6 +58,38 @@ def test_noalloc_decode_split_k(dev):
         print("[noalloc] %s" % case.name, flush=True)
         y, y_ref = _both(case, dev, torch.bfloat16)
         assert torch.equal(y, y_ref), case.name
+
+
+def test_noalloc_in_a_graph(dev):
+    """A caller that captures its work in a HIP graph (the kind of caller the
+    entry point is for): the captured call, replayed with other no-allocation
+    calls in between that overwrite the scratch, equals the eager call every
+    time (each call writes what it reads from the scratch before reading it)."""
+    case = inputs.linear_case(3, 1, M=64)          # K=25600, N=5120: split-K partials in the scratch too
+    other = inputs.linear_case(1, 0, M=300, K=1024, N=600)
+    print("[noalloc] graph %s, between replays %s" % (case.name, other.name), flush=True)
+    x, xo = case.x.to(dev), other.x.to(dev)
+    a, pw = _layer(case, dev)
+    ao, pwo = _layer(other, dev)
+    y_ref = binding.linear(x, a, case.b, pw, out_dtype=torch.bfloat16)
+    y = torch.empty_like(y_ref)
+    yo = torch.empty(other.M, other.N, dtype=torch.bfloat16, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        binding.linear_noalloc(x, a, case.b, pw, out=y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.linear_noalloc(x, a, case.b, pw, out=y)
+    for i in range(3):
+        y.fill_(float("nan"))
+        binding.linear_noalloc(xo, ao, other.b, pwo, out=yo)   # overwrites the scratch
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), "replay %d differs from the eager call" % i
 
 
 def test_noalloc_refuses_beyond_scratch(dev):
