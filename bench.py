@@ -519,6 +519,28 @@ def prepare_stream_main(args, torch, binding, inputs, dev):
     emit(args, res)
 
 
+def mfma_probe_tflops(torch, binding, dev, operands, iters=20000, reps=5):
+    """Back-to-back scaled-FP4 MFMAs on register operands (one workgroup per
+    CU): TFLOP/s, the median over reps launches."""
+    import statistics
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    binding.mfma_probe(operands, cus, 200, out)
+    ts = []
+    for _ in range(reps):
+        with Timer(torch) as t:
+            binding.mfma_probe(operands, cus, iters, out)
+        torch.cuda.synchronize()
+        ts.append(t.ms())
+    return cus * 4 * iters * 8 * MFMA_FLOPS / (statistics.median(ts) * 1e-3) / 1e12
+
+
+def random_probe_operands(torch, binding, dev):
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    return torch.randint(0, 256, (binding.MFMA_PROBE_OPERAND_BYTES,), dtype=torch.uint8, device=dev, generator=gen)
+
+
 def peaks_main(args, torch, binding, dev):
     """The ceilings the kernels are read against, measured on this device:
     back-to-back scaled-FP4 MFMAs on register operands (one workgroup of 4
@@ -530,24 +552,12 @@ def peaks_main(args, torch, binding, dev):
     launches follow one another in a step."""
     import statistics
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(11)
-    nops = binding.MFMA_PROBE_OPERAND_BYTES
-    operands = {"constant": torch.full((nops,), 0x22, dtype=torch.uint8, device=dev),  # E2M1 1.0 in each nibble
-                "random": torch.randint(0, 256, (nops,), dtype=torch.uint8, device=dev, generator=gen)}
-    out = torch.empty(cus * 256, dtype=torch.float32, device=dev)
     iters = 20000
-    flops = cus * 4 * iters * 8 * MFMA_FLOPS
-    mfma = {}
-    for name, ops in operands.items():
-        binding.mfma_probe(ops, cus, 200, out)
-        ts = []
-        for _ in range(5):
-            with Timer(torch) as t:
-                binding.mfma_probe(ops, cus, iters, out)
-            torch.cuda.synchronize()
-            ts.append(t.ms())
-        mfma[name] = round(flops / (statistics.median(ts) * 1e-3) / 1e12, 1)
+    operands = {"constant": torch.full((binding.MFMA_PROBE_OPERAND_BYTES,), 0x22, dtype=torch.uint8, device=dev),
+                "random": random_probe_operands(torch, binding, dev)}  # constant: E2M1 1.0 in each nibble
+    mfma = {k: round(mfma_probe_tflops(torch, binding, dev, ops, iters), 1) for k, ops in operands.items()}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(12)
     reads = {}
     iout = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
     for mib, copies in ((70, 8), (470, 2), (2048, 1)):
@@ -973,6 +983,12 @@ def main():
                                "kernel": kname,
                                "avg_launch_us": round(1e3 * gemm_ms / len(entries), 3),
                                "kernel_source_digest": digest}
+            # the practical ceiling on this device in the same run: back-to-back
+            # MFMAs on random operands, where the matrix cores run power-limited
+            probe = mfma_probe_tflops(torch, binding, dev, random_probe_operands(torch, binding, dev), 8000, 3)
+            out["mfma_ceiling_random_operands"] = {"tflops": round(probe, 1),
+                                                   "gemm_fraction_of_it": round(tf / probe, 4),
+                                                   "probe": "macaq_debug_mfma_probe (bench.py --workload peaks)"}
         if wl == 5 and not args.no_block_sweep:
             # the other Hadamard blocks of the large prefill workload: the
             # same layers and plain path, fused step with b = 64 and 128
