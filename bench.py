@@ -535,6 +535,30 @@ def mfma_probe_tflops(torch, binding, dev, operands, iters=20000, reps=5):
     return cus * 4 * iters * 8 * MFMA_FLOPS / (statistics.median(ts) * 1e-3) / 1e12
 
 
+def read_probe_gbs(torch, binding, dev, mib, copies, workgroups, reps=16):
+    """Plain read of `mib` MiB (copies rotated past the last-level cache) by
+    the read probe: GB/s per launch over reps back-to-back launches, the
+    median of 3."""
+    import statistics
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(12)
+    bufs = [torch.randint(0, 1 << 30, (mib << 18,), dtype=torch.int32, device=dev, generator=gen)
+            for _ in range(copies)]
+    iout = torch.empty(workgroups * 256, dtype=torch.int32, device=dev)
+    for b in bufs:
+        binding.read_probe(b, workgroups, iout)
+    ts = []
+    for _ in range(3):
+        with Timer(torch) as t:
+            for i in range(reps):
+                binding.read_probe(bufs[i % copies], workgroups, iout)
+        torch.cuda.synchronize()
+        ts.append(t.ms() / reps)
+    del bufs
+    torch.cuda.empty_cache()
+    return (mib << 20) / (statistics.median(ts) * 1e-3) / 1e9
+
+
 def random_probe_operands(torch, binding, dev):
     gen = torch.Generator(device=dev)
     gen.manual_seed(11)
@@ -559,26 +583,9 @@ def peaks_main(args, torch, binding, dev):
     gen = torch.Generator(device=dev)
     gen.manual_seed(12)
     reads = {}
-    iout = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
     for mib, copies in ((70, 8), (470, 2), (2048, 1)):
-        bufs = [torch.randint(0, 1 << 30, (mib << 18,), dtype=torch.int32, device=dev, generator=gen)
-                for _ in range(copies)]
-        row = {}
-        reps = 16
-        for wgs in (256, 512, 1024, 4096):
-            for i in range(copies):
-                binding.read_probe(bufs[i], wgs, iout)
-            ts = []
-            for _ in range(3):
-                with Timer(torch) as t:  # back-to-back launches, copies rotated
-                    for i in range(reps):
-                        binding.read_probe(bufs[i % copies], wgs, iout)
-                torch.cuda.synchronize()
-                ts.append(t.ms() / reps)
-            row[str(wgs)] = round((mib << 20) / (statistics.median(ts) * 1e-3) / 1e9, 1)
-        reads["%d MiB" % mib] = row
-        del bufs
-        torch.cuda.empty_cache()
+        reads["%d MiB" % mib] = {str(w): round(read_probe_gbs(torch, binding, dev, mib, copies, w), 1)
+                                 for w in (256, 512, 1024, 4096)}
     src = [torch.randint(0, 1 << 30, (128 << 20,), dtype=torch.int32, device=dev, generator=gen) for _ in range(2)]
     dst = [torch.empty_like(x) for x in src]
     ts = []
@@ -972,6 +979,11 @@ def main():
                                "kernel": "gemm_kernel (weights streamed per wave)",
                                "avg_launch_us": round(1e3 * gemm_ms / len(entries), 3),
                                "kernel_source_digest": digest}
+            # the practical ceiling at this size in the same run: a plain read
+            # of 70 MiB (a call's weights), the better of two grids
+            ceil_gbs = max(read_probe_gbs(torch, binding, dev, 70, 8, w) for w in (512, 4096))
+            out["read_ceiling_70MiB"] = {"gbs": round(ceil_gbs, 1), "gemm_fraction_of_it": round(gb / ceil_gbs, 4),
+                                         "probe": "macaq_debug_read_probe (bench.py --workload peaks)"}
         else:
             tf = flops / (gemm_ms * 1e-3) / 1e12
             kname = ("gemm_wide_kernel (256 x 256 tiles, scaled-FP4 MFMA)" if wl == 5 else
