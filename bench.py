@@ -995,12 +995,13 @@ def main():
                                "kernel": kname,
                                "avg_launch_us": round(1e3 * gemm_ms / len(entries), 3),
                                "kernel_source_digest": digest}
-            # the practical ceiling on this device in the same run: back-to-back
-            # MFMAs on random operands, where the matrix cores run power-limited
-            probe = mfma_probe_tflops(torch, binding, dev, random_probe_operands(torch, binding, dev), 8000, 3)
-            out["mfma_ceiling_random_operands"] = {"tflops": round(probe, 1),
-                                                   "gemm_fraction_of_it": round(tf / probe, 4),
-                                                   "probe": "macaq_debug_mfma_probe (bench.py --workload peaks)"}
+            if wl in (2, 5):
+                # the practical ceiling on this device in the same run: back-to-back
+                # MFMAs on random operands, where the matrix cores run power-limited
+                probe = mfma_probe_tflops(torch, binding, dev, random_probe_operands(torch, binding, dev), 8000, 3)
+                out["mfma_ceiling_random_operands"] = {"tflops": round(probe, 1),
+                                                       "gemm_fraction_of_it": round(tf / probe, 4),
+                                                       "probe": "macaq_debug_mfma_probe (bench.py --workload peaks)"}
         if wl == 5 and not args.no_block_sweep:
             # the other Hadamard blocks of the large prefill workload: the
             # same layers and plain path, fused step with b = 64 and 128
